@@ -1,0 +1,234 @@
+"""fp64 CPU oracle of GPTQ layer quantization -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never does, and the two
+share no code: the oracle is numpy (fp64) plus the C column pass in
+``gptq_oracle.c`` (fp64, OpenMP over rows).
+
+Steps, in the pages' order:
+
+1. ``hessian``: H = 2 X X^T, summed over all calibration tokens (page "LLM 量化
+   方法原理与实现详解", §4.1 GPTQ, the Hessian line of the printed sketch).
+2. ``act_order_perm``: optional column order by descending diag(H) (page
+   "量化经典：LLM.int8 / GPTQ / AWQ", §二 "方法核心" step 2 orders columns by the
+   Hessian; the descending direction is this build's workload choice).
+3. ``damp``: H_d = H + lambda I with lambda = damp_rel * mean(diag H) (not on the
+   pages; the standard regulariser that makes H_d positive definite).
+4. ``inv_chol_upper``: U = upper Cholesky factor of H_d^-1 (U^T U = H_d^-1).  The
+   sketch on page "LLM 量化方法原理与实现详解" §4.1 inverts H "via Cholesky";
+   this is the plain definition written with library primitives.  ``obs_rows``
+   is the literal elimination sequence H_F^-1 of page "PTQ 权重量化：从 GPTQ 到
+   AWQ" (GPTQ section) and pins U in the tests.
+5. ``gptq``: the greedy column pass with error feedback (C, ``gptq_oracle.c``),
+   unblocked by default, or with lazy batches of B columns.
+6. ``layer_loss``: ||W X - W_hat X||_F^2 = 1/2 sum_r D_r H D_r^T with D = W_hat - W
+   and the undamped H (page "LLM 量化方法原理与实现详解", §4.1 objective).
+
+Every function is pinned by ``tests/test_oracle_*.py`` (closed forms, special
+cases, invariants, brute force and the pages' worked example).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        from . import build as _b
+        path = _b.build(force=False)
+        lib = ctypes.CDLL(path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_rtn.argtypes = [i64, i64, vp, i32, i32, i64, vp, vp, vp]
+        lib.oracle_rtn.restype = i32
+        lib.oracle_gptq_pass.argtypes = [i64, i64, vp, i64, vp, i32, i32, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_gptq_pass.restype = i32
+        lib.oracle_hessian_entries.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp]
+        lib.oracle_hessian_entries.restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------
+# inputs
+# ----------------------------------------------------------------------------
+def widen(X: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of X given as bf16 bit patterns (uint16) or fp32."""
+    if X.dtype == np.uint16:
+        return (X.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return X.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# step 1: Hessian
+# ----------------------------------------------------------------------------
+def hessian(X: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """H = 2 X X^T in fp64 (full symmetric matrix), summed over token chunks."""
+    d = X.shape[0]
+    H = np.zeros((d, d), dtype=np.float64)
+    for t0 in range(0, X.shape[1], chunk):
+        xc = widen(X[:, t0:t0 + chunk])
+        H += xc @ xc.T
+    H *= 2.0
+    return H
+
+
+def hessian_entries(X: np.ndarray, rows, cols) -> np.ndarray:
+    """Sampled entries H[i, j] = 2 sum_t X[i,t] X[j,t], each an fp64 dot product."""
+    X = np.ascontiguousarray(X)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.zeros(rows.shape[0], dtype=np.float64)
+    _lib().oracle_hessian_entries(_p(X), int(X.dtype == np.uint16), X.shape[0], X.shape[1], X.shape[1],
+                                  rows.shape[0], _p(rows), _p(cols), _p(out))
+    return out
+
+
+def hessian_diag(X: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """diag(H) = 2 sum_t X[i,t]^2 in fp64."""
+    out = np.zeros(X.shape[0], dtype=np.float64)
+    for t0 in range(0, X.shape[1], chunk):
+        xc = widen(X[:, t0:t0 + chunk])
+        out += np.einsum("it,it->i", xc, xc)
+    return 2.0 * out
+
+
+# ----------------------------------------------------------------------------
+# steps 2-4: order, damping, inverse factor
+# ----------------------------------------------------------------------------
+def act_order_perm(diag: np.ndarray) -> np.ndarray:
+    """Columns by descending diag(H); equal keys keep the lower index first."""
+    return np.argsort(-np.asarray(diag, dtype=np.float64), kind="stable").astype(np.int32)
+
+
+def damp(H: np.ndarray, damp_rel: float) -> np.ndarray:
+    Hd = np.array(H, dtype=np.float64, copy=True)
+    lam = damp_rel * np.mean(np.diag(Hd))
+    Hd[np.diag_indices_from(Hd)] += lam
+    return Hd
+
+
+def inv_chol_upper(Hd: np.ndarray) -> np.ndarray:
+    """Upper U with U^T U = Hd^-1 (Cholesky factor of the inverse, transposed)."""
+    L = np.linalg.cholesky(np.linalg.inv(Hd))
+    return np.ascontiguousarray(L.T)
+
+
+def obs_rows(Hd: np.ndarray) -> np.ndarray:
+    """Literal OBS elimination: row j of V is row j of H_F^-1 on F = {j, ..., d-1}.
+
+    Starting from H_d^-1, after column j is fixed the inverse Hessian of the
+    remaining set is the Schur-complement downdate
+    Hinv_F <- Hinv_F - Hinv_F[:, j] Hinv_F[j, :] / Hinv_F[j, j].
+    O(d^3) Python-level work: use on small matrices only.
+    """
+    d = Hd.shape[0]
+    Hinv = np.linalg.inv(Hd)
+    V = np.zeros_like(Hinv)
+    for j in range(d):
+        V[j, j:] = Hinv[j, j:]
+        col = Hinv[j + 1:, j].copy()
+        row = Hinv[j, j + 1:].copy()
+        Hinv[j + 1:, j + 1:] -= np.outer(col, row) / Hinv[j, j]
+    return V
+
+
+# ----------------------------------------------------------------------------
+# step 5: the column pass
+# ----------------------------------------------------------------------------
+def gptq_pass(W: np.ndarray, U: np.ndarray, bits: int, sym: bool, group: int, block: int = 0):
+    """Column pass on rows of W (processing order).  Returns a dict of arrays."""
+    W64 = np.ascontiguousarray(W, dtype=np.float64)
+    U64 = np.ascontiguousarray(U, dtype=np.float64)
+    n, d = W64.shape
+    g = group if group > 0 else d
+    ng = d // g
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scales = np.zeros((n, ng), dtype=np.float32)
+    zeros = np.zeros((n, ng), dtype=np.float32)
+    w_at_q = np.zeros((n, d), dtype=np.float64)
+    err = np.zeros((n, d), dtype=np.float64)
+    st = _lib().oracle_gptq_pass(n, d, _p(W64), d, _p(U64), bits, int(bool(sym)), group, block,
+                                 _p(codes), _p(scales), _p(zeros), _p(w_at_q), _p(err))
+    if st != 0:
+        raise ValueError(f"oracle_gptq_pass failed ({st})")
+    return dict(codes=codes, scales=scales, zeros=zeros, w_at_q=w_at_q, err=err)
+
+
+def gptq(W: np.ndarray, H: np.ndarray, bits: int, sym: bool, group: int, damp_rel: float,
+         act_order: bool = False, block: int = 0, rows=None, hdiag=None):
+    """Whole-layer GPTQ.  Codes are returned in the original column order.
+
+    ``rows`` (optional) selects the output rows to quantize: rows are
+    independent given U, so a sample of rows gives exact per-row results.
+    ``hdiag`` (optional) is the fp64 diag(H) used as the ordering key.
+    """
+    W = np.asarray(W)
+    d = W.shape[1]
+    g = group if group > 0 else d
+    if rows is not None:
+        W = W[np.asarray(rows)]
+    perm = np.arange(d, dtype=np.int32)
+    Hp = H
+    if act_order:
+        perm = act_order_perm(np.diag(H) if hdiag is None else hdiag)
+        Hp = H[np.ix_(perm, perm)]
+    Hd = damp(Hp, damp_rel)
+    U = inv_chol_upper(Hd)
+    out = gptq_pass(W[:, perm], U, bits, sym, group, block)
+    codes = np.empty_like(out["codes"])
+    codes[:, perm] = out["codes"]
+    g_idx = np.empty(d, dtype=np.int32)
+    g_idx[perm] = np.arange(d, dtype=np.int32) // g
+    out.update(codes_perm=out["codes"], codes=codes, g_idx=g_idx, perm=perm, U=U, Hd=Hd)
+    return out
+
+
+def rtn(W: np.ndarray, bits: int, sym: bool, group: int):
+    """Round-to-nearest baseline with the same grids as the column pass."""
+    W32 = np.ascontiguousarray(W, dtype=np.float32)
+    n, d = W32.shape
+    g = group if group > 0 else d
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scales = np.zeros((n, d // g), dtype=np.float32)
+    zeros = np.zeros((n, d // g), dtype=np.float32)
+    st = _lib().oracle_rtn(n, d, _p(W32), bits, int(bool(sym)), group, _p(codes), _p(scales), _p(zeros))
+    if st != 0:
+        raise ValueError(f"oracle_rtn failed ({st})")
+    return dict(codes=codes, scales=scales, zeros=zeros)
+
+
+# ----------------------------------------------------------------------------
+# step 6: dequantization and loss
+# ----------------------------------------------------------------------------
+def dequant(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int, g_idx=None) -> np.ndarray:
+    """W_hat = (code - zero) * scale in fp32 (the stored format), as fp64."""
+    d = codes.shape[1]
+    g = group if group > 0 else d
+    gi = np.arange(d) // g if g_idx is None else np.asarray(g_idx)
+    s = scales[:, gi]
+    z = zeros[:, gi]
+    return ((codes.astype(np.float32) - z) * s).astype(np.float64)
+
+
+def layer_loss(W: np.ndarray, What: np.ndarray, H: np.ndarray) -> float:
+    """||(W - W_hat) X||_F^2 written through H = 2 X X^T: 1/2 sum_r D_r H D_r^T."""
+    D = np.asarray(What, dtype=np.float64) - np.asarray(W, dtype=np.float64)
+    return 0.5 * float(np.sum((D @ H) * D))
+
+
+def layer_loss_from_x(W: np.ndarray, What: np.ndarray, X: np.ndarray) -> float:
+    """||W X - W_hat X||_F^2 computed directly from the activations."""
+    D = np.asarray(What, dtype=np.float64) - np.asarray(W, dtype=np.float64)
+    R = D @ widen(X)
+    return float(np.sum(R * R))
