@@ -1,0 +1,186 @@
+"""GPTQ layer-quantization benchmark on one MI355X.
+
+One step = the whole hot path over one synthetic layer with every input
+resident in HBM: H = 2 X X^T over all calibration tokens, damping + inverse
+factor, and the column pass with lazy batch updates (W restored from a pristine
+device copy first).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload q_proj_7b] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ ms/layer + TFLOP/s (XXᵀ, lazy update) vs MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (AMD published)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak (AMD published)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
+    """The oracle as it stands, timed on a bounded sample of the same workload."""
+    import oracle
+    d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
+    n_s = min(n, 8192)
+    rows = min(d_out, 32)
+    t0 = time.perf_counter()
+    H = oracle.hessian(lay["X"][:, :n_s])
+    t_h = time.perf_counter() - t0
+    Hf = H * (n / n_s)  # stand-in Hessian of the right scale for the factor step
+    t0 = time.perf_counter()
+    perm = np.arange(d_in)
+    if cfg_d["act_order"]:
+        perm = oracle.act_order_perm(np.diag(Hf))
+        Hf = Hf[np.ix_(perm, perm)]
+    U = oracle.inv_chol_upper(oracle.damp(Hf, cfg_d["damp"]))
+    t_p = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gptq_pass(lay["W"][:rows][:, perm], U, cfg_d["bits"], cfg_d["sym"], cfg_d["group"])
+    t_q = time.perf_counter() - t0
+    est_ms = 1e3 * (t_h * n / n_s + t_p + t_q * d_out / rows)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": cores, "kind": "oracle",
+            "sample": (f"H on {n_s} of {n} tokens (x{n / n_s:g}), full {d_in}x{d_in} factor, column pass on "
+                       f"{rows} of {d_out} rows (x{d_out / rows:g}); measured {t_h:.2f}+{t_p:.2f}+{t_q:.2f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="q_proj_7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs GPTQ on one GPU only "
+              f"(the layer's H all-reduce and row sharding are described in DESIGN.md, not built).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import datagen
+    import post_weight_quantization_21_amd as gq
+
+    gq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    lay = datagen.make_layer(args.workload)
+    log(f"generated {args.workload}: W {lay['W'].shape} X {lay['X'].shape} {lay['X'].dtype} in {time.perf_counter() - t0:.1f}s")
+    d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
+    cfg_d = dict(bits=lay["bits"], sym=lay["sym"], group=lay["group"], block=lay["block"], damp=lay["damp"],
+                 act_order=lay["act_order"])
+    cfg = gq.config(lay["bits"], lay["sym"], lay["group"], lay["block"], lay["damp"], lay["act_order"])
+
+    if lay["X"].dtype == np.uint16:
+        X = torch.from_numpy(lay["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(lay["X"]).to(dev)
+    W0 = torch.from_numpy(lay["W"]).to(dev)
+    W = torch.empty_like(W0)
+    H = torch.zeros(d_in, d_in, dtype=torch.float32, device=dev)
+    hdiag = torch.zeros(d_in, dtype=torch.float64, device=dev) if lay["act_order"] else None
+    U = torch.empty(d_in, d_in, dtype=torch.float32, device=dev)
+    perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    ng = gq.n_groups(d_in, lay["group"])
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device=dev)
+    scales = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    zeros = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    g_idx = torch.empty(d_in, dtype=torch.int32, device=dev)
+    ws_h = torch.empty(max(1, gq.workspace_bytes(gq.OP_HESSIAN, 0, d_in, n)), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(gq.workspace_bytes(gq.OP_PREPARE, 0, d_in, 0, cfg), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(gq.workspace_bytes(gq.OP_QUANTIZE, d_out, d_in, 0, cfg), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        H.zero_()
+        if hdiag is not None:
+            hdiag.zero_()
+        if ev:
+            ev[0].record(stream)
+        gq.hessian_accumulate(H, X, hdiag, ws=ws_h)
+        if ev:
+            ev[1].record(stream)
+        gq.prepare_hinv(H, cfg, U, perm, info, hdiag=hdiag, ws=ws_p)
+        if ev:
+            ev[2].record(stream)
+        W.copy_(W0)
+        if ev:
+            ev[3].record(stream)
+        gq.quantize_layer(W, U, cfg, codes, scales, zeros, perm, g_idx, ws=ws_q)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        log(f"factorization reported info={int(info.item())}")
+        return 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    ph = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
+    t_h, t_p, t_c, t_q = ph.mean(axis=0)
+    log(f"phases (ms): hessian {t_h:.3f}  prepare {t_p:.3f}  copy {t_c:.3f}  quantize {t_q:.3f}  step {ms_step:.3f}")
+
+    syrk_flops = float(d_in) * (d_in + 1) * n
+    lazy_flops = float(d_out) * d_in * max(0, d_in - lay["block"])
+    achieved = syrk_flops / (t_h * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->f32 (XX^T), f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "d_out": d_out, "d_in": d_in, "n_tok": n, "x_dtype": lay["x_dtype"],
+                   "bits": lay["bits"], "symmetric": lay["sym"], "group_size": lay["group"],
+                   "block_size": lay["block"], "damp_rel": lay["damp"], "act_order": lay["act_order"],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "hessian_accumulate (syrk_bf16_kernel + split-K reduce)",
+                     "flops_per_launch": syrk_flops},
+        "phases_ms": {"hessian": round(t_h, 3), "prepare": round(t_p, 3), "restore_w": round(t_c, 3),
+                      "quantize": round(t_q, 3)},
+        "lazy_update": {"flops": lazy_flops,
+                        "tflops_lower_bound": round(lazy_flops / (t_q * 1e-3) / 1e12, 2),
+                        "peak": PEAK_F32_TFLOPS,
+                        "note": "lazy-update flops over the whole column-pass phase (batch kernels included)"},
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(lay, cfg_d)
+        log(f"cpu baseline took {time.perf_counter() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

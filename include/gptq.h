@@ -1,0 +1,201 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library.
+ *
+ * GPTQ quantizes one linear layer W (d_out x d_in) at a time so that W X stays
+ * close to W_hat X on calibration activations X (page "LLM 量化方法原理与实现
+ * 详解", §4.1 GPTQ, objective and Hessian; page "量化经典：LLM.int8 / GPTQ /
+ * AWQ", §二 "方法核心").  The library runs the four steps on one GPU:
+ *
+ *   gptq_hessian_accumulate  H += 2 X X^T                       (step 1)
+ *   gptq_prepare_hinv        order, damping, U = chol(H_d^-1)   (steps 2-3)
+ *   gptq_quantize_layer      greedy column pass with error feedback and
+ *                            lazy batch updates                 (step 4)
+ *   gptq_rtn_quantize        round-to-nearest baseline (no feedback)
+ *   gptq_layer_loss          ||W X - W_hat X||_F^2 through H, the check
+ *
+ * Conventions shared by every entry point
+ *   - All pointers except `cfg` and `out` arguments of gptq_workspace_bytes
+ *     are DEVICE pointers on the current HIP device.  The caller owns every
+ *     buffer; the library never allocates: scratch memory is the `ws`
+ *     argument, sized by gptq_workspace_bytes().
+ *   - Matrices are row-major and densely packed unless a leading dimension is
+ *     given.  Device pointers must be 16-byte aligned.
+ *   - Calls are asynchronous and ordered on `stream`; the library never
+ *     synchronizes the device.  Argument errors are reported synchronously by
+ *     the return value (nothing is launched then); a failed kernel launch
+ *     returns GPTQ_ERR_HIP.  gptq_last_error() gives a message for the calling
+ *     thread's last failure.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics).
+ *
+ * Quantization grid (page "LLM 量化方法原理与实现详解", §2.2 and §2.3):
+ *   symmetric:  qmax = 2^(b-1)-1, scale = max|x| / qmax,
+ *               q = clamp(rint(x / scale), -qmax, qmax), stored code = q + 2^(b-1),
+ *               stored zero = 2^(b-1);
+ *   asymmetric: lo = min(min x, 0), hi = max(max x, 0), scale = (hi-lo)/(2^b-1),
+ *               zero = clamp(rint(-lo/scale), 0, 2^b-1),
+ *               code = clamp(rint(x/scale + zero), 0, 2^b-1);
+ *   a group whose scale would be 0 gets scale 1 (and zero 0 when asymmetric).
+ *   Decisions are made in fp32 with round-half-to-even.  Dequantized value:
+ *   w_hat = (code - zero) * scale.  Groups are `group_size` consecutive input
+ *   columns of one output row (in processing order); group_size 0 = one group
+ *   per row.  scales/zeros are [d_out][n_groups] fp32, codes [d_out][d_in] u8.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define GPTQ_API __attribute__((visibility("default")))
+#else
+#define GPTQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment or config value */
+    GPTQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (see each call) */
+    GPTQ_ERR_WORKSPACE = -3,   /* ws NULL or smaller than gptq_workspace_bytes() */
+    GPTQ_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} gptq_status;
+
+typedef enum { GPTQ_DT_F32 = 0, GPTQ_DT_BF16 = 1 } gptq_dtype;
+
+typedef enum {
+    GPTQ_OP_HESSIAN = 0,
+    GPTQ_OP_PREPARE = 1,
+    GPTQ_OP_QUANTIZE = 2,
+    GPTQ_OP_LOSS = 3
+} gptq_op;
+
+typedef struct {
+    int32_t bits;       /* 2..8 */
+    int32_t symmetric;  /* 1: symmetric grid, 0: asymmetric grid (see above) */
+    int32_t group_size; /* 0 (one group per row) or a divisor of d_in */
+    int32_t block_size; /* lazy batch width B: 32, 64 or 128 */
+    float damp_rel;     /* lambda = damp_rel * mean(diag H), >= 0 */
+    int32_t act_order;  /* 1: process columns by descending diag(H) */
+} gptq_config;
+
+/*
+ * Step 1 -- Hessian accumulation (page "LLM 量化方法原理与实现详解", §4.1: the
+ * Hessian of the layer objective is 2 X X^T; page "量化经典" §二 step 1).
+ *
+ *   H      [d_in][d_in] fp32, in/out.  Only the upper triangle (i <= j) is
+ *          read and written: H[i][j] += 2 * sum_t X[i][t] X[j][t].
+ *          Repeated calls accumulate token chunks.
+ *   hdiag  [d_in] fp64, in/out, may be NULL: hdiag[i] += 2 * sum_t X[i][t]^2
+ *          accumulated in fp64 (the exact-enough ordering key for act-order).
+ *   X      [d_in][ldx] activations, one row per input channel, n_tok tokens
+ *          used per row; bf16 (raw 16-bit patterns) or fp32 per x_dtype.
+ *          ldx * element size must be a multiple of 16 bytes.
+ *   ws     scratch of gptq_workspace_bytes(GPTQ_OP_HESSIAN, 0, d_in, n_tok, NULL).
+ * n_tok == 0 is a no-op.  bf16 inputs are multiplied exactly and summed in
+ * fp32 by matrix-core (MFMA) instructions.
+ */
+GPTQ_API gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void *X, gptq_dtype x_dtype,
+                                    int64_t d_in, int64_t n_tok, int64_t ldx,
+                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Steps 2-3 -- column order, damping and the inverse-Hessian factor.
+ * The GPTQ update spreads a column's rounding error with the matching row of
+ * the inverse Hessian of the not-yet-quantized columns (page "PTQ 权重量化：
+ * 从 GPTQ 到 AWQ", GPTQ section); those rows are, up to a per-row scale, the
+ * rows of the upper Cholesky factor of H_d^-1 (page "LLM 量化方法原理与实现
+ * 详解", §4.1 sketch: the inverse is obtained with a Cholesky factorization).
+ *
+ *   H        [d_in][d_in] fp32 upper triangle (from step 1); not modified.
+ *   hdiag    [d_in] fp64 or NULL; ordering key when cfg->act_order (if NULL
+ *            the fp32 diagonal of H is used).
+ *   cfg      host pointer; uses damp_rel and act_order.
+ *   U        [d_in][d_in] fp32 out: upper triangle = U with U^T U = H_d^-1,
+ *            H_d = P H P^T + lambda I, lambda = damp_rel * mean(diag H);
+ *            strictly lower triangle = 0.
+ *   perm     [d_in] int32 out (may be NULL when !act_order): processing
+ *            position k holds original column perm[k]; identity if !act_order.
+ *            Order: descending key, ties by lower original index.
+ *   info_dev device int32 out: 0 on success, j+1 if the j-th pivot (processing
+ *            order) of the factorization of H_d was not positive (then U is
+ *            not meaningful).  Read it after synchronizing the stream.
+ *   ws       scratch of gptq_workspace_bytes(GPTQ_OP_PREPARE, 0, d_in, 0, cfg).
+ */
+GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg,
+                              float *U, int32_t *perm, int32_t *info_dev,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step 4 -- the greedy column pass with error feedback and lazy batches
+ * (page "PTQ 权重量化：从 GPTQ 到 AWQ", GPTQ section: update formula and the
+ * 128-column lazy batch; page "量化经典" §二 steps 3-4).  For each column j in
+ * processing order, for every row: fit the group grid when j starts a group
+ * (from the current weights), quantize w_j, e = (w_j - w_hat_j) / U[j][j],
+ * and w_k -= e * U[j][k] for the later columns -- inside the current batch at
+ * once, for columns beyond it when the batch of block_size columns ends.
+ *
+ *   W       [d_out][d_in] fp32, in/out (working storage).  On entry the
+ *           layer in ORIGINAL column order.  On return W[r][k] holds, for
+ *           processing position k, the weight's value when it was quantized.
+ *   U, perm from gptq_prepare_hinv (perm may be NULL when !cfg->act_order).
+ *   codes   [d_out][d_in] u8 out, ORIGINAL column order.
+ *   scales, zeros [d_out][n_groups] fp32 out, groups in processing order.
+ *   g_idx   [d_in] int32 out or NULL: group of each ORIGINAL column.
+ *   ws      scratch of gptq_workspace_bytes(GPTQ_OP_QUANTIZE, d_out, d_in, 0, cfg).
+ * GPTQ_ERR_UNSUPPORTED when block_size is not 32/64/128, or when group_size
+ * is neither 0, nor a divisor of block_size in {32, 64, 128}, nor a multiple
+ * of block_size.
+ */
+GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
+                                const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros,
+                                int32_t *g_idx, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Round-to-nearest baseline (page "PTQ 权重量化：从 GPTQ 到 AWQ", section on
+ * RTN's limits: every weight rounded on its own): same grids as above fitted
+ * on the original W, no error feedback, natural column order.  Uses bits,
+ * symmetric and group_size of cfg.
+ */
+GPTQ_API gptq_status gptq_rtn_quantize(const float *W, int64_t d_out, int64_t d_in, const gptq_config *cfg,
+                              uint8_t *codes, float *scales, float *zeros, hipStream_t stream);
+
+/*
+ * Layer loss ||W X - W_hat X||_F^2 = 1/2 sum_r D_r H D_r^T with D = W_hat - W
+ * (page "LLM 量化方法原理与实现详解", §4.1 objective; H = 2 X X^T undamped).
+ *
+ *   W         [d_out][d_in] original fp32 weights, ORIGINAL column order.
+ *   codes     [d_out][d_in] u8, ORIGINAL column order.
+ *   scales, zeros [d_out][n_groups]; g_idx [d_in] group of each original
+ *             column, or NULL for column c in group c / group_size.
+ *   H         [d_in][d_in] fp32, upper triangle read (original order).
+ *   loss_dev  device double out.
+ *   ws        scratch of gptq_workspace_bytes(GPTQ_OP_LOSS, d_out, d_in, 0, NULL).
+ * Products are fp32 on matrix cores; tile sums are reduced in fp64.
+ */
+GPTQ_API gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const float *scales, const float *zeros,
+                            const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in,
+                            int32_t group_size, double *loss_dev, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Scratch bytes needed by `op` for these sizes (cfg may be NULL for
+ * GPTQ_OP_HESSIAN and GPTQ_OP_LOSS).  `out` is a host pointer. */
+GPTQ_API gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_tok, const gptq_config *cfg,
+                                 size_t *out);
+
+/* Static text for a status code. */
+GPTQ_API const char *gptq_status_string(gptq_status status);
+/* Message of the calling thread's last failed call ("" if none). */
+GPTQ_API const char *gptq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,212 @@
+"""Python binding of libgptq (GPTQ layer quantization on MI355X / gfx950).
+
+Thin argument marshalling over the C ABI declared in ``include/gptq.h``:
+every step of the method runs in the library's HIP kernels.  PyTorch only
+provides device memory (tensors, workspaces) and the current HIP stream.
+The binding refuses to run without the built library: there is no fallback.
+
+Names follow the C ABI: ``hessian_accumulate``, ``prepare_hinv``,
+``quantize_layer``, ``rtn_quantize``, ``layer_loss``, ``workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgptq.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+DT_F32, DT_BF16 = 0, 1
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS = 0, 1, 2, 3
+
+EXPORTED = (
+    "gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_rtn_quantize",
+    "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
+)
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gptq status {status}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    """Mirror of ``gptq_config``."""
+    _fields_ = [("bits", ctypes.c_int32), ("symmetric", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("damp_rel", ctypes.c_float), ("act_order", ctypes.c_int32)]
+
+
+def config(bits: int = 4, symmetric: bool = False, group_size: int = 128, block_size: int = 128,
+           damp_rel: float = 0.01, act_order: bool = False) -> Config:
+    return Config(int(bits), int(bool(symmetric)), int(group_size), int(block_size), float(damp_rel),
+                  int(bool(act_order)))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgptq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m post_weight_quantization_21_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(Config)
+    sig = {
+        "gptq_hessian_accumulate": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
+        "gptq_prepare_hinv": [vp, vp, i64, cfgp, vp, vp, vp, vp, sz, vp],
+        "gptq_quantize_layer": [vp, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp, sz, vp],
+        "gptq_rtn_quantize": [vp, i64, i64, cfgp, vp, vp, vp, vp],
+        "gptq_layer_loss": [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, vp],
+        "gptq_workspace_bytes": [ctypes.c_int, i64, i64, i64, cfgp, ctypes.POINTER(sz)],
+        "gptq_status_string": [ctypes.c_int],
+        "gptq_last_error": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_char_p if name in ("gptq_status_string", "gptq_last_error") else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = load_library().gptq_last_error().decode(errors="replace")
+        raise GptqError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def workspace_bytes(op: int, d_out: int, d_in: int, n_tok: int = 0, cfg: Config | None = None) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().gptq_workspace_bytes(op, d_out, d_in, n_tok, ctypes.byref(cfg) if cfg else None,
+                                               ctypes.byref(out)))
+    return int(out.value)
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(H, X, hdiag=None, ws=None, stream=None) -> None:
+    """H (fp32 [d,d], upper) += 2 X X^T; hdiag (fp64 [d]) += 2 sum x^2.  X: bf16 or fp32 [d][n]."""
+    import torch
+    _need_cuda(H, hdiag)
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit stride along tokens")
+    if X.dtype == torch.bfloat16:
+        dt = DT_BF16
+    elif X.dtype == torch.float32:
+        dt = DT_F32
+    else:
+        raise ValueError("X must be bfloat16 or float32")
+    d, n = X.shape
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_HESSIAN, 0, d, n), X.device)
+    _check(load_library().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), _ptr(X), dt, d, n, X.stride(0), _ptr(ws),
+                                                  ws.numel(), _stream(stream)))
+
+
+def prepare_hinv(H, cfg: Config, U, perm=None, info=None, hdiag=None, ws=None, stream=None):
+    """U = upper Cholesky factor of the damped (and ordered) inverse Hessian.  Returns the info tensor."""
+    import torch
+    _need_cuda(H, U, perm, info, hdiag)
+    d = H.shape[0]
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=H.device)
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0, cfg), H.device)
+    _check(load_library().gptq_prepare_hinv(_ptr(H), _ptr(hdiag), d, ctypes.byref(cfg), _ptr(U), _ptr(perm),
+                                            _ptr(info), _ptr(ws), ws.numel(), _stream(stream)))
+    return info
+
+
+def quantize_layer(W, U, cfg: Config, codes, scales, zeros, perm=None, g_idx=None, ws=None, stream=None) -> None:
+    """GPTQ column pass (in place on W); writes codes/scales/zeros/g_idx."""
+    _need_cuda(W, U, codes, scales, zeros, perm, g_idx)
+    d_out, d_in = W.shape
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_QUANTIZE, d_out, d_in, 0, cfg), W.device)
+    _check(load_library().gptq_quantize_layer(_ptr(W), d_out, d_in, _ptr(U), _ptr(perm), ctypes.byref(cfg),
+                                              _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(ws),
+                                              ws.numel(), _stream(stream)))
+
+
+def rtn_quantize(W, cfg: Config, codes, scales, zeros, stream=None) -> None:
+    _need_cuda(W, codes, scales, zeros)
+    d_out, d_in = W.shape
+    _check(load_library().gptq_rtn_quantize(_ptr(W), d_out, d_in, ctypes.byref(cfg), _ptr(codes), _ptr(scales),
+                                            _ptr(zeros), _stream(stream)))
+
+
+def layer_loss(W, codes, scales, zeros, H, group_size: int, g_idx=None, out=None, ws=None, stream=None):
+    """||W X - W_hat X||^2 through H (device fp64 scalar tensor)."""
+    import torch
+    _need_cuda(W, codes, scales, zeros, H, g_idx, out)
+    d_out, d_in = W.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=W.device)
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_LOSS, d_out, d_in), W.device)
+    _check(load_library().gptq_layer_loss(_ptr(W), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(H),
+                                          d_out, d_in, int(group_size), _ptr(out), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
+    return out
+
+
+@dataclass
+class LayerResult:
+    codes: object
+    scales: object
+    zeros: object
+    g_idx: object
+    perm: object
+    info: object
+
+
+def n_groups(d_in: int, group_size: int) -> int:
+    return d_in // group_size if group_size > 0 else 1
+
+
+def gptq_layer(W, X, cfg: Config, H=None, hdiag=None):
+    """Convenience: all four steps on device tensors (W is overwritten)."""
+    import torch
+    dev = W.device
+    d_out, d_in = W.shape
+    if H is None:
+        H = torch.zeros(d_in, d_in, dtype=torch.float32, device=dev)
+        if cfg.act_order and hdiag is None:
+            hdiag = torch.zeros(d_in, dtype=torch.float64, device=dev)
+        hessian_accumulate(H, X, hdiag)
+    U = torch.empty(d_in, d_in, dtype=torch.float32, device=dev)
+    perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+    info = prepare_hinv(H, cfg, U, perm, hdiag=hdiag)
+    ng = n_groups(d_in, cfg.group_size)
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device=dev)
+    scales = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    zeros = torch.empty(d_out, ng, dtype=torch.float32, device=dev)
+    g_idx = torch.empty(d_in, dtype=torch.int32, device=dev)
+    quantize_layer(W, U, cfg, codes, scales, zeros, perm, g_idx)
+    return LayerResult(codes, scales, zeros, g_idx, perm, info), H, U

@@ -1,0 +1,154 @@
+// C ABI entry points: argument checks, workspace sizing, dispatch.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gptq_status fail(gptq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gptq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return GPTQ_OK;
+    return fail(GPTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a = 16) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gptq_status check_cfg(const gptq_config *c, int64_t d_in, const char *fn) {
+    if (!c) return fail(GPTQ_ERR_INVALID_ARG, "%s: cfg is NULL", fn);
+    if (c->bits < 2 || c->bits > 8) return fail(GPTQ_ERR_INVALID_ARG, "%s: bits=%d outside 2..8", fn, c->bits);
+    if (c->group_size < 0 || (c->group_size > 0 && d_in % c->group_size != 0))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: group_size=%d does not divide d_in=%lld", fn, c->group_size, (long long)d_in);
+    if (!(c->damp_rel >= 0.0f)) return fail(GPTQ_ERR_INVALID_ARG, "%s: damp_rel must be >= 0", fn);
+    return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gptq_status_string(gptq_status st) {
+    switch (st) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+    case GPTQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case GPTQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *gptq_last_error(void) { return g_last_error; }
+
+gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_tok, const gptq_config *cfg, size_t *out) {
+    if (!out) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: out is NULL");
+    if (d_in <= 0 || d_out < 0 || n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: bad sizes");
+    switch (op) {
+    case GPTQ_OP_HESSIAN:
+        *out = gptq::hessian_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
+        return GPTQ_OK;
+    case GPTQ_OP_PREPARE:
+        *out = gptq::prepare_ws_bytes(d_in);
+        return GPTQ_OK;
+    case GPTQ_OP_QUANTIZE: {
+        if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: quantize needs cfg");
+        if (cfg->block_size <= 0) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: block_size must be > 0");
+        *out = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
+        return GPTQ_OK;
+    }
+    case GPTQ_OP_LOSS:
+        *out = gptq::loss_ws_bytes(d_out, d_in);
+        return GPTQ_OK;
+    }
+    return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: unknown op %d", op);
+}
+
+gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void *X, gptq_dtype x_dtype, int64_t d_in,
+                                    int64_t n_tok, int64_t ldx, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_hessian_accumulate";
+    if (d_in <= 0 || n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: d_in must be > 0 and n_tok >= 0", fn);
+    if (x_dtype != GPTQ_DT_F32 && x_dtype != GPTQ_DT_BF16) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    if (ldx < n_tok) return fail(GPTQ_ERR_INVALID_ARG, "%s: ldx < n_tok", fn);
+    const int64_t esz = x_dtype == GPTQ_DT_BF16 ? 2 : 4;
+    if (!H || (n_tok > 0 && !X)) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(H) || (X && !aligned(X)) || (hdiag && !aligned(hdiag, 8)) || (ldx * esz) % 16 != 0)
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned and ldx*elem a multiple of 16", fn);
+    if (n_tok == 0) return GPTQ_OK;
+    const size_t need = gptq::hessian_ws_bytes(d_in, n_tok, x_dtype);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, ws, stream), fn);
+}
+
+gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg, float *U,
+                              int32_t *perm, int32_t *info_dev, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_prepare_hinv";
+    if (d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: d_in must be > 0", fn);
+    if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "%s: cfg is NULL", fn);
+    if (!(cfg->damp_rel >= 0.0f)) return fail(GPTQ_ERR_INVALID_ARG, "%s: damp_rel must be >= 0", fn);
+    if (!H || !U || !info_dev) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (cfg->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "%s: act_order needs perm", fn);
+    if (!aligned(H) || !aligned(U) || (perm && !aligned(perm, 4)) || !aligned(info_dev, 4) || (hdiag && !aligned(hdiag, 8)))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (d_in > (int64_t)1 << 20) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_in too large", fn);
+    const size_t need = gptq::prepare_ws_bytes(d_in);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_prepare(H, hdiag, d_in, cfg->damp_rel, cfg->act_order ? 1 : 0, U, perm, info_dev, ws, stream), fn);
+}
+
+gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
+                                const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros, int32_t *g_idx,
+                                void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_quantize_layer";
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    gptq_status st = check_cfg(cfg, d_in, fn);
+    if (st != GPTQ_OK) return st;
+    if (!W || !U || !codes || !scales || !zeros) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (cfg->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "%s: act_order needs perm", fn);
+    if (!aligned(W) || !aligned(U) || !aligned(scales, 4) || !aligned(zeros, 4) || (perm && !aligned(perm, 4)) ||
+        (g_idx && !aligned(g_idx, 4)))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (!gptq::quantize_supported(*cfg, d_in))
+        return fail(GPTQ_ERR_UNSUPPORTED, "%s: block_size=%d group_size=%d not supported", fn, cfg->block_size, cfg->group_size);
+    if (d_out > ((int64_t)1 << 31) / 2) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_out too large", fn);
+    const size_t need = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_quantize(W, d_out, d_in, U, perm, *cfg, codes, scales, zeros, g_idx, ws, stream), fn);
+}
+
+gptq_status gptq_rtn_quantize(const float *W, int64_t d_out, int64_t d_in, const gptq_config *cfg, uint8_t *codes,
+                              float *scales, float *zeros, hipStream_t stream) {
+    const char *fn = "gptq_rtn_quantize";
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    gptq_status st = check_cfg(cfg, d_in, fn);
+    if (st != GPTQ_OK) return st;
+    if (!W || !codes || !scales || !zeros) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(W, 4) || !aligned(scales, 4) || !aligned(zeros, 4)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return hip_status(gptq::run_rtn(W, d_out, d_in, *cfg, codes, scales, zeros, stream), fn);
+}
+
+gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const float *scales, const float *zeros,
+                            const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in, int32_t group_size,
+                            double *loss_dev, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_layer_loss";
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    if (group_size < 0 || (group_size > 0 && d_in % group_size != 0))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: group_size does not divide d_in", fn);
+    if (!W || !codes || !scales || !zeros || !H || !loss_dev) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(W, 4) || !aligned(H, 4) || !aligned(loss_dev, 8)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    const size_t need = gptq::loss_ws_bytes(d_out, d_in);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_loss(W, codes, scales, zeros, g_idx, H, d_out, d_in, group_size, loss_dev, ws, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal declarations of the gfx950 GPTQ library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "gptq.h"
+
+namespace gptq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// Matrix-core output layout of the 32x32 MFMA family (v_mfma_f32_32x32x*):
+// accumulator register r of lane l holds D[row][col] with
+//   col = l % 32, row = 8 * (r / 4) + 4 * (l / 32) + (r % 4).
+__device__ __forceinline__ int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__device__ __forceinline__ int mfma32_col(int lane) { return lane & 31; }
+
+// ---------------------------------------------------------------------------
+// fp32 matrix-core GEMM:  C = alpha * op(A) op(B) + beta * C   (see gemm_f32.hip)
+// ---------------------------------------------------------------------------
+enum GemmEpilogue { EPI_STORE = 0, EPI_DOT = 1 };
+
+struct GemmDesc {
+    int64_t M = 0, N = 0, K = 0;
+    const float *A = nullptr;
+    int64_t lda = 0;
+    int a_trans = 0;  // 0: A[m][k] = A[m*lda+k];  1: A[m][k] = A[k*lda+m]
+    const float *B = nullptr;
+    int64_t ldb = 0;
+    int b_trans = 0;  // 0: B[k][n] = B[k*ldb+n];  1: B[k][n] = B[n*ldb+k]
+    float *C = nullptr;
+    int64_t ldc = 0;
+    float alpha = 1.0f, beta = 0.0f;
+    int upper_only = 0;  // write only C[m][n] with m <= n (skip tiles below the diagonal)
+    int a_upper = 0;     // A upper triangular: A[m][k] == 0 for k < m (K range trimmed)
+    int b_upper = 0;     // B upper triangular: B[k][n] == 0 for k > n (K range trimmed)
+    int batch = 1;       // blockIdx.z; operands advance by the strides below
+    int64_t strideA = 0, strideB = 0, strideC = 0;
+    // EPI_DOT: instead of storing, partial[tile] = sum over the tile of
+    // (op(A) op(B))[m][n] * Dm[m*ldd+n] in fp64 (one double per workgroup).
+    int epilogue = EPI_STORE;
+    const float *Dm = nullptr;
+    int64_t ldd = 0;
+    double *partial = nullptr;
+};
+
+constexpr int kGemmTile = 128;
+int64_t gemm_num_tiles(const GemmDesc &g);
+hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Hessian (hessian.hip)
+// ---------------------------------------------------------------------------
+size_t hessian_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt);
+hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, int64_t d_in, int64_t n_tok,
+                       int64_t ldx, void *ws, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Prepare (prepare.hip)
+// ---------------------------------------------------------------------------
+size_t prepare_ws_bytes(int64_t d_in);
+hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float damp_rel, int act_order, float *U,
+                       int32_t *perm, int32_t *info, void *ws, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Quantization (quantize.hip)
+// ---------------------------------------------------------------------------
+size_t quantize_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c);
+int quantize_supported(const gptq_config &c, int64_t d_in);
+hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
+                        const gptq_config &c, uint8_t *codes, float *scales, float *zeros, int32_t *g_idx,
+                        void *ws, hipStream_t s);
+hipError_t run_rtn(const float *W, int64_t d_out, int64_t d_in, const gptq_config &c, uint8_t *codes,
+                   float *scales, float *zeros, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Loss (loss.hip)
+// ---------------------------------------------------------------------------
+size_t loss_ws_bytes(int64_t d_out, int64_t d_in);
+hipError_t run_loss(const float *W, const uint8_t *codes, const float *scales, const float *zeros,
+                    const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in, int32_t group_size,
+                    double *loss, void *ws, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gptq
