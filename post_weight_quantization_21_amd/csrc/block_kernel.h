@@ -1,0 +1,199 @@
+// Column-pass batch kernel of GPTQ (page "PTQ 权重量化：从 GPTQ 到 AWQ", GPTQ
+// section: each quantized column's error goes onto the not-yet-quantized
+// columns through the matching row of the inverse Hessian factor).
+//
+// Four lanes per output row.  The row's BT weights of the batch stay in
+// registers (BT/4 per lane) for the whole batch; the BT x BT block of U sits
+// in LDS.  For each column j:
+// fit the group grid when j starts a group (GT > 0: from the current
+// weights; GT == 0: the grid was fitted before the batch), quantize, form
+// e = (w_j - w_hat_j) / U[j][j], update w_k -= e U[j][k] for the batch's later
+// columns, and store -e into E^T for the trailing matrix-core update.  The
+// unrolled column loop is branch-free: the LDS copy of U is zero on and below
+// the diagonal, so every lane can run the same update; columns past the batch
+// end see zero weights and a zero U block, so they change nothing and are
+// never stored.
+#pragma once
+
+#include "block_args.h"
+#include "quant_grid.h"
+
+namespace gptq {
+
+// Quad helpers (4 consecutive lanes own one row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Value of lane `src_lane` of each quad (src_lane is a constant after unrolling).
+__device__ __forceinline__ float quad_bcast(float v, int src_lane) {
+    switch (src_lane) {
+    case 0: return dpp_f<0x00>(v);
+    case 1: return dpp_f<0x55>(v);
+    case 2: return dpp_f<0xAA>(v);
+    default: return dpp_f<0xFF>(v);
+    }
+}
+__device__ __forceinline__ float quad_xor1(float v) { return dpp_f<0xB1>(v); }  // quad_perm(1,0,3,2)
+__device__ __forceinline__ float quad_xor2(float v) { return dpp_f<0x4E>(v); }  // quad_perm(2,3,0,1)
+
+constexpr int kRowLanes = 4;                           // lanes per output row
+constexpr int kBlockRows = kBlockThreads / kRowLanes;  // rows per workgroup
+
+// Each output row is owned by a quad of lanes; lane q of the quad keeps
+// columns q, q+4, q+8, ... of the batch in registers.  Column j's owner
+// broadcasts the weight to its quad (DPP), all four lanes quantize it (same
+// result), and each lane pushes the error onto its own later columns.
+template <int BT, int GT>
+__global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(BlockArgs a) {
+    constexpr int CPL = BT / kRowLanes;
+    __shared__ float us[BT][BT];  // U block, strictly lower part and diagonal zero
+    __shared__ float inv_d[BT];
+    __shared__ int32_t pcol[BT];
+    const int tid = threadIdx.x;
+    const int nc = a.ncols;
+    {
+        const float *src = a.U + a.c0 * a.ldu + a.c0;
+        const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
+        for (int e4 = tid; e4 < BT * BT / 4; e4 += kBlockThreads) {
+            const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i < nc) {
+                if (vec) {
+                    v = *reinterpret_cast<const float4 *>(src + i * a.ldu + k);
+                } else {
+                    if (k + 0 < nc) v.x = src[i * a.ldu + k + 0];
+                    if (k + 1 < nc) v.y = src[i * a.ldu + k + 1];
+                    if (k + 2 < nc) v.z = src[i * a.ldu + k + 2];
+                    if (k + 3 < nc) v.w = src[i * a.ldu + k + 3];
+                }
+            }
+            if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
+            if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
+            if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
+            if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
+            v.x = (k + 0 > i) ? v.x : 0.0f;
+            v.y = (k + 1 > i) ? v.y : 0.0f;
+            v.z = (k + 2 > i) ? v.z : 0.0f;
+            v.w = (k + 3 > i) ? v.w : 0.0f;
+            *reinterpret_cast<float4 *>(&us[i][k]) = v;
+        }
+    }
+    if (tid < BT) {
+        const int64_t k = a.c0 + (tid < nc ? tid : 0);
+        pcol[tid] = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + tid);
+    }
+    __syncthreads();
+
+    const int q = tid & (kRowLanes - 1);
+    const int64_t r = (int64_t)blockIdx.x * kBlockRows + (tid >> 2);
+    const bool active = r < a.d_out;
+    float *wrow = a.W + r * a.ldw + a.c0;
+    float w[CPL];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int k = q + kRowLanes * t;
+        w[t] = (active && k < nc) ? wrow[k] : 0.0f;
+    }
+
+    Grid gr = grid_make(0.0f, 0.0f, 0.0f, a.bits, a.sym);
+    if constexpr (GT == 0) {
+        if (active) {
+            const int64_t gi = a.c0 / a.g;
+            gr = grid_from_stored(a.scales[r * a.ng + gi], a.zeros[r * a.ng + gi], a.bits, a.sym);
+        }
+    }
+    constexpr int NG = GT > 0 ? BT / GT : 1;
+    float g_s[NG], g_z[NG];
+    uint32_t cw[(CPL + 3) / 4];
+#pragma unroll
+    for (int t = 0; t < (CPL + 3) / 4; ++t) cw[t] = 0u;
+    float *et = a.Et + r;  // rows past d_out land in the padding of E^T
+
+#pragma unroll
+    for (int j = 0; j < BT; ++j) {
+        const int oq = j & (kRowLanes - 1), ot = j / kRowLanes;
+        if constexpr (GT > 0) {
+            if (j % GT == 0) {
+                float amax = 0.0f, lo = 0.0f, hi = 0.0f;
+#pragma unroll
+                for (int t = j / kRowLanes; t < (j + GT) / kRowLanes; ++t) {
+                    amax = fmaxf(amax, fabsf(w[t]));
+                    lo = fminf(lo, w[t]);
+                    hi = fmaxf(hi, w[t]);
+                }
+                amax = fmaxf(amax, quad_xor1(amax));
+                lo = fminf(lo, quad_xor1(lo));
+                hi = fmaxf(hi, quad_xor1(hi));
+                amax = fmaxf(amax, quad_xor2(amax));
+                lo = fminf(lo, quad_xor2(lo));
+                hi = fmaxf(hi, quad_xor2(hi));
+                gr = grid_make(amax, lo, hi, a.bits, a.sym);
+                g_s[j / GT] = gr.s;
+                g_z[j / GT] = gr.zero;
+            }
+        }
+        const float wj = quad_bcast(w[ot], oq);
+        const float code = grid_code(wj, gr);
+        const float wh = grid_dequant(code, gr);
+        const float e = (wj - wh) * inv_d[j];
+        cw[ot / 4] |= (q == oq ? (uint32_t)code : 0u) << (8 * (ot & 3));
+        et[(int64_t)j * a.ldet] = -e;
+#pragma unroll
+        for (int t = ot; t < CPL; ++t) w[t] = fmaf(-e, us[j][q + kRowLanes * t], w[t]);
+    }
+
+    if (!active) return;
+    if constexpr (GT > 0) {
+        if (q == 0) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                if (g * GT < nc) {
+                    const int64_t gi = (a.c0 + g * GT) / a.g;
+                    a.scales[r * a.ng + gi] = g_s[g];
+                    a.zeros[r * a.ng + gi] = g_z[g];
+                }
+        }
+    }
+    // w[t] is never touched after its column is quantized: it is the value at quantization time.
+    uint8_t *crow = a.codes + r * a.ldc;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int k = q + kRowLanes * t;
+        if (k < nc) {
+            wrow[k] = w[t];
+            crow[pcol[k]] = (uint8_t)(cw[t / 4] >> (8 * (t & 3)));
+        }
+    }
+}
+
+template <int BT>
+hipError_t launch_block_bt(const BlockArgs &a, int gt, hipStream_t s) {
+    if (!a.Et || !a.W || !a.U || !a.codes) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)ceil_div(a.d_out, kBlockRows);
+    switch (gt) {
+    case 0:
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+        break;
+    case 32:
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 32>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+        break;
+    case 64:
+        if constexpr (BT >= 64) {
+            hipLaunchKernelGGL((gptq_block_kernel<BT, 64>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+            break;
+        }
+        return hipErrorInvalidValue;
+    case 128:
+        if constexpr (BT >= 128) {
+            hipLaunchKernelGGL((gptq_block_kernel<BT, 128>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+            break;
+        }
+        return hipErrorInvalidValue;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gptq

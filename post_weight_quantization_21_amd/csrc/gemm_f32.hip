@@ -124,6 +124,22 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g, int vec_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // C values are fetched before the K loop so their latency hides behind the
+    // matrix-core work; every store comes after every load of the tile.
+    float cold[2][2][16];
+    if (EPI == EPI_STORE && g.beta != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+                    cold[i][j][r] = (m < g.M && n < g.N) ? C[m * g.ldc + n] : 0.0f;
+                }
+    }
+
     if (kbeg < kend) {
         float4 ra[4], rb[4];
         la.load(kbeg, kend, tid, ra);
@@ -169,10 +185,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g, int vec_
                     const int64_t m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
                     const int64_t n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
                     if (m < g.M && n < g.N && (!g.upper_only || m <= n)) {
-                        float *dst = C + m * g.ldc + n;
                         float v = g.alpha * acc[i][j][r];
-                        if (g.beta != 0.0f) v += g.beta * *dst;
-                        *dst = v;
+                        if (g.beta != 0.0f) v += g.beta * cold[i][j][r];
+                        C[m * g.ldc + n] = v;
                     }
                 }
     } else {

@@ -139,21 +139,42 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
         }
     }
 
+    if (out_partial) {
+        const int64_t t = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        float *dst = out_partial + t * (TS * TS);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int li = wm * 64 + i * 32 + mfma32_row(r, lane);
+                    const int lj = wn * 64 + j * 32 + mfma32_col(lane);
+                    dst[li * TS + lj] = acc[i][j][r];
+                }
+        return;
+    }
+    // H += 2 acc: all reads first, then all writes (no load waits behind a store).
+    float hold[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int li = wm * 64 + i * 32 + mfma32_row(r, lane);
-                const int lj = wn * 64 + j * 32 + mfma32_col(lane);
-                if (out_partial) {
-                    const int64_t t = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-                    out_partial[t * (TS * TS) + li * TS + lj] = acc[i][j][r];
-                } else {
-                    const int64_t gi = r0 + li, gj = c0 + lj;
-                    if (gi < d && gj < d && gi <= gj) H[gi * d + gj] += 2.0f * acc[i][j][r];
-                }
+                const int64_t gi = r0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+                const int64_t gj = c0 + wn * 64 + j * 32 + mfma32_col(lane);
+                hold[i][j][r] = (gi < d && gj < d && gi <= gj) ? H[gi * d + gj] : 0.0f;
+            }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t gi = r0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+                const int64_t gj = c0 + wn * 64 + j * 32 + mfma32_col(lane);
+                if (gi < d && gj < d && gi <= gj) H[gi * d + gj] = hold[i][j][r] + 2.0f * acc[i][j][r];
             }
 }
 

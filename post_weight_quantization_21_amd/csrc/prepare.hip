@@ -85,62 +85,91 @@ __global__ __launch_bounds__(kThreads) void iota_kernel(int32_t *__restrict__ p,
 }
 
 // UL-Cholesky of the diagonal block A[k0:k0+nb, k0:k0+nb] (upper storage) and
-// the inverse of its factor.  One workgroup.
-//   factor:  for j = nb-1 .. 0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
-//            c_ii' -= t_ij t_i'j  (i <= i' < j)
-//   inverse: V = T^-1 row by row from the bottom: V_ii = 1/t_ii,
-//            V_ic = -V_ii * sum_{m=i+1..c} t_im V_mc  (c > i)
-// Writes T into A's block and V into U's block (strictly lower parts = 0).
-__global__ __launch_bounds__(kThreads) void panel_kernel(float *__restrict__ A, float *__restrict__ U, int64_t d,
-                                                         int64_t k0, int nb, int32_t *__restrict__ info) {
-    __shared__ float c[NB][NB + 1];
-    __shared__ float v[NB][NB + 1];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < NB * NB; e += kThreads) {
-        const int i = e / NB, j = e % NB;
-        c[i][j] = (i < nb && j < nb && i <= j) ? A[(k0 + i) * d + k0 + j] : 0.0f;
-        v[i][j] = 0.0f;
+// the inverse of its factor, on one wave64 with no block barriers.
+//   factor:  lane i holds row i of the block in registers.  For j = NB-1..0:
+//            t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
+//            c_ii' -= t_ij t_i'j (i' < j)  -- column j is shared through LDS.
+//   inverse: lane c holds column c of V = T^-1.  For i = NB-1..0:
+//            V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
+//            reading row i of T from LDS with wave-uniform addresses.
+// Rows and columns past nb are padded with the identity.  Writes T into A's
+// block and V into U's block (strictly lower parts = 0).
+__global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, float *__restrict__ U, int64_t d,
+                                                      int64_t k0, int nb, int32_t *__restrict__ info) {
+    __shared__ float col[NB];
+    __shared__ float tr[NB][NB + 4];
+    const int lane = threadIdx.x;
+    // Block into LDS (coalesced rows), identity padding past nb.
+    for (int e = lane; e < NB * NB; e += kWave) {
+        const int i = e / NB, m = e % NB;
+        const bool in = i < nb && m < nb;
+        tr[i][m] = in ? (i <= m ? A[(k0 + i) * d + k0 + m] : 0.0f) : (i == m ? 1.0f : 0.0f);
     }
     __syncthreads();
-    for (int j = nb - 1; j >= 0; --j) {
-        if (tid == 0) {
-            float p = c[j][j];
-            if (!(p > 0.0f)) {
-                atomicCAS(info, 0, (int32_t)(k0 + j + 1));
-                p = 1.0f;
-            }
-            c[j][j] = sqrtf(p);
-        }
-        __syncthreads();
-        const float inv = 1.0f / c[j][j];
-        for (int i = tid; i < j; i += kThreads) c[i][j] *= inv;
-        __syncthreads();
-        for (int e = tid; e < j * j; e += kThreads) {
-            const int i = e / j, i2 = e % j;
-            if (i <= i2) c[i][i2] -= c[i][j] * c[i2][j];
-        }
-        __syncthreads();
-    }
-    // Inverse: TPC threads per column, strided partial dot products.
-    constexpr int TPC = kThreads / NB;
-    const int col = tid / TPC, q = tid % TPC;
-    for (int i = nb - 1; i >= 0; --i) {
-        const float vii = 1.0f / c[i][i];
-        float s = 0.0f;
-        if (col > i && col < nb)
-            for (int m = i + 1 + q; m <= col; m += TPC) s += c[i][m] * v[m][col];
+    float c[NB];
 #pragma unroll
-        for (int off = 1; off < TPC; off <<= 1) s += __shfl_xor(s, off);
-        if (q == 0) {
-            if (col == i) v[i][i] = vii;
-            else if (col > i && col < nb) v[i][col] = -vii * s;
-        }
-        __syncthreads();
+    for (int m = 0; m < NB; ++m) c[m] = tr[lane][m];
+    int32_t first_bad = 0;
+#pragma unroll
+    for (int j = NB - 1; j >= 0; --j) {
+        col[lane] = c[j];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the column is in LDS
+        __builtin_amdgcn_wave_barrier();
+        const float p0 = col[j];
+        const bool bad = !(p0 > 0.0f);
+        first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(k0 + j + 1) : first_bad;
+        // hardware sqrt / reciprocal (about 1 ulp): the factor only has to be accurate,
+        // and branch-free selects keep the whole wave on one path.
+        const float tjj = __builtin_amdgcn_sqrtf(bad ? 1.0f : p0);
+        const float inv = __builtin_amdgcn_rcpf(tjj);
+        float t = c[j] * inv;
+        t = lane == j ? tjj : t;
+        t = lane > j ? 0.0f : t;
+        c[j] = t;
+        __builtin_amdgcn_wave_barrier();
+        col[lane] = t;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i2 = 0; i2 < j; ++i2) c[i2] = fmaf(-t, col[i2], c[i2]);
+        __builtin_amdgcn_wave_barrier();
     }
-    for (int e = tid; e < nb * nb; e += kThreads) {
-        const int i = e / nb, j = e % nb;
-        if (i <= j) A[(k0 + i) * d + k0 + j] = c[i][j];
-        U[(k0 + i) * d + k0 + j] = (i <= j) ? v[i][j] : 0.0f;
+    if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
+    // T (upper part) to LDS for the inverse and for the coalesced store into A.
+#pragma unroll
+    for (int m = 0; m < NB; ++m) tr[lane][m] = m >= lane ? c[m] : 0.0f;
+    __syncthreads();
+    for (int e = lane; e < nb * NB; e += kWave) {
+        const int i = e / NB, m = e % NB;
+        if (m < nb && m >= i) A[(k0 + i) * d + k0 + m] = tr[i][m];
+    }
+    float v[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) v[m] = 0.0f;
+#pragma unroll
+    for (int i = NB - 1; i >= 0; --i) {
+        const float rii = __builtin_amdgcn_rcpf(tr[i][i]);
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+        for (int m = i + 1; m < NB; ++m) {
+            const float prod = tr[i][m] * v[m];
+            if ((m & 3) == 0) s0 += prod;
+            else if ((m & 3) == 1) s1 += prod;
+            else if ((m & 3) == 2) s2 += prod;
+            else s3 += prod;
+        }
+        float x = -rii * ((s0 + s1) + (s2 + s3));
+        x = lane == i ? rii : x;
+        v[i] = lane < i ? 0.0f : x;
+    }
+    __syncthreads();
+    // Column `lane` of V into LDS, then coalesced rows into U (zero below the diagonal).
+#pragma unroll
+    for (int m = 0; m < NB; ++m) tr[m][lane] = v[m];
+    __syncthreads();
+    for (int e = lane; e < nb * NB; e += kWave) {
+        const int i = e / NB, m = e % NB;
+        if (m < nb) U[(k0 + i) * d + k0 + m] = tr[i][m];
     }
 }
 
@@ -214,7 +243,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     for (int64_t kb = nblk - 1; kb >= 0; --kb) {
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kThreads), 0, s, A, U, d, k0, nb, info);
+        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, k0, nb, info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (k0 == 0) break;
         // Panel solve: A[0:k0, k0:k0+nb] <- A[0:k0, k0:k0+nb] V^T  (V = T_kk^-1 in U's block)

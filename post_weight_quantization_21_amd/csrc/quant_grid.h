@@ -7,59 +7,71 @@
 // (v_rndne_f32), the rounding of the pages' torch.round.  Readings of points
 // the pages leave open: the asymmetric range always contains 0
 // (lo = min(min x, 0), hi = max(max x, 0)); a zero-width group gets scale 1.
+//
+// Both grids are evaluated by one branch-free formula,
+//     code = clamp(rint(x / s + zoff), qlo, qhi) + zadd,
+// symmetric: zoff = 0, [qlo, qhi] = [-qmax, qmax], zadd = 2^(b-1);
+// asymmetric: zoff = zero, [qlo, qhi] = [0, 2^b - 1], zadd = 0.
+// (x/s + 0 equals x/s, and a -0 that would become +0 is clamped and shifted to
+// the same code, so the symmetric case is exactly the printed rint(x/s).)
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace gptq {
 
-struct GridSpec {
-    int bits;
-    int sym;
+struct Grid {
+    float s, zoff, qlo, qhi, zadd, zero;
 };
 
-// Symmetric grid from max|x| of the group.
-__device__ __forceinline__ void grid_sym(float amax, int bits, float &scale, float &zero) {
+// Grid of a group from its statistics: amax = max|x|, lo = min(min x, 0), hi = max(max x, 0).
+__device__ __forceinline__ Grid grid_make(float amax, float lo, float hi, int bits, int sym) {
 #pragma clang fp contract(off)
-    const float qmax = (float)((1 << (bits - 1)) - 1);
-    float s = amax / qmax;
-    scale = (s == 0.0f) ? 1.0f : s;
-    zero = (float)(1 << (bits - 1));
+    Grid g;
+    const float half = (float)(1 << (bits - 1));
+    const float qmax_s = half - 1.0f;
+    const float maxq = (float)((1 << bits) - 1);
+    // symmetric
+    float ss = amax / qmax_s;
+    ss = (ss == 0.0f) ? 1.0f : ss;
+    // asymmetric
+    float sa = (hi - lo) / maxq;
+    const bool za = (sa == 0.0f);
+    sa = za ? 1.0f : sa;
+    float z = za ? 0.0f : fminf(fmaxf(rintf(-lo / sa), 0.0f), maxq);
+    g.s = sym ? ss : sa;
+    g.zoff = sym ? 0.0f : z;
+    g.qlo = sym ? -qmax_s : 0.0f;
+    g.qhi = sym ? qmax_s : maxq;
+    g.zadd = sym ? half : 0.0f;
+    g.zero = sym ? half : z;
+    return g;
 }
 
-// Asymmetric grid from the group's min and max (both already clamped to span 0).
-__device__ __forceinline__ void grid_asym(float lo, float hi, int bits, float &scale, float &zero) {
-#pragma clang fp contract(off)
-    const float maxq = (float)((1 << bits) - 1);
-    float s = (hi - lo) / maxq;
-    if (s == 0.0f) {
-        scale = 1.0f;
-        zero = 0.0f;
-    } else {
-        float z = rintf(-lo / s);
-        scale = s;
-        zero = fminf(fmaxf(z, 0.0f), maxq);
-    }
+// A grid given by its stored scale and zero point.
+__device__ __forceinline__ Grid grid_from_stored(float s, float zero, int bits, int sym) {
+    Grid g;
+    const float half = (float)(1 << (bits - 1));
+    g.s = s;
+    g.zoff = sym ? 0.0f : zero;
+    g.qlo = sym ? -(half - 1.0f) : 0.0f;
+    g.qhi = sym ? (half - 1.0f) : (float)((1 << bits) - 1);
+    g.zadd = sym ? half : 0.0f;
+    g.zero = zero;
+    return g;
 }
 
 // Stored code (as a float holding a small integer).
-__device__ __forceinline__ float grid_code(float x, float scale, float zero, int bits, int sym) {
+__device__ __forceinline__ float grid_code(float x, const Grid &g) {
 #pragma clang fp contract(off)
-    if (sym) {
-        const float qmax = (float)((1 << (bits - 1)) - 1);
-        float q = rintf(x / scale);
-        q = fminf(fmaxf(q, -qmax), qmax);
-        return q + zero;
-    }
-    const float maxq = (float)((1 << bits) - 1);
-    float q = rintf(x / scale + zero);
-    return fminf(fmaxf(q, 0.0f), maxq);
+    const float q = rintf(x / g.s + g.zoff);
+    return fminf(fmaxf(q, g.qlo), g.qhi) + g.zadd;
 }
 
-// Rounded to fp32 on its own (never fused into a following add), like the stored format.
-__device__ __forceinline__ float grid_dequant(float code, float scale, float zero) {
+// Dequantized value, rounded to fp32 on its own (never fused into a following add).
+__device__ __forceinline__ float grid_dequant(float code, const Grid &g) {
 #pragma clang fp contract(off)
-    return (code - zero) * scale;
+    return (code - g.zero) * g.s;
 }
 
 }  // namespace gptq

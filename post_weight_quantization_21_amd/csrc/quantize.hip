@@ -12,148 +12,13 @@
 //                  columns of the batch, store -e into E^T.
 //   trailing GEMM  W[:, c0+B:] += (-E) U[c0:c0+B, c0+B:]  on fp32 matrix cores.
 // Rows are independent, so no lane ever talks to another.
-#include "common.h"
+#include "block_args.h"
 #include "quant_grid.h"
 
 namespace gptq {
 namespace {
 
 constexpr int kThreads = 256;
-
-// Column indices read from a permutation are clamped into [0, n) so that a
-// malformed permutation can only give wrong results, never a wild access.
-__device__ __forceinline__ int32_t clamp_col(int32_t c, int64_t n) {
-    return c < 0 ? 0 : (c >= n ? (int32_t)(n - 1) : c);
-}
-
-struct BlockArgs {
-    float *W;
-    int64_t ldw, d_out, c0;
-    int ncols;
-    const float *U;
-    int64_t ldu;
-    float *Et;  // [B][d_out], holds -e
-    uint8_t *codes;
-    int64_t ldc;
-    const int32_t *perm;
-    float *scales, *zeros;
-    int64_t ng, g;
-    int bits, sym, vec;
-};
-
-template <int BT, int GT>
-__global__ __launch_bounds__(kThreads) void gptq_block_kernel(BlockArgs a) {
-    __shared__ float us[BT][BT];
-    __shared__ float inv_d[BT];
-    __shared__ int32_t pcol[BT];
-    const int tid = threadIdx.x;
-    const int nc = a.ncols;
-    for (int e = tid; e < BT * BT; e += kThreads) {
-        const int i = e / BT, k = e % BT;
-        us[i][k] = (i < nc && k < nc && i <= k) ? a.U[(a.c0 + i) * a.ldu + a.c0 + k] : 0.0f;
-    }
-    if (tid < BT) {
-        const int64_t k = a.c0 + (tid < nc ? tid : 0);
-        pcol[tid] = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + tid);
-    }
-    __syncthreads();
-    if (tid < BT) inv_d[tid] = tid < nc ? 1.0f / us[tid][tid] : 0.0f;
-    __syncthreads();
-
-    const int64_t r = (int64_t)blockIdx.x * kThreads + tid;
-    const bool active = r < a.d_out;
-    float w[BT];
-    float *wrow = a.W + r * a.ldw + a.c0;
-#pragma unroll
-    for (int j = 0; j < BT; j += 4) {
-        if (active && a.vec && j + 4 <= nc) {
-            const float4 v = *reinterpret_cast<const float4 *>(wrow + j);
-            w[j] = v.x;
-            w[j + 1] = v.y;
-            w[j + 2] = v.z;
-            w[j + 3] = v.w;
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) w[j + t] = (active && j + t < nc) ? wrow[j + t] : 0.0f;
-        }
-    }
-
-    float s = 1.0f, z = 0.0f;
-    if constexpr (GT == 0) {
-        if (active) {
-            const int64_t gi = a.c0 / a.g;
-            s = a.scales[r * a.ng + gi];
-            z = a.zeros[r * a.ng + gi];
-        }
-    }
-    uint32_t cw[BT / 4];
-#pragma unroll
-    for (int j = 0; j < BT / 4; ++j) cw[j] = 0u;
-
-#pragma unroll
-    for (int j = 0; j < BT; ++j) {
-        if (j < nc) {
-            if constexpr (GT > 0) {
-                if (j % GT == 0) {
-                    if (a.sym) {
-                        float amax = 0.0f;
-#pragma unroll
-                        for (int k = j; k < j + GT; ++k) amax = fmaxf(amax, fabsf(w[k]));
-                        grid_sym(amax, a.bits, s, z);
-                    } else {
-                        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-                        for (int k = j; k < j + GT; ++k) {
-                            lo = fminf(lo, w[k]);
-                            hi = fmaxf(hi, w[k]);
-                        }
-                        grid_asym(lo, hi, a.bits, s, z);
-                    }
-                    if (active) {
-                        const int64_t gi = (a.c0 + j) / a.g;
-                        a.scales[r * a.ng + gi] = s;
-                        a.zeros[r * a.ng + gi] = z;
-                    }
-                }
-            }
-            const float code = grid_code(w[j], s, z, a.bits, a.sym);
-            const float wh = grid_dequant(code, s, z);
-            const float e = (w[j] - wh) * inv_d[j];
-            cw[j >> 2] |= ((uint32_t)code) << (8 * (j & 3));
-            if (active) a.Et[(int64_t)j * a.d_out + r] = -e;
-#pragma unroll
-            for (int k = j + 1; k < BT; ++k) w[k] = fmaf(-e, us[j][k], w[k]);
-        }
-    }
-
-    if (!active) return;
-    // w[j] is never touched after column j is quantized: it is the value at quantization time.
-#pragma unroll
-    for (int j = 0; j < BT; j += 4) {
-        if (a.vec && j + 4 <= nc) {
-            *reinterpret_cast<float4 *>(wrow + j) = make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (j + t < nc) wrow[j + t] = w[j + t];
-        }
-    }
-    uint8_t *crow = a.codes + r * a.ldc;
-    if (!a.perm && a.vec && (a.ldc % 16 == 0) && (a.c0 % 16 == 0)) {
-#pragma unroll
-        for (int j = 0; j < BT; j += 16) {
-            if (j + 16 <= nc) {
-                *reinterpret_cast<uint4 *>(crow + a.c0 + j) = make_uint4(cw[j / 4], cw[j / 4 + 1], cw[j / 4 + 2], cw[j / 4 + 3]);
-            } else {
-                for (int t = j; t < nc && t < j + 16; ++t) crow[a.c0 + t] = (uint8_t)(cw[t >> 2] >> (8 * (t & 3)));
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < BT; ++j)
-            if (j < nc) crow[pcol[j]] = (uint8_t)(cw[j >> 2] >> (8 * (j & 3)));
-    }
-}
 
 // One wave per (row, group): fit the group's grid from W (current values);
 // optionally write the codes (round-to-nearest).  Groups g_first .. g_first+g_count-1.
@@ -179,18 +44,14 @@ __global__ __launch_bounds__(kThreads) void rtn_kernel(const float *__restrict__
         hi = fmaxf(hi, __shfl_xor(hi, off));
         amax = fmaxf(amax, __shfl_xor(amax, off));
     }
-    float s, z;
-    if (sym)
-        grid_sym(amax, bits, s, z);
-    else
-        grid_asym(lo, hi, bits, s, z);
+    const Grid gr = grid_make(amax, lo, hi, bits, sym);
     if (lane == 0) {
-        scales[r * ng + gi] = s;
-        zeros[r * ng + gi] = z;
+        scales[r * ng + gi] = gr.s;
+        zeros[r * ng + gi] = gr.zero;
     }
     if (codes) {
         uint8_t *dst = codes + r * ldc + gi * g;
-        for (int64_t k = lane; k < g; k += kWave) dst[k] = (uint8_t)grid_code(src[k], s, z, bits, sym);
+        for (int64_t k = lane; k < g; k += kWave) dst[k] = (uint8_t)grid_code(src[k], gr);
     }
 }
 
@@ -224,25 +85,21 @@ int group_tile(const gptq_config &c, int64_t d_in) {
     return (g <= c.block_size && c.block_size % g == 0) ? (int)g : 0;
 }
 
-template <int BT>
-hipError_t launch_block(const BlockArgs &a, int gt, unsigned grid, hipStream_t s) {
-    switch (gt) {
-    case 0:
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 0>), dim3(grid), dim3(kThreads), 0, s, a);
-        break;
-    case 32:
-        if constexpr (BT >= 32) hipLaunchKernelGGL((gptq_block_kernel<BT, 32>), dim3(grid), dim3(kThreads), 0, s, a);
-        break;
-    case 64:
-        if constexpr (BT >= 64) hipLaunchKernelGGL((gptq_block_kernel<BT, 64>), dim3(grid), dim3(kThreads), 0, s, a);
-        break;
-    case 128:
-        if constexpr (BT >= 128) hipLaunchKernelGGL((gptq_block_kernel<BT, 128>), dim3(grid), dim3(kThreads), 0, s, a);
-        break;
-    default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+// E^T rows are padded to whole workgroups so the batch kernel stores without a row test.
+int64_t et_ld(int64_t d_out) { return ceil_div(d_out, kBlockThreads) * kBlockThreads; }
+
+// Workspace of the column pass: E^T [B][ldet] and (act-order only) a copy of
+// W for the column gather.
+struct QuantLayout {
+    size_t et_off, wc_off, total;
+};
+
+QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
+    QuantLayout l;
+    l.et_off = 0;
+    l.wc_off = align_up((size_t)c.block_size * (size_t)et_ld(d_out) * sizeof(float), 256);
+    l.total = l.wc_off + (c.act_order ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
+    return l;
 }
 
 }  // namespace
@@ -254,11 +111,7 @@ int quantize_supported(const gptq_config &c, int64_t d_in) {
     return g % c.block_size == 0;
 }
 
-size_t quantize_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c) {
-    size_t b = align_up((size_t)c.block_size * (size_t)d_out * sizeof(float), 256);
-    if (c.act_order) b += align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256);
-    return b;
-}
+size_t quantize_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c) { return quant_layout(d_out, d_in, c).total; }
 
 hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
                         const gptq_config &c, uint8_t *codes, float *scales, float *zeros, int32_t *g_idx,
@@ -267,12 +120,13 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     const int64_t ng = d_in / g;
     const int B = c.block_size;
     const int gt = group_tile(c, d_in);
-    float *Et = static_cast<float *>(ws);
+    const QuantLayout lay = quant_layout(d_out, d_in, c);
+    char *wsb = static_cast<char *>(ws);
+    float *Et = reinterpret_cast<float *>(wsb + lay.et_off);
     hipError_t e;
     const int32_t *pp = c.act_order ? perm : nullptr;
     if (pp) {
-        float *Wc = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                              align_up((size_t)B * (size_t)d_out * sizeof(float), 256));
+        float *Wc = reinterpret_cast<float *>(wsb + lay.wc_off);
         const int64_t n = d_out * d_in, n4 = n / 4;
         hipLaunchKernelGGL(copy_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n4, kThreads), 65536)), dim3(kThreads), 0,
                            s, reinterpret_cast<const float4 *>(W), reinterpret_cast<float4 *>(Wc), n4);
@@ -289,7 +143,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(d_in, kThreads)), dim3(kThreads), 0, s, pp, d_in, g, g_idx);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const unsigned grid = (unsigned)ceil_div(d_out, kThreads);
+    const int64_t ldet = et_ld(d_out);
     const int vec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15) == 0);
     for (int64_t c0 = 0; c0 < d_in; c0 += B) {
         const int nc = (int)std::min<int64_t>(B, d_in - c0);
@@ -300,7 +154,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
                                zeros);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        BlockArgs a;
+        BlockArgs a{};
         a.W = W;
         a.ldw = d_in;
         a.d_out = d_out;
@@ -309,6 +163,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         a.U = U;
         a.ldu = d_in;
         a.Et = Et;
+        a.ldet = ldet;
         a.codes = codes;
         a.ldc = d_in;
         a.perm = pp;
@@ -320,11 +175,11 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         a.sym = c.symmetric ? 1 : 0;
         a.vec = vec;
         if (B == 32)
-            e = launch_block<32>(a, gt, grid, s);
+            e = launch_block_32(a, gt, s);
         else if (B == 64)
-            e = launch_block<64>(a, gt, grid, s);
+            e = launch_block_64(a, gt, s);
         else
-            e = launch_block<128>(a, gt, grid, s);
+            e = launch_block_128(a, gt, s);
         if (e != hipSuccess) return e;
         const int64_t c1 = c0 + nc;
         if (c1 < d_in) {
@@ -333,7 +188,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             t.N = d_in - c1;
             t.K = nc;
             t.A = Et;
-            t.lda = d_out;
+            t.lda = ldet;
             t.a_trans = 1;
             t.B = U + c0 * d_in + c1;
             t.ldb = d_in;
