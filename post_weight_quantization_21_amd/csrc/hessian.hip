@@ -2,9 +2,10 @@
 // 原理与实现详解", §4.1: the layer objective's Hessian is 2 X X^T).
 //
 // bf16 activations: a symmetric rank-k update on gfx950 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  X is [d_in][ldx], one row per
-// channel, tokens contiguous, so both MFMA operands of a tile are row panels of
-// X read along K.  Only tiles on or above the diagonal are computed (the
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate), 256 x 256 tiles per 4-wave
+// workgroup with 128 x 128 per wave (accumulators in AGPRs), so each 16-byte
+// LDS read feeds four MFMAs.  X is [d_in][ldx], one row per channel, tokens
+// contiguous, so both MFMA operands of a tile are row panels of X read along K.  Only tiles on or above the diagonal are computed (the
 // algorithmic d(d+1)/2 * N multiply-adds).  When a layer has too few tiles to
 // fill the chip, tokens are split across workgroups and the partial tiles are
 // summed in a fixed order by a second kernel, so H is bit-reproducible.
@@ -15,22 +16,23 @@
 namespace gptq {
 namespace {
 
-constexpr int TS = 128;        // output tile edge
-constexpr int KT = 64;         // bf16 elements of K per LDS stage
-constexpr int KPAD = KT + 8;   // LDS row length in bf16 (144 B: conflict-free 16 B reads)
+constexpr int TS = 256;        // output tile edge (4 waves, each 128 x 128)
+constexpr int KT = 64;         // bf16 elements of K per LDS stage (8 chunks of 16 B per row)
 constexpr int kThreads = 256;
-constexpr int kTargetBlocks = 1024;
+constexpr int kCUs = 256;
 
+// LDS panel: 256 rows x 128 B, unpadded.  Logical 16-byte chunk c of row r sits
+// at position c ^ (r & 7), so eight consecutive rows read at one logical chunk
+// hit eight different bank groups.
 struct SyrkSmem {
-    uint16_t a[2][TS][KPAD];
-    uint16_t b[2][TS][KPAD];
+    uint4 a[2][TS][KT / 8];
+    uint4 b[2][TS][KT / 8];
 };
 
 __device__ __forceinline__ void tile_of(int64_t t, int nt, int &ti, int &tj) {
     // Upper-triangle tiles in row-major order: row i holds nt - i tiles.
     int i = 0;
     int64_t before = 0;
-    // nt <= 1024 here; a short scan is cheaper than the float root for small nt.
     while (before + (nt - i) <= t) {
         before += nt - i;
         ++i;
@@ -39,158 +41,183 @@ __device__ __forceinline__ void tile_of(int64_t t, int nt, int &ti, int &tj) {
     tj = i + (int)(t - before);
 }
 
-struct PanelLoader {
-    const uint16_t *X;
-    int64_t ldx, d;
-
-    // 128 rows x 64 bf16: 1024 chunks of 8 elements, 4 per thread.
-    __device__ __forceinline__ void load(int64_t row0, int64_t k0, int64_t kend, int tid, uint4 (&r)[4]) const {
+// One stage of a 256-row panel straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l of a wave writes LDS bytes [16 l, 16 l + 16)
+// of the wave's 1 KB window).  Wave w fills rows 64 w .. 64 w + 63, eight rows
+// per instruction; each lane fetches the global chunk that belongs at its LDS
+// position.  Rows past d are clamped to row d-1 (valid memory; those outputs
+// are discarded).
+__device__ __forceinline__ void panel_dma(uint4 (*dst)[KT / 8], const uint16_t *X, int64_t ldx, int64_t d,
+                                          int64_t row0, int64_t k0, int wave, int lane) {
+    const int rr = lane >> 3, pos = lane & 7;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + kThreads * i;
-            const int row = idx >> 3, c = (idx & 7) * 8;
-            const int64_t gr = row0 + row, gk = k0 + c;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gr < d) {
-                const uint16_t *src = X + gr * ldx + gk;
-                if (gk + 8 <= kend) {
-                    v = *reinterpret_cast<const uint4 *>(src);
-                } else if (gk < kend) {
-                    uint16_t tmp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) tmp[e] = (gk + e < kend) ? src[e] : (uint16_t)0;
-                    v.x = tmp[0] | ((uint32_t)tmp[1] << 16);
-                    v.y = tmp[2] | ((uint32_t)tmp[3] << 16);
-                    v.z = tmp[4] | ((uint32_t)tmp[5] << 16);
-                    v.w = tmp[6] | ((uint32_t)tmp[7] << 16);
-                }
-            }
-            r[i] = v;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int row = wave * 64 + i * 8 + rr;
+        const int c = pos ^ (row & 7);
+        int64_t gr = row0 + row;
+        gr = gr < d ? gr : d - 1;
+        const uint16_t *src = X + gr * ldx + k0 + c * 8;
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                         (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 8][0]),
+                                         16, 0, 0);
     }
-    __device__ __forceinline__ static void store(uint16_t (*s)[KPAD], int tid, const uint4 (&r)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + kThreads * i;
-            const int row = idx >> 3, c = (idx & 7) * 8;
-            *reinterpret_cast<uint4 *>(&s[row][c]) = r[i];
-        }
-    }
-};
+}
 
-// grid.x = upper tiles, grid.y = token splits.  out_partial == nullptr: H += 2 acc.
+// The same LDS image from masked register loads (last, partial stage of K).
+__device__ __forceinline__ void panel_tail(uint4 (*dst)[KT / 8], const uint16_t *X, int64_t ldx, int64_t d,
+                                           int64_t row0, int64_t k0, int64_t kend, int wave, int lane) {
+    const int rr = lane >> 3, pos = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = wave * 64 + i * 8 + rr;
+        const int c = pos ^ (row & 7);
+        const int64_t gr = row0 + row, gk = k0 + c * 8;
+        uint16_t tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = (gr < d && gk + e < kend) ? X[gr * ldx + gk + e] : (uint16_t)0;
+        dst[row][pos] = make_uint4(tmp[0] | ((uint32_t)tmp[1] << 16), tmp[2] | ((uint32_t)tmp[3] << 16),
+                                   tmp[4] | ((uint32_t)tmp[5] << 16), tmp[6] | ((uint32_t)tmp[7] << 16));
+    }
+}
+
+// grid.x = splits * tiles (split-major).  Each wave owns a 128 x 128 quarter
+// of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators.
+// out_partial == nullptr: H += 2 acc (upper triangle); else raw partial tile.
 __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx, int64_t d,
-                                                             int64_t n_tok, int64_t kchunk, int nt,
+                                                             int64_t n_tok, int64_t kchunk, int nt, int64_t ntiles,
                                                              float *__restrict__ H, float *__restrict__ out_partial) {
+    const int64_t t_lin = blockIdx.x % ntiles, split = blockIdx.x / ntiles;
     int ti, tj;
-    tile_of(blockIdx.x, nt, ti, tj);
+    tile_of(t_lin, nt, ti, tj);
     const bool diag = ti == tj;
     const int64_t r0 = (int64_t)ti * TS, c0 = (int64_t)tj * TS;
-    const int64_t kbeg = (int64_t)blockIdx.y * kchunk;
+    const int64_t kbeg = split * kchunk;
     const int64_t kend = (kbeg + kchunk) < n_tok ? (kbeg + kchunk) : n_tok;
 
     __shared__ SyrkSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    PanelLoader ld{X, ldx, d};
+    // In a diagonal tile the lower-left quarter lies below the diagonal: it is
+    // computed with the others (uniform control flow) and never stored.
+    const bool idle = diag && wm > wn;
 
-    floatx16 acc[2][2];
+    floatx16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    auto fill = [&](int buf, int64_t k0) {
+        if (k0 + KT <= kend) {
+            panel_dma(sm.a[buf], X, ldx, d, r0, k0, wave, lane);
+            if (!diag) panel_dma(sm.b[buf], X, ldx, d, c0, k0, wave, lane);
+        } else {
+            panel_tail(sm.a[buf], X, ldx, d, r0, k0, kend, wave, lane);
+            if (!diag) panel_tail(sm.b[buf], X, ldx, d, c0, k0, kend, wave, lane);
+        }
+    };
+
     if (kbeg < kend) {
-        uint4 ra[4], rb[4];
-        ld.load(r0, kbeg, kend, tid, ra);
-        if (!diag) ld.load(c0, kbeg, kend, tid, rb);
-        PanelLoader::store(sm.a[0], tid, ra);
-        if (!diag) PanelLoader::store(sm.b[0], tid, rb);
+        fill(0, kbeg);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         int buf = 0;
+        const int row = lane & 31, half = lane >> 5;
         for (int64_t k0 = kbeg; k0 < kend; k0 += KT) {
-            const bool more = k0 + KT < kend;
-            if (more) {
-                ld.load(r0, k0 + KT, kend, tid, ra);
-                if (!diag) ld.load(c0, k0 + KT, kend, tid, rb);
-            }
-            uint16_t(*sa)[KPAD] = sm.a[buf];
-            uint16_t(*sb)[KPAD] = diag ? sm.a[buf] : sm.b[buf];
-            const int row = lane & 31, kh = (lane >> 5) * 8;
+            if (k0 + KT < kend) fill(buf ^ 1, k0 + KT);
+            {
+                uint4(*sa)[KT / 8] = sm.a[buf];
+                uint4(*sb)[KT / 8] = diag ? sm.a[buf] : sm.b[buf];
 #pragma unroll
-            for (int kk = 0; kk < KT; kk += 16) {
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&sa[wm * 64 + row][kk + kh]);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&sa[wm * 64 + 32 + row][kk + kh]);
-                const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sb[wn * 64 + row][kk + kh]);
-                const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&sb[wn * 64 + 32 + row][kk + kh]);
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+                for (int ks = 0; ks < KT / 16; ++ks) {
+                    const int c = 2 * ks + half;
+                    bf16x8 fa[4], fb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ra = wm * 128 + i * 32 + row;
+                        fa[i] = __builtin_bit_cast(bf16x8, sa[ra][c ^ (ra & 7)]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int rb = wn * 128 + j * 32 + row;
+                        fb[j] = __builtin_bit_cast(bf16x8, sb[rb][c ^ (rb & 7)]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                }
             }
-            if (more) {
-                PanelLoader::store(sm.a[buf ^ 1], tid, ra);
-                if (!diag) PanelLoader::store(sm.b[buf ^ 1], tid, rb);
-            }
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             buf ^= 1;
         }
     }
 
     if (out_partial) {
-        const int64_t t = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-        float *dst = out_partial + t * (TS * TS);
+        float *dst = out_partial + (int64_t)blockIdx.x * (TS * TS);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int li = wm * 64 + i * 32 + mfma32_row(r, lane);
-                    const int lj = wn * 64 + j * 32 + mfma32_col(lane);
+                    const int li = wm * 128 + i * 32 + mfma32_row(r, lane);
+                    const int lj = wn * 128 + j * 32 + mfma32_col(lane);
                     dst[li * TS + lj] = acc[i][j][r];
                 }
         return;
     }
-    // H += 2 acc: all reads first, then all writes (no load waits behind a store).
-    float hold[2][2][16];
+    if (idle) return;
+    // H += 2 acc, one 32 x 32 sub-tile at a time: its reads before its writes.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t gi = r0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                const int64_t gj = c0 + wn * 64 + j * 32 + mfma32_col(lane);
-                hold[i][j][r] = (gi < d && gj < d && gi <= gj) ? H[gi * d + gj] : 0.0f;
-            }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j) {
+            float hold[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t gi = r0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                const int64_t gj = c0 + wn * 64 + j * 32 + mfma32_col(lane);
-                if (gi < d && gj < d && gi <= gj) H[gi * d + gj] = hold[i][j][r] + 2.0f * acc[i][j][r];
+                const int64_t gi = r0 + wm * 128 + i * 32 + mfma32_row(r, lane);
+                const int64_t gj = c0 + wn * 128 + j * 32 + mfma32_col(lane);
+                hold[r] = (gi < d && gj < d && gi <= gj) ? H[gi * d + gj] : 0.0f;
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t gi = r0 + wm * 128 + i * 32 + mfma32_row(r, lane);
+                const int64_t gj = c0 + wn * 128 + j * 32 + mfma32_col(lane);
+                if (gi < d && gj < d && gi <= gj) H[gi * d + gj] = hold[r] + 2.0f * acc[i][j][r];
+            }
+        }
 }
 
 // H[upper] += 2 * sum_s partial[s][tile]  (fixed summation order).
 __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(const float *__restrict__ part, int splits,
                                                                int64_t ntiles, int nt, int64_t d,
                                                                float *__restrict__ H) {
+    const int64_t t = blockIdx.x / (TS * TS / (kThreads * 4));
+    const int64_t chunk = blockIdx.x % (TS * TS / (kThreads * 4));
     int ti, tj;
-    tile_of(blockIdx.x, nt, ti, tj);
-    for (int e = threadIdx.x; e < TS * TS; e += kThreads) {
-        const int li = e / TS, lj = e % TS;
-        const int64_t gi = (int64_t)ti * TS + li, gj = (int64_t)tj * TS + lj;
-        if (gi >= d || gj >= d || gi > gj) continue;
-        float s = 0.0f;
-        for (int k = 0; k < splits; ++k) s += part[((int64_t)k * ntiles + blockIdx.x) * (TS * TS) + e];
-        H[gi * d + gj] += 2.0f * s;
+    tile_of(t, nt, ti, tj);
+    const int e0 = (int)(chunk * kThreads * 4 + threadIdx.x * 4);
+    const int li = e0 / TS, lj = e0 % TS;
+    const int64_t gi = (int64_t)ti * TS + li, gj0 = (int64_t)tj * TS + lj;
+    if (gi >= d) return;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < splits; ++k) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + ((int64_t)k * ntiles + t) * (TS * TS) + e0);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t gj = gj0 + c;
+        if (gj < d && gi <= gj) H[gi * d + gj] += 2.0f * sv[c];
     }
 }
 
@@ -227,15 +254,28 @@ struct SyrkPlan {
     int64_t kchunk;
 };
 
+// Token splits: pick the count that minimizes an estimate of
+//   rounds of workgroups over the CUs x stages per split  +  partial-tile traffic.
 SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
     SyrkPlan p;
     p.nt = (int)ceil_div(d, TS);
     p.ntiles = (int64_t)p.nt * (p.nt + 1) / 2;
-    int64_t want = ceil_div(kTargetBlocks, p.ntiles);
-    int64_t maxs = n_tok / (8 * KT);  // keep at least 8 stages per split
-    if (want > maxs) want = maxs;
-    if (want < 1) want = 1;
-    p.kchunk = ceil_div(ceil_div(n_tok, want), KT) * KT;
+    const double stage_us = 2.0;                        // one 256x256x64 stage per CU (measured order)
+    const double part_us = 2.0 * TS * TS * 4 / 4.0e6;  // write + read of one partial tile at ~4 TB/s (whole chip)
+    double best = 1e300;
+    int best_s = 1;
+    for (int s = 1; s <= 64; ++s) {
+        const int64_t kc = ceil_div(ceil_div(n_tok, s), KT) * KT;
+        if (s > 1 && kc < 8 * KT) break;
+        const int64_t wgs = p.ntiles * s;
+        const double rounds = (double)ceil_div(wgs, kCUs);
+        const double t = rounds * (double)(kc / KT) * stage_us + (s > 1 ? (double)wgs * part_us : 0.0);
+        if (t < best) {
+            best = t;
+            best_s = s;
+        }
+    }
+    p.kchunk = ceil_div(ceil_div(n_tok, best_s), KT) * KT;
     p.splits = (int)ceil_div(n_tok, p.kchunk);
     if (p.splits < 1) p.splits = 1;
     return p;
@@ -256,13 +296,13 @@ hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, in
     if (dt == GPTQ_DT_BF16) {
         SyrkPlan p = plan_syrk(d, n_tok);
         float *part = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
-        hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)p.ntiles, (unsigned)p.splits), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t *>(X), ldx, d, n_tok, p.kchunk, p.nt, H, part);
+        hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(p.ntiles * p.splits)), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(X), ldx, d, n_tok, p.kchunk, p.nt, p.ntiles, H, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (part) {
-            hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)p.ntiles), dim3(kThreads), 0, s, part, p.splits,
-                               p.ntiles, p.nt, d, H);
+            hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)(p.ntiles * (TS * TS / (kThreads * 4)))), dim3(kThreads),
+                               0, s, part, p.splits, p.ntiles, p.nt, d, H);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

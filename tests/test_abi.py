@@ -50,9 +50,10 @@ def test_workspace_sizes():
     assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, ca) >= 128 * 4096 * 4 + 4096 * 4096 * 4
     assert gq.workspace_bytes(gq.OP_PREPARE, 0, 4096) >= 2 * 4096 * 4096 * 4
     assert gq.workspace_bytes(gq.OP_LOSS, 64, 128) >= 64 * 128 * 4 + 128 * 128 * 4
-    # H tiles alone fill the chip at d_in = 8192: no split over tokens, no workspace
-    assert gq.workspace_bytes(gq.OP_HESSIAN, 0, 8192, 131072) == 0
-    assert gq.workspace_bytes(gq.OP_HESSIAN, 0, 4096, 262144) > 0
+    # a single tile with few tokens is not split over tokens: no workspace
+    assert gq.workspace_bytes(gq.OP_HESSIAN, 0, 128, 512) == 0
+    # few tiles and many tokens: token splits with partial tiles in the workspace
+    assert gq.workspace_bytes(gq.OP_HESSIAN, 0, 4096, 262144) >= 2 * 136 * 256 * 256 * 4
     with pytest.raises(gq.GptqError) as ei:
         gq.workspace_bytes(9, 1, 1)
     assert ei.value.status == gq.ERR_INVALID_ARG
