@@ -36,7 +36,7 @@ CFLAGS = [
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=1200)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:

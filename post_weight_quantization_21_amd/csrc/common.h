@@ -55,6 +55,11 @@ constexpr int kGemmTile = 128;
 int64_t gemm_num_tiles(const GemmDesc &g);
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s);
 
+// Lazy batch update W[:, c1:] += (-E) U[c0:c1, c1:] (trailing.hip).
+// W points at column c1; Et is [K][ldet] (ldet >= M rounded up to 128); Ub points at U[c0][c1].
+hipError_t launch_trailing_update(float *W, int64_t ldw, int64_t M, int64_t N, const float *Et, int64_t ldet, int K,
+                                  const float *Ub, int64_t ldu, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Hessian (hessian.hip)
 // ---------------------------------------------------------------------------
@@ -88,7 +93,7 @@ hipError_t run_loss(const float *W, const uint8_t *codes, const float *scales, c
                     const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in, int32_t group_size,
                     double *loss, void *ws, hipStream_t s);
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace gptq

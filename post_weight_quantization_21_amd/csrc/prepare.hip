@@ -92,18 +92,23 @@ __global__ __launch_bounds__(kThreads) void iota_kernel(int32_t *__restrict__ p,
 //   inverse: lane c holds column c of V = T^-1.  For i = NB-1..0:
 //            V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
 //            reading row i of T from LDS with wave-uniform addresses.
-// Rows and columns past nb are padded with the identity.  Writes T into A's
-// block and V into U's block (strictly lower parts = 0).
+// Rows and columns past nb are padded with the identity.  Writes T into A's block and V into U's block (strictly
+// lower parts = 0).
 __global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, float *__restrict__ U, int64_t d,
                                                       int64_t k0, int nb, int32_t *__restrict__ info) {
     __shared__ float col[NB];
     __shared__ float tr[NB][NB + 4];
     const int lane = threadIdx.x;
-    // Block into LDS (coalesced rows), identity padding past nb.
-    for (int e = lane; e < NB * NB; e += kWave) {
-        const int i = e / NB, m = e % NB;
-        const bool in = i < nb && m < nb;
-        tr[i][m] = in ? (i <= m ? A[(k0 + i) * d + k0 + m] : 0.0f) : (i == m ? 1.0f : 0.0f);
+    // Block into LDS: all loads in flight at once, identity padding past nb.
+    {
+        float ld[NB];
+#pragma unroll
+        for (int it = 0; it < NB; ++it) {
+            const bool in = it < nb && lane < nb;
+            ld[it] = in ? (it <= lane ? A[(k0 + it) * d + k0 + lane] : 0.0f) : (it == lane ? 1.0f : 0.0f);
+        }
+#pragma unroll
+        for (int it = 0; it < NB; ++it) tr[it][lane] = ld[it];
     }
     __syncthreads();
     float c[NB];
@@ -112,30 +117,27 @@ __global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, flo
     int32_t first_bad = 0;
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
-        col[lane] = c[j];
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the column is in LDS
-        __builtin_amdgcn_wave_barrier();
-        const float p0 = col[j];
+        const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));  // pivot, from lane j
         const bool bad = !(p0 > 0.0f);
         first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(k0 + j + 1) : first_bad;
-        // hardware sqrt / reciprocal (about 1 ulp): the factor only has to be accurate,
-        // and branch-free selects keep the whole wave on one path.
+        // hardware sqrt / reciprocal (about 1 ulp): the factor only has to be
+        // accurate; branch-free selects keep the wave on one path.
         const float tjj = __builtin_amdgcn_sqrtf(bad ? 1.0f : p0);
         const float inv = __builtin_amdgcn_rcpf(tjj);
         float t = c[j] * inv;
         t = lane == j ? tjj : t;
         t = lane > j ? 0.0f : t;
         c[j] = t;
-        __builtin_amdgcn_wave_barrier();
-        col[lane] = t;
-        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (j == 0) break;
+        col[lane] = t;  // column j of the factor, shared through LDS
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i2 = 0; i2 < j; ++i2) c[i2] = fmaf(-t, col[i2], c[i2]);
         __builtin_amdgcn_wave_barrier();
     }
     if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
-    // T (upper part) to LDS for the inverse and for the coalesced store into A.
+    // T rows (upper part) to LDS for the inverse and the coalesced store into A.
 #pragma unroll
     for (int m = 0; m < NB; ++m) tr[lane][m] = m >= lane ? c[m] : 0.0f;
     __syncthreads();
@@ -144,8 +146,6 @@ __global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, flo
         if (m < nb && m >= i) A[(k0 + i) * d + k0 + m] = tr[i][m];
     }
     float v[NB];
-#pragma unroll
-    for (int m = 0; m < NB; ++m) v[m] = 0.0f;
 #pragma unroll
     for (int i = NB - 1; i >= 0; --i) {
         const float rii = __builtin_amdgcn_rcpf(tr[i][i]);

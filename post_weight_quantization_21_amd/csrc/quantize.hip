@@ -183,20 +183,8 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         if (e != hipSuccess) return e;
         const int64_t c1 = c0 + nc;
         if (c1 < d_in) {
-            GemmDesc t;
-            t.M = d_out;
-            t.N = d_in - c1;
-            t.K = nc;
-            t.A = Et;
-            t.lda = ldet;
-            t.a_trans = 1;
-            t.B = U + c0 * d_in + c1;
-            t.ldb = d_in;
-            t.C = W + c1;
-            t.ldc = d_in;
-            t.alpha = 1.0f;
-            t.beta = 1.0f;
-            if ((e = launch_gemm_f32(t, s)) != hipSuccess) return e;
+            e = launch_trailing_update(W + c1, d_in, d_out, d_in - c1, Et, ldet, nc, U + c0 * d_in + c1, d_in, s);
+            if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;
