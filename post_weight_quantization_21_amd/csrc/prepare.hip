@@ -7,12 +7,13 @@
 // of U.  Route (2/3 d^3 flops, fp32):
 //   1. H_d = P H P^T + lambda I           (gather + one-workgroup damping)
 //   2. UL-Cholesky H_d = T T^T, T upper   (blocked, from the bottom-right
-//      corner: panel factor on one workgroup, panel solve and symmetric
-//      rank-k update of the rest on matrix cores)
-//   3. U = T^-1                           (the panel kernel also inverts each
-//      diagonal block; off-diagonal blocks are merged pairwise by the block
-//      formula inv([[A, B], [0, C]]) = [[A^-1, -A^-1 B C^-1], [0, C^-1]],
-//      one batched matrix-core product pair per level.)
+//      corner, blocks of 64: one wave factors the diagonal block and inverts
+//      its factor; one fused kernel then solves the block's panel and applies
+//      the rank-64 update to the leading block on matrix cores)
+//   3. U = T^-1                           (the off-diagonal blocks are merged
+//      pairwise by the block formula inv([[A, B], [0, C]]) =
+//      [[A^-1, -A^-1 B C^-1], [0, C^-1]], one batched matrix-core product
+//      pair per level.)
 // Indeed T T^T = H_d gives H_d^-1 = T^-T T^-1 = U^T U with U = T^-1 upper.
 #include "common.h"
 
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void order_kernel(const double *__restric
 
 // A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper triangle.
 __global__ __launch_bounds__(kThreads) void gather_sym_kernel(const float *__restrict__ H, const int32_t *__restrict__ perm,
-                                                              int64_t d, float *__restrict__ A) {
+                                                              int64_t d, int64_t lda, float *__restrict__ A) {
     const int64_t a = blockIdx.y;
     for (int64_t b = a + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < d; b += (int64_t)gridDim.x * kThreads) {
         int64_t pa = perm ? min(max((int64_t)perm[a], (int64_t)0), d - 1) : a;
@@ -54,15 +55,15 @@ __global__ __launch_bounds__(kThreads) void gather_sym_kernel(const float *__res
             pa = pb;
             pb = t;
         }
-        A[a * d + b] = H[pa * d + pb];
+        A[a * lda + b] = H[pa * d + pb];
     }
 }
 
 // lambda = damp_rel * mean(diag A) (fp64, fixed tree); A[i][i] += lambda.  One workgroup.
-__global__ __launch_bounds__(kThreads) void damp_kernel(float *__restrict__ A, int64_t d, float damp_rel) {
+__global__ __launch_bounds__(kThreads) void damp_kernel(float *__restrict__ A, int64_t d, int64_t lda, float damp_rel) {
     __shared__ double red[kThreads];
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < d; i += kThreads) s += (double)A[i * d + i];
+    for (int64_t i = threadIdx.x; i < d; i += kThreads) s += (double)A[i * lda + i];
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(float *__restrict__ A, i
         __syncthreads();
     }
     const float lam = (float)((double)damp_rel * red[0] / (double)d);
-    for (int64_t i = threadIdx.x; i < d; i += kThreads) A[i * d + i] += lam;
+    for (int64_t i = threadIdx.x; i < d; i += kThreads) A[i * lda + i] += lam;
 }
 
 __global__ __launch_bounds__(kThreads) void fill_kernel(float *__restrict__ p, int64_t n, float v) {
@@ -92,28 +93,38 @@ __global__ __launch_bounds__(kThreads) void iota_kernel(int32_t *__restrict__ p,
 //   inverse: lane c holds column c of V = T^-1.  For i = NB-1..0:
 //            V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
 //            reading row i of T from LDS with wave-uniform addresses.
-// Rows and columns past nb are padded with the identity.  Writes T into A's block and V into U's block (strictly
-// lower parts = 0).
-__global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, float *__restrict__ U, int64_t d,
-                                                      int64_t k0, int nb, int32_t *__restrict__ info) {
-    __shared__ float col[NB];
-    __shared__ float tr[NB][NB + 4];
+// Rows and columns past nb are padded with the identity.  Reads the block from
+// the working matrix A and writes V into U's block (strictly lower part = 0);
+// T's diagonal blocks themselves are not needed later.
+// The wave is alone on its CU, so it may take every register; that lets the
+// scheduler keep a whole column of LDS reads in flight.
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d, int64_t lda, int64_t k0, int nb,
+                  int32_t *__restrict__ info) {
+    __shared__ __attribute__((aligned(16))) float col[NB];
+    __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
     const int lane = threadIdx.x;
-    // Block into LDS: all loads in flight at once, identity padding past nb.
+    // Row `lane` of the block straight into registers (16-byte loads, all in
+    // flight at once); rows and columns past nb are padded with the identity.
+    float c[NB];
     {
-        float ld[NB];
+        const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
 #pragma unroll
-        for (int it = 0; it < NB; ++it) {
-            const bool in = it < nb && lane < nb;
-            ld[it] = in ? (it <= lane ? A[(k0 + it) * d + k0 + lane] : 0.0f) : (it == lane ? 1.0f : 0.0f);
+        for (int q = 0; q < NB / 4; ++q) {
+            // chunks past nb are not read (lda is a multiple of 4, so a chunk
+            // that starts below nb ends inside the row)
+            const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+            c[4 * q + 0] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
         }
 #pragma unroll
-        for (int it = 0; it < NB; ++it) tr[it][lane] = ld[it];
+        for (int m = 0; m < NB; ++m) {
+            const bool in = lane < nb && m < nb;
+            c[m] = in ? (m >= lane ? c[m] : 0.0f) : (m == lane ? 1.0f : 0.0f);
+        }
     }
-    __syncthreads();
-    float c[NB];
-#pragma unroll
-    for (int m = 0; m < NB; ++m) c[m] = tr[lane][m];
     int32_t first_bad = 0;
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
@@ -132,27 +143,39 @@ __global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, flo
         col[lane] = t;  // column j of the factor, shared through LDS
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
+        float4 cv[NB / 4];
 #pragma unroll
-        for (int i2 = 0; i2 < j; ++i2) c[i2] = fmaf(-t, col[i2], c[i2]);
+        for (int q = 0; q < (j + 3) / 4; ++q) cv[q] = *reinterpret_cast<const float4 *>(&col[4 * q]);
+        // c[j-1] first: it is the next step's pivot.
+#pragma unroll
+        for (int i2 = j - 1; i2 >= 0; --i2) c[i2] = fmaf(-t, cv[i2 / 4][i2 % 4], c[i2]);
         __builtin_amdgcn_wave_barrier();
     }
     if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
-    // T rows (upper part) to LDS for the inverse and the coalesced store into A.
+    // Rows of T (upper part) to LDS for the inverse.  (T's diagonal blocks are
+    // not needed after this kernel: only their inverses are.)
 #pragma unroll
-    for (int m = 0; m < NB; ++m) tr[lane][m] = m >= lane ? c[m] : 0.0f;
-    __syncthreads();
-    for (int e = lane; e < nb * NB; e += kWave) {
-        const int i = e / NB, m = e % NB;
-        if (m < nb && m >= i) A[(k0 + i) * d + k0 + m] = tr[i][m];
+    for (int q = 0; q < NB / 4; ++q) {
+        float4 v;
+        v.x = (4 * q + 0 >= lane) ? c[4 * q + 0] : 0.0f;
+        v.y = (4 * q + 1 >= lane) ? c[4 * q + 1] : 0.0f;
+        v.z = (4 * q + 2 >= lane) ? c[4 * q + 2] : 0.0f;
+        v.w = (4 * q + 3 >= lane) ? c[4 * q + 3] : 0.0f;
+        *reinterpret_cast<float4 *>(&tr[lane][4 * q]) = v;
     }
+    __syncthreads();
     float v[NB];
 #pragma unroll
     for (int i = NB - 1; i >= 0; --i) {
-        const float rii = __builtin_amdgcn_rcpf(tr[i][i]);
+        // row i of T, from its first 16-byte chunk that holds column i
+        float4 trow[NB / 4];
+#pragma unroll
+        for (int q = i / 4; q < NB / 4; ++q) trow[q] = *reinterpret_cast<const float4 *>(&tr[i][4 * q]);
+        const float rii = __builtin_amdgcn_rcpf(trow[i / 4][i % 4]);
         float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
         for (int m = i + 1; m < NB; ++m) {
-            const float prod = tr[i][m] * v[m];
+            const float prod = trow[m / 4][m % 4] * v[m];
             if ((m & 3) == 0) s0 += prod;
             else if ((m & 3) == 1) s1 += prod;
             else if ((m & 3) == 2) s2 += prod;
@@ -162,22 +185,187 @@ __global__ __launch_bounds__(kWave) void panel_kernel(float *__restrict__ A, flo
         x = lane == i ? rii : x;
         v[i] = lane < i ? 0.0f : x;
     }
-    __syncthreads();
-    // Column `lane` of V into LDS, then coalesced rows into U (zero below the diagonal).
+    // Column `lane` of V into U's block (zero below the diagonal): each store
+    // instruction writes one row, lanes along the columns.
+    if (lane < nb) {
+        float *dst = U + k0 * d + k0 + lane;
 #pragma unroll
-    for (int m = 0; m < NB; ++m) tr[m][lane] = v[m];
-    __syncthreads();
-    for (int e = lane; e < nb * NB; e += kWave) {
-        const int i = e / NB, m = e % NB;
-        if (m < nb) U[(k0 + i) * d + k0 + m] = tr[i][m];
+        for (int m = 0; m < NB; ++m)
+            if (m < nb) dst[m * d] = v[m];
     }
 }
 
-hipError_t merge_level(float *A, float *U, float *T, int64_t d, int64_t s, int64_t p_first, int64_t npairs,
-                       int64_t ni, int64_t nj, hipStream_t st) {
-    // pairs p_first .. p_first+npairs-1 of size (ni rows, nj cols): i0 = 2ps, j0 = i0 + ni.
-    const int64_t i0 = 2 * p_first * s, j0 = i0 + ni;
-    const int64_t stride = 2 * s * (d + 1);
+// Panel solve fused with the symmetric rank-NB update of the leading block,
+// one 128 x 128 upper tile of A[0:k0, 0:k0] per workgroup:
+//   P_i = A[rows i, k0:k0+NB] V^T        (V = T_kk^-1, so P = panel T_kk^-T)
+//   A[i, j] -= P_i P_j^T                  (upper part)
+// and the diagonal tile also writes P_i into the factor T (Tf[rows i, k0:k0+NB]).
+// Both products run on fp32 matrix cores in transposed form, D[col][row], so
+// each lane's accumulators hold four consecutive columns of one row of A.
+constexpr int FT = 128;           // tile edge
+constexpr int FLD = FT + 4;       // LDS row length of the k-major panels
+constexpr int kFThreads = 256;
+
+struct FusedSmem {
+    float pi[NB][FLD];   // panel rows i, k-major (later P_i^T)
+    float pj[NB][FLD];   // panel rows j, k-major (later P_j^T)
+    float vb[NB][NB + 4];  // vb[m][c] = V[c][m]
+};
+
+__device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) {
+    int i = 0;
+    int64_t before = 0;
+    while (before + (nt - i) <= t) {
+        before += nt - i;
+        ++i;
+    }
+    ti = i;
+    tj = i + (int)(t - before);
+}
+
+__global__ __launch_bounds__(kFThreads) void panel_update_kernel(float *__restrict__ A, float *__restrict__ Tf,
+                                                                 const float *__restrict__ U, int64_t d, int64_t lda,
+                                                                 int64_t k0, int nb, int nt) {
+    int ti, tj;
+    tile_upper(blockIdx.x, nt, ti, tj);
+    const bool diag = ti == tj;
+    const int64_t r0 = (int64_t)ti * FT, s0 = (int64_t)tj * FT;
+    __shared__ FusedSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hi = lane >> 5, lo = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Rows of A this tile updates, in the transposed accumulator layout: for
+    // each 32x32 block (si, ri) and g = 0..3, A[r][s .. s+3] with
+    // r = r0 + wm*64 + ri*32 + lo, s = s0 + wn*64 + si*32 + 8g + 4*hi.
+    float4 cold[2][2][4];
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t r = r0 + wm * 64 + ri * 32 + lo;
+                const int64_t sc = s0 + wn * 64 + si * 32 + 8 * g + 4 * hi;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (r < k0 && sc < k0) v = *reinterpret_cast<const float4 *>(A + r * lda + sc);
+                cold[si][ri][g] = v;
+            }
+
+    // Panels (k-major) and V into LDS; columns past the block's nb are zero.
+    for (int e4 = tid; e4 < FT * NB / 4; e4 += kFThreads) {
+        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (m < nb) {  // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed
+            if (r0 + r < k0) a = *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m);
+            if (!diag && s0 + r < k0) b = *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m);
+            if (m + 1 >= nb) a.y = b.y = 0.0f;
+            if (m + 2 >= nb) a.z = b.z = 0.0f;
+            if (m + 3 >= nb) a.w = b.w = 0.0f;
+        }
+        sm.pi[m + 0][r] = a.x;
+        sm.pi[m + 1][r] = a.y;
+        sm.pi[m + 2][r] = a.z;
+        sm.pi[m + 3][r] = a.w;
+        if (!diag) {
+            sm.pj[m + 0][r] = b.x;
+            sm.pj[m + 1][r] = b.y;
+            sm.pj[m + 2][r] = b.z;
+            sm.pj[m + 3][r] = b.w;
+        }
+    }
+    for (int e = tid; e < NB * NB; e += kFThreads) {
+        const int c = e / NB, m = e % NB;
+        sm.vb[m][c] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+    }
+    __syncthreads();
+
+    // P^T[c][r] = sum_m V[c][m] panel[r][m]: wave w covers rows 32w..32w+31, all NB columns.
+    floatx16 pa[2], pb[2];
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) pa[ci][q] = pb[ci][q] = 0.0f;
+#pragma unroll 8
+    for (int m = 0; m < NB; m += 2) {
+        const float v0 = sm.vb[m + hi][lo], v1 = sm.vb[m + hi][32 + lo];
+        const float xa = sm.pi[m + hi][32 * wave + lo];
+        pa[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[0], 0, 0, 0);
+        pa[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, xa, pa[1], 0, 0, 0);
+        if (!diag) {
+            const float xb = sm.pj[m + hi][32 * wave + lo];
+            pb[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[0], 0, 0, 0);
+            pb[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, xb, pb[1], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every wave is done reading the panels
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int c = ci * 32 + mfma32_row(q, lane);
+            sm.pi[c][32 * wave + lo] = pa[ci][q];
+            if (!diag) sm.pj[c][32 * wave + lo] = pb[ci][q];
+        }
+    __syncthreads();
+    float(*pjs)[FLD] = diag ? sm.pi : sm.pj;
+
+    if (diag) {  // this row block's P goes into the factor
+        for (int e = tid; e < FT * NB; e += kFThreads) {
+            const int r = e / NB, c = e % NB;
+            if (r0 + r < k0 && c < nb) Tf[(r0 + r) * lda + k0 + c] = sm.pi[c][r];
+        }
+    }
+
+    // A[r][s] -= sum_c P_i[r][c] P_j[s][c], as D[s][r] = sum_c P_j^T[c][s] P_i^T[c][r].
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < NB; c += 2) {
+        const float y0 = pjs[c + hi][wn * 64 + lo], y1 = pjs[c + hi][wn * 64 + 32 + lo];
+        const float x0 = sm.pi[c + hi][wm * 64 + lo], x1 = sm.pi[c + hi][wm * 64 + 32 + lo];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(y0, x0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(y0, x1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(y1, x0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(y1, x1, acc[1][1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t r = r0 + wm * 64 + ri * 32 + lo;
+                const int64_t sc = s0 + wn * 64 + si * 32 + 8 * g + 4 * hi;
+                if (r >= k0 || sc >= k0) continue;
+                float4 v = cold[si][ri][g];
+                v.x -= acc[si][ri][4 * g + 0];
+                v.y -= acc[si][ri][4 * g + 1];
+                v.z -= acc[si][ri][4 * g + 2];
+                v.w -= acc[si][ri][4 * g + 3];
+                float *dst = A + r * lda + sc;
+                if (!diag || r <= sc) {
+                    *reinterpret_cast<float4 *>(dst) = v;
+                } else {  // diagonal tile: keep only r <= s
+                    if (r <= sc + 0) dst[0] = v.x;
+                    if (r <= sc + 1) dst[1] = v.y;
+                    if (r <= sc + 2) dst[2] = v.z;
+                    if (r <= sc + 3) dst[3] = v.w;
+                }
+            }
+}
+
+// Pairwise merge of inverted diagonal blocks at one level (block size sz):
+//   U12 = -U11 T12 U22   for pairs p_first .. p_first+npairs-1 of (ni x nj) blocks,
+// with T12 read from the factor Tf and the product U11 T12 staged in Tw.
+hipError_t merge_level(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t sz, int64_t p_first,
+                       int64_t npairs, int64_t ni, int64_t nj, hipStream_t st) {
+    const int64_t i0 = 2 * p_first * sz, j0 = i0 + ni;
     GemmDesc g;
     g.batch = (int)npairs;
     g.M = ni;
@@ -186,11 +374,12 @@ hipError_t merge_level(float *A, float *U, float *T, int64_t d, int64_t s, int64
     g.A = U + i0 * d + i0;  // U11 (upper triangular, lower part zero)
     g.lda = d;
     g.a_upper = 1;
-    g.B = A + i0 * d + j0;  // T12
-    g.ldb = d;
-    g.C = T + i0 * d + j0;
-    g.ldc = d;
-    g.strideA = g.strideB = g.strideC = stride;
+    g.B = Tf + i0 * lda + j0;  // T12
+    g.ldb = lda;
+    g.C = Tw + i0 * lda + j0;
+    g.ldc = lda;
+    g.strideA = 2 * sz * (d + 1);
+    g.strideB = g.strideC = 2 * sz * (lda + 1);
     hipError_t e = launch_gemm_f32(g, st);
     if (e != hipSuccess) return e;
     GemmDesc h;
@@ -198,8 +387,8 @@ hipError_t merge_level(float *A, float *U, float *T, int64_t d, int64_t s, int64
     h.M = ni;
     h.N = nj;
     h.K = nj;
-    h.A = T + i0 * d + j0;
-    h.lda = d;
+    h.A = Tw + i0 * lda + j0;
+    h.lda = lda;
     h.B = U + j0 * d + j0;  // U22 (upper triangular)
     h.ldb = d;
     h.b_upper = 1;
@@ -207,18 +396,26 @@ hipError_t merge_level(float *A, float *U, float *T, int64_t d, int64_t s, int64
     h.ldc = d;
     h.alpha = -1.0f;
     h.beta = 0.0f;
-    h.strideA = h.strideB = h.strideC = stride;
+    h.strideA = 2 * sz * (lda + 1);
+    h.strideB = h.strideC = 2 * sz * (d + 1);
     return launch_gemm_f32(h, st);
 }
 
+int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
+
 }  // namespace
 
-size_t prepare_ws_bytes(int64_t d) { return 2 * align_up((size_t)d * (size_t)d * sizeof(float), 256); }
+// Workspace: the working matrix A (Schur complements), the factor Tf and the
+// merge staging Tw, each [d][pad4(d)] fp32.
+size_t prepare_ws_bytes(int64_t d) { return 3 * align_up((size_t)d * (size_t)pad4(d) * sizeof(float), 256); }
 
 hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float damp_rel, int act_order, float *U,
                        int32_t *perm, int32_t *info, void *ws, hipStream_t s) {
+    const int64_t lda = pad4(d);
+    const size_t mat = align_up((size_t)d * (size_t)lda * sizeof(float), 256);
     float *A = static_cast<float *>(ws);
-    float *T = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up((size_t)d * d * sizeof(float), 256));
+    float *Tf = reinterpret_cast<float *>(static_cast<char *>(ws) + mat);
+    float *Tw = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * mat);
     hipError_t e;
     hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, s, info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -230,67 +427,43 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned gx = (unsigned)((d + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(gather_sym_kernel, dim3(gx, (unsigned)d), dim3(kThreads), 0, s, H, act_order ? perm : nullptr,
-                       d, A);
+                       d, lda, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, A, d, damp_rel);
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, A, d, lda, damp_rel);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nU = d * d;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(nU, kThreads), 65536)), dim3(kThreads), 0, s,
                        U, nU, 0.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
+    // UL-Cholesky from the bottom-right corner: factor (and invert) the diagonal
+    // block, then solve its panel and update the leading block in one pass.
     const int64_t nblk = ceil_div(d, NB);
     for (int64_t kb = nblk - 1; kb >= 0; --kb) {
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, k0, nb, info);
+        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, lda, k0, nb, info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (k0 == 0) break;
-        // Panel solve: A[0:k0, k0:k0+nb] <- A[0:k0, k0:k0+nb] V^T  (V = T_kk^-1 in U's block)
-        GemmDesc g;
-        g.M = k0;
-        g.N = nb;
-        g.K = nb;
-        g.A = A + k0;
-        g.lda = d;
-        g.B = U + k0 * d + k0;
-        g.ldb = d;
-        g.b_trans = 1;
-        g.C = A + k0;
-        g.ldc = d;
-        g.alpha = 1.0f;
-        g.beta = 0.0f;
-        if ((e = launch_gemm_f32(g, s)) != hipSuccess) return e;
-        // Rank-nb update of the leading block: A[0:k0, 0:k0] -= P P^T (upper).
-        GemmDesc h;
-        h.M = k0;
-        h.N = k0;
-        h.K = nb;
-        h.A = A + k0;
-        h.lda = d;
-        h.B = A + k0;
-        h.ldb = d;
-        h.b_trans = 1;
-        h.C = A;
-        h.ldc = d;
-        h.alpha = -1.0f;
-        h.beta = 1.0f;
-        h.upper_only = 1;
-        if ((e = launch_gemm_f32(h, s)) != hipSuccess) return e;
+        const int nt = (int)ceil_div(k0, FT);
+        const int64_t ntiles = (int64_t)nt * (nt + 1) / 2;
+        hipLaunchKernelGGL(panel_update_kernel, dim3((unsigned)ntiles), dim3(kFThreads), 0, s, A, Tf, U, d, lda, k0, nb,
+                           nt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // Pairwise merges of the inverted diagonal blocks.
+    // U = T^-1: pairwise merges of the inverted diagonal blocks.
     for (int64_t sz = NB; sz < d; sz *= 2) {
         const int64_t npairs_total = ceil_div(d, 2 * sz);
         int64_t full = d / (2 * sz);
         if (full > 0) {
-            if ((e = merge_level(A, U, T, d, sz, 0, full, sz, sz, s)) != hipSuccess) return e;
+            if ((e = merge_level(Tf, U, Tw, d, lda, sz, 0, full, sz, sz, s)) != hipSuccess) return e;
         }
         if (npairs_total > full) {
             const int64_t i0 = 2 * full * sz;
             const int64_t ni = std::min<int64_t>(sz, d - i0);
             const int64_t nj = d - i0 - ni;
             if (nj > 0)
-                if ((e = merge_level(A, U, T, d, sz, full, 1, ni, nj, s)) != hipSuccess) return e;
+                if ((e = merge_level(Tf, U, Tw, d, lda, sz, full, 1, ni, nj, s)) != hipSuccess) return e;
         }
     }
     return hipSuccess;

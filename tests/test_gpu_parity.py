@@ -76,7 +76,8 @@ def _spd_h(oracle_mod, d, seed, recipe="down_proj_7b"):
     return oracle_mod.hessian(X)
 
 
-@pytest.mark.parametrize("d,act_order", [(64, False), (200, False), (200, True), (1000, True), (2048, False)])
+@pytest.mark.parametrize("d,act_order", [(64, False), (77, True), (130, False), (200, False), (200, True),
+                                         (1000, True), (2048, False)])
 def test_prepare_parity(oracle_mod, d, act_order):
     """U from the GPU vs the oracle's factor of the same fp32 Hessian.
 
