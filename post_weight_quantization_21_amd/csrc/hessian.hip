@@ -5,10 +5,22 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate), 256 x 256 tiles per 4-wave
 // workgroup with 128 x 128 per wave (accumulators in AGPRs), so each 16-byte
 // LDS read feeds four MFMAs.  X is [d_in][ldx], one row per channel, tokens
-// contiguous, so both MFMA operands of a tile are row panels of X read along K.  Only tiles on or above the diagonal are computed (the
-// algorithmic d(d+1)/2 * N multiply-adds).  When a layer has too few tiles to
-// fill the chip, tokens are split across workgroups and the partial tiles are
-// summed in a fixed order by a second kernel, so H is bit-reproducible.
+// contiguous, so both MFMA operands of a tile are row panels of X read along
+// K.  Only tiles on or above the diagonal are computed (the algorithmic
+// d(d+1)/2 * N multiply-adds).  When a layer has too few tiles to fill the
+// chip, tokens are split across workgroups and the partial tiles are summed in
+// a fixed order by a second kernel, so H is bit-reproducible.
+//
+// Pipeline: the panels stream through a ring of four 32-token LDS stages
+// filled by direct global->LDS loads, three stages ahead of the matrix cores;
+// the MFMA operands of the next 16-token step are read from LDS while the
+// current step's MFMAs run; the LDS reads and global->LDS loads are issued one
+// per MFMA.  Work order: workgroup b runs on XCD b % 8.  The upper tiles, in
+// bands of four tile rows taken column by column, are cut into eight
+// contiguous groups, one per XCD, and every XCD walks its group split after
+// split: the tiles an XCD holds at once share a few row panels in its L2, and
+// all XCDs read the same token range at the same time, so L2 misses are
+// mostly served by the shared last-level cache rather than HBM.
 //
 // fp32 activations go through the fp32 matrix-core GEMM (upper tiles only).
 #include "common.h"
@@ -17,20 +29,30 @@ namespace gptq {
 namespace {
 
 constexpr int TS = 256;        // output tile edge (4 waves, each 128 x 128)
-constexpr int KT = 64;         // bf16 elements of K per LDS stage (8 chunks of 16 B per row)
+constexpr int KT = 32;         // tokens per LDS stage: 64 bytes of bf16 per row
+constexpr int CH = KT / 8;     // 16-byte chunks per row and stage
+constexpr int NS = 4;          // LDS ring depth (stages)
+constexpr int BAND = 4;        // tile rows per band of the work order
 constexpr int kThreads = 256;
 constexpr int kCUs = 256;
+constexpr int kXCDs = 8;
 
-// LDS panel: 256 rows x 128 B, unpadded.  Logical 16-byte chunk c of row r sits
-// at position c ^ (r & 7), so eight consecutive rows read at one logical chunk
-// hit eight different bank groups.
+// LDS panels: NS stages x 256 rows x 64 B, unpadded.  Logical chunk c of row r
+// sits at position c ^ swz(r): the 16 rows that one LDS read cycle serves at a
+// common logical chunk then fall into 16 distinct 16-byte bank groups.
 struct SyrkSmem {
-    uint4 a[2][TS][KT / 8];
-    uint4 b[2][TS][KT / 8];
+    uint4 a[NS][TS][CH];
+    uint4 b[NS][TS][CH];
 };
 
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+__device__ __forceinline__ int64_t tile_linear(int ti, int tj, int nt) {
+    return (int64_t)ti * nt - (int64_t)ti * (ti - 1) / 2 + (tj - ti);
+}
+
+// Row-major upper-triangle index -> (ti, tj); row i holds nt - i tiles.
 __device__ __forceinline__ void tile_of(int64_t t, int nt, int &ti, int &tj) {
-    // Upper-triangle tiles in row-major order: row i holds nt - i tiles.
     int i = 0;
     int64_t before = 0;
     while (before + (nt - i) <= t) {
@@ -41,58 +63,111 @@ __device__ __forceinline__ void tile_of(int64_t t, int nt, int &ti, int &tj) {
     tj = i + (int)(t - before);
 }
 
-// One stage of a 256-row panel straight from global memory into LDS
-// (global_load_lds_dwordx4: lane l of a wave writes LDS bytes [16 l, 16 l + 16)
-// of the wave's 1 KB window).  Wave w fills rows 64 w .. 64 w + 63, eight rows
-// per instruction; each lane fetches the global chunk that belongs at its LDS
-// position.  Rows past d are clamped to row d-1 (valid memory; those outputs
-// are discarded).
-__device__ __forceinline__ void panel_dma(uint4 (*dst)[KT / 8], const uint16_t *X, int64_t ldx, int64_t d,
-                                          int64_t row0, int64_t k0, int wave, int lane) {
-    const int rr = lane >> 3, pos = lane & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = wave * 64 + i * 8 + rr;
-        const int c = pos ^ (row & 7);
-        int64_t gr = row0 + row;
-        gr = gr < d ? gr : d - 1;
-        const uint16_t *src = X + gr * ldx + k0 + c * 8;
-        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                         (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 8][0]),
-                                         16, 0, 0);
+// Band order: bands of BAND tile rows; inside a band, column by column, rows
+// top to bottom (only i <= j).
+__device__ __forceinline__ void tile_of_band(int64_t t, int nt, int &ti, int &tj) {
+    int r0 = 0;
+    for (;;) {
+        const int r1 = min(r0 + BAND, nt) - 1;
+        const int h = r1 - r0 + 1;
+        // columns r0 .. r1 hold 1 .. h tiles, later columns h each
+        const int64_t ramp = (int64_t)h * (h + 1) / 2;
+        const int64_t cnt = ramp + (int64_t)(nt - 1 - r1) * h;
+        if (t < cnt) {
+            if (t < ramp) {
+                int j = 0;
+                while ((int64_t)(j + 1) * (j + 2) / 2 <= t) ++j;
+                ti = r0 + (int)(t - (int64_t)j * (j + 1) / 2);
+                tj = r0 + j;
+            } else {
+                const int64_t u = t - ramp;
+                tj = r1 + 1 + (int)(u / h);
+                ti = r0 + (int)(u % h);
+            }
+            return;
+        }
+        t -= cnt;
+        r0 += BAND;
     }
 }
 
-// The same LDS image from masked register loads (last, partial stage of K).
-__device__ __forceinline__ void panel_tail(uint4 (*dst)[KT / 8], const uint16_t *X, int64_t ldx, int64_t d,
-                                           int64_t row0, int64_t k0, int64_t kend, int wave, int lane) {
-    const int rr = lane >> 3, pos = lane & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = wave * 64 + i * 8 + rr;
-        const int c = pos ^ (row & 7);
+// One 1 KB piece of a stage of a 256-row panel, straight from global memory
+// into LDS (global_load_lds_dwordx4: lane l of a wave writes LDS bytes
+// [16 l, 16 l + 16) of the wave's window, i.e. 16 rows of 64 B).  Wave w fills
+// rows 64 w .. 64 w + 63 in four pieces i = 0..3; each lane fetches the global
+// chunk that belongs at its LDS position.  Rows past d are clamped to row d-1
+// (valid memory; those outputs are discarded).
+__device__ __forceinline__ void panel_piece(uint4 (*dst)[CH], const uint16_t *X, int64_t ldx, int64_t d,
+                                            int64_t row0, int64_t k0, int wave, int lane, int i) {
+    const int row = wave * 64 + i * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(row);
+    int64_t gr = row0 + row;
+    gr = gr < d ? gr : d - 1;
+    const uint16_t *src = X + gr * ldx + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 16][0]), 16, 0, 0);
+}
+
+// The same LDS image of a partial stage (tokens k0 .. kend-1, the rest zero)
+// from masked register loads.
+__device__ __forceinline__ void panel_tail(uint4 (*dst)[CH], const uint16_t *X, int64_t ldx, int64_t d, int64_t row0,
+                                           int64_t k0, int64_t kend, int tid) {
+    for (int e = tid; e < TS * CH; e += kThreads) {
+        const int row = e / CH, pos = e % CH;
+        const int c = pos ^ swz(row);
         const int64_t gr = row0 + row, gk = k0 + c * 8;
-        uint16_t tmp[8];
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = (gr < d && gk + e < kend) ? X[gr * ldx + gk + e] : (uint16_t)0;
-        dst[row][pos] = make_uint4(tmp[0] | ((uint32_t)tmp[1] << 16), tmp[2] | ((uint32_t)tmp[3] << 16),
-                                   tmp[4] | ((uint32_t)tmp[5] << 16), tmp[6] | ((uint32_t)tmp[7] << 16));
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t lo = (gr < d && gk + 2 * h < kend) ? X[gr * ldx + gk + 2 * h] : 0u;
+            const uint32_t hi = (gr < d && gk + 2 * h + 1 < kend) ? X[gr * ldx + gk + 2 * h + 1] : 0u;
+            w[h] = lo | (hi << 16);
+        }
+        dst[row][pos] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-// grid.x = splits * tiles (split-major).  Each wave owns a 128 x 128 quarter
-// of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators.
-// out_partial == nullptr: H += 2 acc (upper triangle); else raw partial tile.
+// s_waitcnt with lgkmcnt(0) and at most n vector-memory operations outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: the waits before it are explicit.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void bar() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct Frags {
+    bf16x8 a[4], b[4];
+};
+
+// grid.x = 8 * ceil(tiles / 8) * splits.  Each wave owns a
+// 128 x 128 quarter of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16
+// accumulators.  out_partial == nullptr: H += 2 acc (upper triangle); else the
+// raw partial tile goes to out_partial[split * ntiles + row-major tile index].
 __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx, int64_t d,
                                                              int64_t n_tok, int64_t kchunk, int nt, int64_t ntiles,
-                                                             float *__restrict__ H, float *__restrict__ out_partial) {
-    const int64_t t_lin = blockIdx.x % ntiles, split = blockIdx.x / ntiles;
+                                                             int splits, float *__restrict__ H,
+                                                             float *__restrict__ out_partial) {
+    // XCD x owns band-order positions [g0, g1) and runs them split after split.
+    const int64_t xcd = blockIdx.x % kXCDs, slot = blockIdx.x / kXCDs;
+    const int64_t g0 = xcd * ntiles / kXCDs, g1 = (xcd + 1) * ntiles / kXCDs, gsz = g1 - g0;
+    if (gsz <= 0 || slot >= gsz * splits) return;
+    const int64_t split = slot / gsz;
     int ti, tj;
-    tile_of(t_lin, nt, ti, tj);
+    tile_of_band(g0 + slot % gsz, nt, ti, tj);
     const bool diag = ti == tj;
     const int64_t r0 = (int64_t)ti * TS, c0 = (int64_t)tj * TS;
     const int64_t kbeg = split * kchunk;
     const int64_t kend = (kbeg + kchunk) < n_tok ? (kbeg + kchunk) : n_tok;
+    const int nfull = kend > kbeg ? (int)((kend - kbeg) / KT) : 0;
+    const bool has_tail = kend > kbeg + (int64_t)nfull * KT;
 
     __shared__ SyrkSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -109,56 +184,87 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto fill = [&](int buf, int64_t k0) {
-        if (k0 + KT <= kend) {
-            panel_dma(sm.a[buf], X, ldx, d, r0, k0, wave, lane);
-            if (!diag) panel_dma(sm.b[buf], X, ldx, d, c0, k0, wave, lane);
-        } else {
-            panel_tail(sm.a[buf], X, ldx, d, r0, k0, kend, wave, lane);
-            if (!diag) panel_tail(sm.b[buf], X, ldx, d, c0, k0, kend, wave, lane);
-        }
+    // This lane's operand rows are base + (lane % 32) with bases that are
+    // multiples of 32, so they share one swizzle; logical chunk 2 ks + lane / 32.
+    const int lrow = lane & 31, half = lane >> 5;
+    const int sw = swz(lrow);
+    // Stage st of both panels into ring slot `slot` (diagonal tiles load their
+    // one panel twice, which keeps the load count per stage uniform: 8 per wave).
+    auto issue_piece = [&](int st, int slot, int p) {
+        const int64_t k0 = kbeg + (int64_t)st * KT;
+        if (p < 4)
+            panel_piece(sm.a[slot], X, ldx, d, r0, k0, wave, lane, p);
+        else
+            panel_piece(sm.b[slot], X, ldx, d, c0, k0, wave, lane, p - 4);
+    };
+    // Operand p of a 16-token step: p < 4 is A row block p, else B row block p-4.
+    auto read_frag = [&](int slot, int ks, int p, Frags &f) {
+        const int pos = (2 * ks + half) ^ sw;
+        if (p < 4)
+            f.a[p] = __builtin_bit_cast(bf16x8, sm.a[slot][wm * 128 + p * 32 + lrow][pos]);
+        else
+            f.b[p - 4] = __builtin_bit_cast(bf16x8, sm.b[slot][wn * 128 + (p - 4) * 32 + lrow][pos]);
+    };
+    auto mfma = [&](const Frags &f, int q) {
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
     };
 
-    if (kbeg < kend) {
-        fill(0, kbeg);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        int buf = 0;
-        const int row = lane & 31, half = lane >> 5;
-        for (int64_t k0 = kbeg; k0 < kend; k0 += KT) {
-            if (k0 + KT < kend) fill(buf ^ 1, k0 + KT);
-            {
-                uint4(*sa)[KT / 8] = sm.a[buf];
-                uint4(*sb)[KT / 8] = diag ? sm.a[buf] : sm.b[buf];
+    if (nfull > 0) {
+        // Exactly one stage is issued per step (past the end: the last stage
+        // again, into a slot nobody reads), so the in-flight count is fixed:
+        // at each wait, the stage being waited for is followed by one more.
 #pragma unroll
-                for (int ks = 0; ks < KT / 16; ++ks) {
-                    const int c = 2 * ks + half;
-                    bf16x8 fa[4], fb[4];
+        for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ra = wm * 128 + i * 32 + row;
-                        fa[i] = __builtin_bit_cast(bf16x8, sa[ra][c ^ (ra & 7)]);
-                    }
+            for (int p = 0; p < 8; ++p) issue_piece(min(st, nfull - 1), st, p);
+        wait_vm_lgkm0<16>();  // stage 0 landed
+        bar();
+        Frags f0, f1;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int rb = wn * 128 + j * 32 + row;
-                        fb[j] = __builtin_bit_cast(bf16x8, sb[rb][c ^ (rb & 7)]);
-                    }
+        for (int p = 0; p < 8; ++p) read_frag(0, 0, p, f0);
+        // Each step is two half-steps of 16 MFMAs; the LDS reads of the other
+        // half's operands and the global->LDS loads of the stage NS-1 ahead
+        // are issued one per MFMA (the scheduling fences hold that order), so
+        // the matrix core never waits on instruction issue.
+        for (int k = 0; k < nfull; ++k) {
+            const int cur = k % NS, nxt = (k + 1) % NS;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-                }
+            for (int q = 0; q < 16; ++q) {
+                mfma(f0, q);
+                if (q >= 1 && q <= 8) read_frag(cur, 1, q - 1, f1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            buf ^= 1;
+            wait_vm_lgkm0<8>();  // stage k+1 landed (and this wave's operand reads are done)
+            bar();               // ... for every wave; slot (k-1) % NS is free
+            const int st = min(k + NS - 1, nfull - 1), slot = (k + NS - 1) % NS;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                mfma(f1, q);
+                if (q >= 1 && q <= 8) issue_piece(st, slot, q - 1);
+                if (q >= 7 && q <= 14) read_frag(nxt, 0, q - 7, f0);  // unused after the last step
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vm_lgkm0<0>();
+    }
+    if (has_tail) {
+        const int64_t k0 = kbeg + (int64_t)nfull * KT;
+        __syncthreads();  // every wave is done with the ring
+        panel_tail(sm.a[0], X, ldx, d, r0, k0, kend, tid);
+        panel_tail(sm.b[0], X, ldx, d, c0, k0, kend, tid);
+        __syncthreads();
+        Frags f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) read_frag(0, ks, p, f);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mfma(f, q);
         }
     }
 
     if (out_partial) {
-        float *dst = out_partial + (int64_t)blockIdx.x * (TS * TS);
+        float *dst = out_partial + (split * ntiles + tile_linear(ti, tj, nt)) * (TS * TS);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -255,20 +361,20 @@ struct SyrkPlan {
 };
 
 // Token splits: pick the count that minimizes an estimate of
-//   rounds of workgroups over the CUs x stages per split  +  partial-tile traffic.
+//   rounds of workgroups over one XCD's CUs x stages per split  +  partial-tile traffic.
 SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
     SyrkPlan p;
     p.nt = (int)ceil_div(d, TS);
     p.ntiles = (int64_t)p.nt * (p.nt + 1) / 2;
-    const double stage_us = 2.0;                        // one 256x256x64 stage per CU (measured order)
+    const double stage_us = 1.0;                        // one 256x256x32 stage per CU (order of magnitude)
     const double part_us = 2.0 * TS * TS * 4 / 4.0e6;  // write + read of one partial tile at ~4 TB/s (whole chip)
     double best = 1e300;
     int best_s = 1;
     for (int s = 1; s <= 64; ++s) {
         const int64_t kc = ceil_div(ceil_div(n_tok, s), KT) * KT;
-        if (s > 1 && kc < 8 * KT) break;
+        if (s > 1 && kc < 16 * KT) break;
         const int64_t wgs = p.ntiles * s;
-        const double rounds = (double)ceil_div(wgs, kCUs);
+        const double rounds = (double)ceil_div(ceil_div(p.ntiles, kXCDs) * s, kCUs / kXCDs);  // largest group
         const double t = rounds * (double)(kc / KT) * stage_us + (s > 1 ? (double)wgs * part_us : 0.0);
         if (t < best) {
             best = t;
@@ -296,8 +402,10 @@ hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, in
     if (dt == GPTQ_DT_BF16) {
         SyrkPlan p = plan_syrk(d, n_tok);
         float *part = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
-        hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(p.ntiles * p.splits)), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t *>(X), ldx, d, n_tok, p.kchunk, p.nt, p.ntiles, H, part);
+        hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(kXCDs * ceil_div(p.ntiles, kXCDs) * p.splits)),
+                           dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(X), ldx, d, n_tok, p.kchunk, p.nt, p.ntiles, p.splits, H,
+                           part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (part) {

@@ -32,6 +32,7 @@ def _gpu():
 # step 1: Hessian
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("d,n,dt", [(64, 512, "bf16"), (300, 2000, "bf16"), (129, 1000, "bf16"), (1024, 8192, "bf16"),
+                                    (64, 24, "bf16"), (72, 72, "bf16"), (1300, 3000, "bf16"),
                                     (128, 512, "f32"), (77, 301, "f32")])
 def test_hessian_parity(oracle_mod, d, n, dt):
     torch = torch_mod()
