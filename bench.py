@@ -29,6 +29,22 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per hessian_accumulate call from the committed counter runs, if they were
+    taken on this workload with the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hessian_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, rec["kernel_source"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != sha:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
     """The oracle as it stands, timed on a bounded sample of the same workload."""
     import oracle
@@ -164,7 +180,7 @@ def main() -> int:
                    "block_size": lay["block"], "damp_rel": lay["damp"], "act_order": lay["act_order"],
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "hessian_accumulate (syrk_bf16_kernel + split-K reduce)",
                      "flops_per_launch": syrk_flops},
         "phases_ms": {"hessian": round(t_h, 3), "prepare": round(t_p, 3), "restore_w": round(t_c, 3),

@@ -52,49 +52,68 @@ __global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(BlockArgs a) 
     __shared__ int32_t pcol[BT];
     const int tid = threadIdx.x;
     const int nc = a.ncols;
-    {
-        const float *src = a.U + a.c0 * a.ldu + a.c0;
-        const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
-        for (int e4 = tid; e4 < BT * BT / 4; e4 += kBlockThreads) {
-            const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (i < nc) {
-                if (vec) {
-                    v = *reinterpret_cast<const float4 *>(src + i * a.ldu + k);
-                } else {
-                    if (k + 0 < nc) v.x = src[i * a.ldu + k + 0];
-                    if (k + 1 < nc) v.y = src[i * a.ldu + k + 1];
-                    if (k + 2 < nc) v.z = src[i * a.ldu + k + 2];
-                    if (k + 3 < nc) v.w = src[i * a.ldu + k + 3];
-                }
-            }
-            if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
-            if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
-            if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
-            if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
-            v.x = (k + 0 > i) ? v.x : 0.0f;
-            v.y = (k + 1 > i) ? v.y : 0.0f;
-            v.z = (k + 2 > i) ? v.z : 0.0f;
-            v.w = (k + 3 > i) ? v.w : 0.0f;
-            *reinterpret_cast<float4 *>(&us[i][k]) = v;
-        }
-    }
-    if (tid < BT) {
-        const int64_t k = a.c0 + (tid < nc ? tid : 0);
-        pcol[tid] = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + tid);
-    }
-    __syncthreads();
-
     const int q = tid & (kRowLanes - 1);
     const int64_t r = (int64_t)blockIdx.x * kBlockRows + (tid >> 2);
     const bool active = r < a.d_out;
     float *wrow = a.W + r * a.ldw + a.c0;
+    // Every global load of the prologue (the U block, the permutation and the
+    // row's weights) is issued before the first LDS store.
+    constexpr int kUPer = (BT * BT / 4 + kBlockThreads - 1) / kBlockThreads;  // float4 chunks per thread
+    float4 uv[kUPer];
+    {
+        const float *src = a.U + a.c0 * a.ldu + a.c0;
+        const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
+        if (vec) {  // full, aligned batch: 16-byte loads
+#pragma unroll
+            for (int u = 0; u < kUPer; ++u) {
+                const int e4 = tid + u * kBlockThreads;
+                const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+                uv[u] = e4 < BT * BT / 4 ? *reinterpret_cast<const float4 *>(src + i * a.ldu + k)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUPer; ++u) {
+                const int e4 = tid + u * kBlockThreads;
+                const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+                const bool in = e4 < BT * BT / 4 && i < nc;
+                const float *p = src + i * a.ldu + k;
+                uv[u].x = (in && k + 0 < nc) ? p[0] : 0.0f;
+                uv[u].y = (in && k + 1 < nc) ? p[1] : 0.0f;
+                uv[u].z = (in && k + 2 < nc) ? p[2] : 0.0f;
+                uv[u].w = (in && k + 3 < nc) ? p[3] : 0.0f;
+            }
+        }
+    }
+    int32_t pc = 0;
+    if (tid < BT) {
+        const int64_t k = a.c0 + (tid < nc ? tid : 0);
+        pc = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + tid);
+    }
     float w[CPL];
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
         const int k = q + kRowLanes * t;
         w[t] = (active && k < nc) ? wrow[k] : 0.0f;
     }
+#pragma unroll
+    for (int u = 0; u < kUPer; ++u) {
+        const int e4 = tid + u * kBlockThreads;
+        if (e4 >= BT * BT / 4) break;
+        const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+        float4 v = uv[u];
+        if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
+        if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
+        if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
+        if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
+        v.x = (k + 0 > i) ? v.x : 0.0f;
+        v.y = (k + 1 > i) ? v.y : 0.0f;
+        v.z = (k + 2 > i) ? v.z : 0.0f;
+        v.w = (k + 3 > i) ? v.w : 0.0f;
+        *reinterpret_cast<float4 *>(&us[i][k]) = v;
+    }
+    if (tid < BT) pcol[tid] = pc;
+    __syncthreads();
 
     Grid gr = grid_make(0.0f, 0.0f, 0.0f, a.bits, a.sym);
     if constexpr (GT == 0) {

@@ -253,30 +253,54 @@ __global__ __launch_bounds__(kFThreads) void panel_update_kernel(float *__restri
             }
 
     // Panels (k-major) and V into LDS; columns past the block's nb are zero.
-    for (int e4 = tid; e4 < FT * NB / 4; e4 += kFThreads) {
-        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (m < nb) {  // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed
-            if (r0 + r < k0) a = *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m);
-            if (!diag && s0 + r < k0) b = *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m);
+    // Every global load of a thread is issued before the first LDS store.
+    {
+        constexpr int kPer = FT * NB / 4 / kFThreads;  // float4 chunks per panel and thread
+        float4 av[kPer], bv[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e4 = tid + q * kFThreads;
+            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+            // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
+            const bool in = m < nb;
+            av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        constexpr int kVPer = NB * NB / kFThreads;
+        float vv[kVPer];
+#pragma unroll
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + q * kFThreads;
+            const int c = e / NB, m = e % NB;
+            vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e4 = tid + q * kFThreads;
+            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+            float4 a = av[q], b = bv[q];
             if (m + 1 >= nb) a.y = b.y = 0.0f;
             if (m + 2 >= nb) a.z = b.z = 0.0f;
             if (m + 3 >= nb) a.w = b.w = 0.0f;
+            sm.pi[m + 0][r] = a.x;
+            sm.pi[m + 1][r] = a.y;
+            sm.pi[m + 2][r] = a.z;
+            sm.pi[m + 3][r] = a.w;
+            if (!diag) {
+                sm.pj[m + 0][r] = b.x;
+                sm.pj[m + 1][r] = b.y;
+                sm.pj[m + 2][r] = b.z;
+                sm.pj[m + 3][r] = b.w;
+            }
         }
-        sm.pi[m + 0][r] = a.x;
-        sm.pi[m + 1][r] = a.y;
-        sm.pi[m + 2][r] = a.z;
-        sm.pi[m + 3][r] = a.w;
-        if (!diag) {
-            sm.pj[m + 0][r] = b.x;
-            sm.pj[m + 1][r] = b.y;
-            sm.pj[m + 2][r] = b.z;
-            sm.pj[m + 3][r] = b.w;
+#pragma unroll
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + q * kFThreads;
+            const int c = e / NB, m = e % NB;
+            sm.vb[m][c] = vv[q];
         }
-    }
-    for (int e = tid; e < NB * NB; e += kFThreads) {
-        const int c = e / NB, m = e % NB;
-        sm.vb[m][c] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
     }
     __syncthreads();
 

@@ -85,12 +85,24 @@ __global__ __launch_bounds__(kThreads) void trailing_kernel(TrailArgs a) {
     const int nst = (a.K + BK - 1) / BK;
 
     // (-E)^T block of this row block, rows past K zeroed.  Et is padded to
-    // whole workgroups of rows, so m0 + 127 < ldet.
-    for (int e4 = tid; e4 < KMAX * TM / 4; e4 += kThreads) {
-        const int k = e4 / (TM / 4), i = (e4 % (TM / 4)) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (k < a.K) v = *reinterpret_cast<const float4 *>(a.Et + (int64_t)k * a.ldet + m0 + i);
-        *reinterpret_cast<float4 *>(&sm.es[k][i]) = v;
+    // whole workgroups of rows, so m0 + 127 < ldet.  All sixteen loads of a
+    // thread are issued before the first LDS store.
+    {
+        constexpr int kPer = KMAX * TM / 4 / kThreads;
+        float4 ev[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e4 = tid + q * kThreads;
+            const int k = e4 / (TM / 4), i = (e4 % (TM / 4)) * 4;
+            ev[q] = k < a.K ? *reinterpret_cast<const float4 *>(a.Et + (int64_t)k * a.ldet + m0 + i)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e4 = tid + q * kThreads;
+            const int k = e4 / (TM / 4), i = (e4 % (TM / 4)) * 4;
+            *reinterpret_cast<float4 *>(&sm.es[k][i]) = ev[q];
+        }
     }
 
     float4 ru[4];
