@@ -85,52 +85,32 @@ __global__ __launch_bounds__(kThreads) void iota_kernel(int32_t *__restrict__ p,
     if (i < n) p[i] = (int32_t)i;
 }
 
-// UL-Cholesky of the diagonal block A[k0:k0+nb, k0:k0+nb] (upper storage) and
-// the inverse of its factor, on one wave64 with no block barriers.
-//   factor:  lane i holds row i of the block in registers.  For j = NB-1..0:
-//            t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
+// UL-Cholesky of one diagonal block and the inverse of its factor, on one
+// wave64 with no workgroup barriers (the other waves of the workgroup, if any,
+// have left).  On entry lane i holds row i of the block in c (upper part;
+// rows and columns past nb padded with the identity).
+//   factor:  for j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
 //            c_ii' -= t_ij t_i'j (i' < j)  -- column j is shared through LDS.
 //   inverse: lane c holds column c of V = T^-1.  For i = NB-1..0:
 //            V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
 //            reading row i of T from LDS with wave-uniform addresses.
-// Rows and columns past nb are padded with the identity.  Reads the block from
-// the working matrix A and writes V into U's block (strictly lower part = 0);
-// T's diagonal blocks themselves are not needed later.
-// The wave is alone on its CU, so it may take every register; that lets the
-// scheduler keep a whole column of LDS reads in flight.
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d, int64_t lda, int64_t k0, int nb,
-                  int32_t *__restrict__ info) {
-    __shared__ __attribute__((aligned(16))) float col[NB];
-    __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
-    const int lane = threadIdx.x;
-    // Row `lane` of the block straight into registers (16-byte loads, all in
-    // flight at once); rows and columns past nb are padded with the identity.
-    float c[NB];
-    {
-        const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
-#pragma unroll
-        for (int q = 0; q < NB / 4; ++q) {
-            // chunks past nb are not read (lda is a multiple of 4, so a chunk
-            // that starts below nb ends inside the row)
-            const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-            c[4 * q + 0] = v.x;
-            c[4 * q + 1] = v.y;
-            c[4 * q + 2] = v.z;
-            c[4 * q + 3] = v.w;
-        }
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            const bool in = lane < nb && m < nb;
-            c[m] = in ? (m >= lane ? c[m] : 0.0f) : (m == lane ? 1.0f : 0.0f);
-        }
-    }
+// Writes V into U's block at (kb, kb) (strictly lower part = 0); T's diagonal
+// blocks themselves are not needed later.  A non-positive pivot j sets
+// *info = kb + j + 1 (first one wins).
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void factor_invert_block(float (&c)[NB], int lane, int nb, int64_t kb, float *__restrict__ U,
+                                                    int64_t d, int32_t *__restrict__ info, float *col,
+                                                    float (*tr)[NB + 4]) {
     int32_t first_bad = 0;
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
         const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));  // pivot, from lane j
         const bool bad = !(p0 > 0.0f);
-        first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(k0 + j + 1) : first_bad;
+        first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(kb + j + 1) : first_bad;
         // hardware sqrt / reciprocal (about 1 ulp): the factor only has to be
         // accurate; branch-free selects keep the wave on one path.
         const float tjj = __builtin_amdgcn_sqrtf(bad ? 1.0f : p0);
@@ -141,8 +121,7 @@ void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d,
         c[j] = t;
         if (j == 0) break;
         col[lane] = t;  // column j of the factor, shared through LDS
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
+        wave_sync_lds();
         float4 cv[NB / 4];
 #pragma unroll
         for (int q = 0; q < (j + 3) / 4; ++q) cv[q] = *reinterpret_cast<const float4 *>(&col[4 * q]);
@@ -152,8 +131,7 @@ void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d,
         __builtin_amdgcn_wave_barrier();
     }
     if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
-    // Rows of T (upper part) to LDS for the inverse.  (T's diagonal blocks are
-    // not needed after this kernel: only their inverses are.)
+    // Rows of T (upper part) to LDS for the inverse.
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
         float4 v;
@@ -163,7 +141,7 @@ void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d,
         v.w = (4 * q + 3 >= lane) ? c[4 * q + 3] : 0.0f;
         *reinterpret_cast<float4 *>(&tr[lane][4 * q]) = v;
     }
-    __syncthreads();
+    wave_sync_lds();
     float v[NB];
 #pragma unroll
     for (int i = NB - 1; i >= 0; --i) {
@@ -188,28 +166,68 @@ void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d,
     // Column `lane` of V into U's block (zero below the diagonal): each store
     // instruction writes one row, lanes along the columns.
     if (lane < nb) {
-        float *dst = U + k0 * d + k0 + lane;
+        float *dst = U + kb * d + kb + lane;
 #pragma unroll
         for (int m = 0; m < NB; ++m)
             if (m < nb) dst[m * d] = v[m];
     }
 }
 
-// Panel solve fused with the symmetric rank-NB update of the leading block,
-// one 128 x 128 upper tile of A[0:k0, 0:k0] per workgroup:
-//   P_i = A[rows i, k0:k0+NB] V^T        (V = T_kk^-1, so P = panel T_kk^-T)
+// Rows past nb (and columns past nb) of a block row become the identity; the
+// strictly lower part is cleared.
+__device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const bool in = lane < nb && m < nb;
+        c[m] = in ? (m >= lane ? c[m] : 0.0f) : (m == lane ? 1.0f : 0.0f);
+    }
+}
+
+// The first (bottom-right) diagonal block A[k0:k0+nb, k0:k0+nb], read from the
+// working matrix.  The wave is alone on its CU, so it may take every register;
+// that lets the scheduler keep a whole column of LDS reads in flight.
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d, int64_t lda, int64_t k0, int nb,
+                  int32_t *__restrict__ info) {
+    __shared__ __attribute__((aligned(16))) float col[NB];
+    __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
+    const int lane = threadIdx.x;
+    // Row `lane` of the block straight into registers (16-byte loads, all in flight at once).
+    float c[NB];
+    const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+        // chunks past nb are not read (lda is a multiple of 4, so a chunk
+        // that starts below nb ends inside the row)
+        const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        c[4 * q + 0] = v.x;
+        c[4 * q + 1] = v.y;
+        c[4 * q + 2] = v.z;
+        c[4 * q + 3] = v.w;
+    }
+    mask_block_row(c, lane, nb);
+    factor_invert_block(c, lane, nb, k0, U, d, info, col, tr);
+}
+
+// One step of the blocked factorization, fused.  Block k0 (columns k0..k0+nb)
+// has been factored and V = T_kk^-1 sits in U's block.  Each workgroup takes
+// one FT x FT upper tile (i, j) of the leading matrix A[0:k0, 0:k0]:
+//   P_i = A[rows i, k0:k0+nb] V^T        (so P = panel T_kk^-T)
 //   A[i, j] -= P_i P_j^T                  (upper part)
-// and the diagonal tile also writes P_i into the factor T (Tf[rows i, k0:k0+NB]).
-// Both products run on fp32 matrix cores in transposed form, D[col][row], so
-// each lane's accumulators hold four consecutive columns of one row of A.
-constexpr int FT = 128;           // tile edge
-constexpr int FLD = FT + 4;       // LDS row length of the k-major panels
+// and a diagonal tile also writes P_i into the factor T (Tf[rows i, k0:k0+nb]).
+// The workgroup of the last diagonal tile, which holds the next block
+// A[k0-NB:k0, k0-NB:k0] at its bottom-right corner, then factors and inverts
+// that block from its updated values: the next step's V is ready when the
+// kernel ends, with no launch and no HBM round trip in between.
+// Products run on fp32 matrix cores in transposed form, D[col][row], so each
+// lane's accumulators hold four consecutive columns of one row of A.
 constexpr int kFThreads = 256;
 
-struct FusedSmem {
-    float pi[NB][FLD];   // panel rows i, k-major (later P_i^T)
-    float pj[NB][FLD];   // panel rows j, k-major (later P_j^T)
-    float vb[NB][NB + 4];  // vb[m][c] = V[c][m]
+template <int FT>
+struct StepSmem {
+    float pi[NB][FT + 4];  // panel rows i, k-major (later P_i^T)
+    float pj[NB][FT + 4];  // panel rows j, k-major (later P_j^T; then the next block)
+    float vb[NB][NB + 4];  // vb[m][c] = V[c][m]  (later rows of T for the inverse)
 };
 
 __device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) {
@@ -223,114 +241,121 @@ __device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) 
     tj = i + (int)(t - before);
 }
 
-__global__ __launch_bounds__(kFThreads) void panel_update_kernel(float *__restrict__ A, float *__restrict__ Tf,
-                                                                 const float *__restrict__ U, int64_t d, int64_t lda,
-                                                                 int64_t k0, int nb, int nt) {
+template <int FT>
+__global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, float *__restrict__ Tf,
+                                                         float *__restrict__ U, int64_t d, int64_t lda, int64_t k0,
+                                                         int nb, int nt, int32_t *__restrict__ info) {
+    constexpr int QB = FT / 64;  // 32-row MFMA blocks per wave quadrant edge
+    constexpr int FLD = FT + 4;
+    // Tiles in reverse order: workgroup 0 takes the last diagonal tile, whose
+    // factorization of the next block is the step's longest chain.
     int ti, tj;
-    tile_upper(blockIdx.x, nt, ti, tj);
+    tile_upper((int64_t)nt * (nt + 1) / 2 - 1 - blockIdx.x, nt, ti, tj);
     const bool diag = ti == tj;
+    const bool last = diag && ti == nt - 1;
     const int64_t r0 = (int64_t)ti * FT, s0 = (int64_t)tj * FT;
-    __shared__ FusedSmem sm;
+    __shared__ __attribute__((aligned(16))) StepSmem<FT> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, lo = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Rows of A this tile updates, in the transposed accumulator layout: for
-    // each 32x32 block (si, ri) and g = 0..3, A[r][s .. s+3] with
-    // r = r0 + wm*64 + ri*32 + lo, s = s0 + wn*64 + si*32 + 8g + 4*hi.
-    float4 cold[2][2][4];
+    // Every global load of a thread is issued before the first LDS store.
+    // (1) This tile's A values in the transposed accumulator layout: for each
+    //     32x32 block (si, ri) and g = 0..3, A[r][s .. s+3] with
+    //     r = r0 + wm*FT/2 + ri*32 + lo, s = s0 + wn*FT/2 + si*32 + 8g + 4*hi.
+    float4 cold[QB][QB][4];
 #pragma unroll
-    for (int si = 0; si < 2; ++si)
+    for (int si = 0; si < QB; ++si)
 #pragma unroll
-        for (int ri = 0; ri < 2; ++ri)
+        for (int ri = 0; ri < QB; ++ri)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int64_t r = r0 + wm * 64 + ri * 32 + lo;
-                const int64_t sc = s0 + wn * 64 + si * 32 + 8 * g + 4 * hi;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < k0 && sc < k0) v = *reinterpret_cast<const float4 *>(A + r * lda + sc);
-                cold[si][ri][g] = v;
+                const int64_t r = r0 + wm * (FT / 2) + ri * 32 + lo;
+                const int64_t sc = s0 + wn * (FT / 2) + si * 32 + 8 * g + 4 * hi;
+                cold[si][ri][g] = (r < k0 && sc < k0) ? *reinterpret_cast<const float4 *>(A + r * lda + sc)
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-
-    // Panels (k-major) and V into LDS; columns past the block's nb are zero.
-    // Every global load of a thread is issued before the first LDS store.
-    {
-        constexpr int kPer = FT * NB / 4 / kFThreads;  // float4 chunks per panel and thread
-        float4 av[kPer], bv[kPer];
+    // (2) panel rows i and j (columns past the block's nb are zero) and V.
+    constexpr int kPer = FT * NB / 4 / kFThreads;
+    float4 av[kPer], bv[kPer];
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int e4 = tid + q * kFThreads;
-            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-            // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
-            const bool in = m < nb;
-            av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-            bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
-                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        constexpr int kVPer = NB * NB / kFThreads;
-        float vv[kVPer];
+    for (int q = 0; q < kPer; ++q) {
+        const int e4 = tid + q * kFThreads;
+        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+        // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
+        const bool in = m < nb;
+        av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    constexpr int kVPer = NB * NB / kFThreads;
+    float vv[kVPer];
 #pragma unroll
-        for (int q = 0; q < kVPer; ++q) {
-            const int e = tid + q * kFThreads;
-            const int c = e / NB, m = e % NB;
-            vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
-        }
+    for (int q = 0; q < kVPer; ++q) {
+        const int e = tid + q * kFThreads;
+        const int c = e / NB, m = e % NB;
+        vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+    }
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int e4 = tid + q * kFThreads;
-            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-            float4 a = av[q], b = bv[q];
-            if (m + 1 >= nb) a.y = b.y = 0.0f;
-            if (m + 2 >= nb) a.z = b.z = 0.0f;
-            if (m + 3 >= nb) a.w = b.w = 0.0f;
-            sm.pi[m + 0][r] = a.x;
-            sm.pi[m + 1][r] = a.y;
-            sm.pi[m + 2][r] = a.z;
-            sm.pi[m + 3][r] = a.w;
-            if (!diag) {
-                sm.pj[m + 0][r] = b.x;
-                sm.pj[m + 1][r] = b.y;
-                sm.pj[m + 2][r] = b.z;
-                sm.pj[m + 3][r] = b.w;
-            }
+    for (int q = 0; q < kPer; ++q) {
+        const int e4 = tid + q * kFThreads;
+        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+        float4 a = av[q], b = bv[q];
+        if (m + 1 >= nb) a.y = b.y = 0.0f;
+        if (m + 2 >= nb) a.z = b.z = 0.0f;
+        if (m + 3 >= nb) a.w = b.w = 0.0f;
+        sm.pi[m + 0][r] = a.x;
+        sm.pi[m + 1][r] = a.y;
+        sm.pi[m + 2][r] = a.z;
+        sm.pi[m + 3][r] = a.w;
+        if (!diag) {
+            sm.pj[m + 0][r] = b.x;
+            sm.pj[m + 1][r] = b.y;
+            sm.pj[m + 2][r] = b.z;
+            sm.pj[m + 3][r] = b.w;
         }
+    }
 #pragma unroll
-        for (int q = 0; q < kVPer; ++q) {
-            const int e = tid + q * kFThreads;
-            const int c = e / NB, m = e % NB;
-            sm.vb[m][c] = vv[q];
-        }
+    for (int q = 0; q < kVPer; ++q) {
+        const int e = tid + q * kFThreads;
+        const int c = e / NB, m = e % NB;
+        sm.vb[m][c] = vv[q];
     }
     __syncthreads();
 
-    // P^T[c][r] = sum_m V[c][m] panel[r][m]: wave w covers rows 32w..32w+31, all NB columns.
-    floatx16 pa[2], pb[2];
+    // P^T[c][r] = sum_m V[c][m] panel[r][m]: 2 x FT/32 output blocks of 32x32,
+    // FT/64 per wave; block b = wave * QB + t covers c-block b % 2, r-block b / 2.
+    floatx16 pa[QB], pb[QB];
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci)
+    for (int t = 0; t < QB; ++t)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) pa[ci][q] = pb[ci][q] = 0.0f;
+        for (int q = 0; q < 16; ++q) pa[t][q] = pb[t][q] = 0.0f;
 #pragma unroll 8
     for (int m = 0; m < NB; m += 2) {
-        const float v0 = sm.vb[m + hi][lo], v1 = sm.vb[m + hi][32 + lo];
-        const float xa = sm.pi[m + hi][32 * wave + lo];
-        pa[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[0], 0, 0, 0);
-        pa[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, xa, pa[1], 0, 0, 0);
-        if (!diag) {
-            const float xb = sm.pj[m + hi][32 * wave + lo];
-            pb[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[0], 0, 0, 0);
-            pb[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, xb, pb[1], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < QB; ++t) {
+            const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
+            const float v0 = sm.vb[m + hi][cb * 32 + lo];
+            const float xa = sm.pi[m + hi][rb * 32 + lo];
+            pa[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[t], 0, 0, 0);
+            if (!diag) {
+                const float xb = sm.pj[m + hi][rb * 32 + lo];
+                pb[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[t], 0, 0, 0);
+            }
         }
     }
     __syncthreads();  // every wave is done reading the panels
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci)
+    for (int t = 0; t < QB; ++t) {
+        const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int c = ci * 32 + mfma32_row(q, lane);
-            sm.pi[c][32 * wave + lo] = pa[ci][q];
-            if (!diag) sm.pj[c][32 * wave + lo] = pb[ci][q];
+            const int c = cb * 32 + mfma32_row(q, lane);
+            sm.pi[c][rb * 32 + lo] = pa[t][q];
+            if (!diag) sm.pj[c][rb * 32 + lo] = pb[t][q];
         }
+    }
     __syncthreads();
     float(*pjs)[FLD] = diag ? sm.pi : sm.pj;
 
@@ -342,36 +367,51 @@ __global__ __launch_bounds__(kFThreads) void panel_update_kernel(float *__restri
     }
 
     // A[r][s] -= sum_c P_i[r][c] P_j[s][c], as D[s][r] = sum_c P_j^T[c][s] P_i^T[c][r].
-    floatx16 acc[2][2];
+    floatx16 acc[QB][QB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < QB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < QB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 #pragma unroll 8
     for (int c = 0; c < NB; c += 2) {
-        const float y0 = pjs[c + hi][wn * 64 + lo], y1 = pjs[c + hi][wn * 64 + 32 + lo];
-        const float x0 = sm.pi[c + hi][wm * 64 + lo], x1 = sm.pi[c + hi][wm * 64 + 32 + lo];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(y0, x0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(y0, x1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(y1, x0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(y1, x1, acc[1][1], 0, 0, 0);
+        float y[QB], x[QB];
+#pragma unroll
+        for (int t = 0; t < QB; ++t) {
+            y[t] = pjs[c + hi][wn * (FT / 2) + t * 32 + lo];
+            x[t] = sm.pi[c + hi][wm * (FT / 2) + t * 32 + lo];
+        }
+#pragma unroll
+        for (int si = 0; si < QB; ++si)
+#pragma unroll
+            for (int ri = 0; ri < QB; ++ri)
+                acc[si][ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[si], x[ri], acc[si][ri], 0, 0, 0);
     }
+    if (last) __syncthreads();  // pj is about to hold the next block: every wave is done reading it
+    // The next block's first row/column in tile coordinates (it is the
+    // tile's bottom-right NB x NB corner).
+    const int64_t nb0 = k0 - NB;
+    float(*blk)[NB + 4] = reinterpret_cast<float(*)[NB + 4]>(&sm.pj[0][0]);
 #pragma unroll
-    for (int si = 0; si < 2; ++si)
+    for (int si = 0; si < QB; ++si)
 #pragma unroll
-        for (int ri = 0; ri < 2; ++ri)
+        for (int ri = 0; ri < QB; ++ri)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int64_t r = r0 + wm * 64 + ri * 32 + lo;
-                const int64_t sc = s0 + wn * 64 + si * 32 + 8 * g + 4 * hi;
+                const int64_t r = r0 + wm * (FT / 2) + ri * 32 + lo;
+                const int64_t sc = s0 + wn * (FT / 2) + si * 32 + 8 * g + 4 * hi;
                 if (r >= k0 || sc >= k0) continue;
                 float4 v = cold[si][ri][g];
                 v.x -= acc[si][ri][4 * g + 0];
                 v.y -= acc[si][ri][4 * g + 1];
                 v.z -= acc[si][ri][4 * g + 2];
                 v.w -= acc[si][ri][4 * g + 3];
+                if (last && r >= nb0 && sc >= nb0) {
+                    // the next block: kept in LDS for this workgroup's factorization
+                    *reinterpret_cast<float4 *>(&blk[r - nb0][sc - nb0]) = v;
+                    continue;
+                }
                 float *dst = A + r * lda + sc;
                 if (!diag || r <= sc) {
                     *reinterpret_cast<float4 *>(dst) = v;
@@ -382,6 +422,22 @@ __global__ __launch_bounds__(kFThreads) void panel_update_kernel(float *__restri
                     if (r <= sc + 3) dst[3] = v.w;
                 }
             }
+    if (!last) return;
+    __syncthreads();  // the next block is complete in LDS
+    if (wave != 0) return;
+    float c[NB];
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(&blk[lane][4 * q]);
+        c[4 * q + 0] = v.x;
+        c[4 * q + 1] = v.y;
+        c[4 * q + 2] = v.z;
+        c[4 * q + 3] = v.w;
+    }
+    mask_block_row(c, lane, NB);
+    // scratch for the factorization: V's LDS copy and the first panel row are dead
+    factor_invert_block(c, lane, NB, nb0, U, d, info, &sm.pi[0][0],
+                        reinterpret_cast<float(*)[NB + 4]>(&sm.vb[0][0]));
 }
 
 // Pairwise merge of inverted diagonal blocks at one level (block size sz):
@@ -427,6 +483,8 @@ hipError_t merge_level(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
 
 int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
 
+constexpr int kStepTile = 64;  // tile edge of the fused step
+
 }  // namespace
 
 // Workspace: the working matrix A (Schur complements), the factor Tf and the
@@ -460,19 +518,23 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                        U, nU, 0.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // UL-Cholesky from the bottom-right corner: factor (and invert) the diagonal
-    // block, then solve its panel and update the leading block in one pass.
+    // UL-Cholesky from the bottom-right corner: factor (and invert) the last
+    // diagonal block, then one fused step per block: solve its panel, update
+    // the leading block and factor the next diagonal block.  64-wide tiles
+    // keep each workgroup's matrix-core chains short (measured faster than
+    // 128-wide tiles for leading blocks up to 8192).
     const int64_t nblk = ceil_div(d, NB);
-    for (int64_t kb = nblk - 1; kb >= 0; --kb) {
+    {
+        const int64_t k0 = (nblk - 1) * NB;
+        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, lda, k0, (int)(d - k0), info);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    for (int64_t kb = nblk - 1; kb >= 1; --kb) {
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, lda, k0, nb, info);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (k0 == 0) break;
-        const int nt = (int)ceil_div(k0, FT);
-        const int64_t ntiles = (int64_t)nt * (nt + 1) / 2;
-        hipLaunchKernelGGL(panel_update_kernel, dim3((unsigned)ntiles), dim3(kFThreads), 0, s, A, Tf, U, d, lda, k0, nb,
-                           nt);
+        const int nt = (int)ceil_div(k0, kStepTile);
+        hipLaunchKernelGGL(step_kernel<kStepTile>, dim3((unsigned)((int64_t)nt * (nt + 1) / 2)), dim3(kFThreads), 0,
+                           s, A, Tf, U, d, lda, k0, nb, nt, info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // U = T^-1: pairwise merges of the inverted diagonal blocks.

@@ -78,7 +78,7 @@ def _spd_h(oracle_mod, d, seed, recipe="down_proj_7b"):
 
 
 @pytest.mark.parametrize("d,act_order", [(64, False), (77, True), (130, False), (200, False), (200, True),
-                                         (1000, True), (2048, False)])
+                                         (1000, True), (2048, False), (2200, True)])
 def test_prepare_parity(oracle_mod, d, act_order):
     """U from the GPU vs the oracle's factor of the same fp32 Hessian.
 
