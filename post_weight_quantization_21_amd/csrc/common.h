@@ -55,11 +55,6 @@ constexpr int kGemmTile = 128;
 int64_t gemm_num_tiles(const GemmDesc &g);
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s);
 
-// Lazy batch update W[:, c1:] += (-E) U[c0:c1, c1:] (trailing.hip).
-// W points at column c1; Et is [K][ldet] (ldet >= M rounded up to 128); Ub points at U[c0][c1].
-hipError_t launch_trailing_update(float *W, int64_t ldw, int64_t M, int64_t N, const float *Et, int64_t ldet, int K,
-                                  const float *Ub, int64_t ldu, hipStream_t s);
-
 // ---------------------------------------------------------------------------
 // Hessian (hessian.hip)
 // ---------------------------------------------------------------------------

@@ -25,12 +25,17 @@ struct GemmSmem {
 // Loads one 128 x 32 (A) or 32 x 128 (B) slab into registers: 4 float4 per thread.
 // `kmajor_src` == 1: the source is contiguous along the 128-wide dimension
 // (A with a_trans, B without b_trans); 0: contiguous along K.
+// VEC: every 16-byte chunk is aligned and lies either wholly inside or
+// wholly outside the matrix (the contiguous extent and the leading dimension
+// are multiples of 4), so the four loads are unconditional 16-byte loads from
+// clamped addresses, zeroed afterwards when out of range: no branches, so all
+// four stay in flight together.  Otherwise element-wise guarded loads.
+template <int VEC>
 struct SlabLoader {
     const float *p;
     int64_t ld;
     int64_t wide0, wide_lim;  // first row/col of the tile along the 128-wide dim, bound
     int kmajor_src;
-    int vec;  // float4 loads allowed (alignment)
 
     __device__ __forceinline__ void load(int64_t k0, int64_t klim, int tid, float4 (&r)[4]) const {
 #pragma unroll
@@ -45,33 +50,32 @@ struct SlabLoader {
                 k = (idx & 7) * 4;
             }
             const int64_t gw = wide0 + w, gk = k0 + k;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kmajor_src) {
-                const float *src = p + gk * ld + gw;
-                if (gk < klim) {
-                    if (vec && gw + 3 < wide_lim) {
-                        v = *reinterpret_cast<const float4 *>(src);
-                    } else {
+            if constexpr (VEC) {
+                const bool in = gk < klim && gw < wide_lim;
+                const int64_t ck = in ? gk : 0, cw = in ? gw : 0;
+                const float4 v = *reinterpret_cast<const float4 *>(kmajor_src ? p + ck * ld + cw : p + cw * ld + ck);
+                r[i] = in ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (kmajor_src) {
+                    const float *src = p + gk * ld + gw;
+                    if (gk < klim) {
                         if (gw + 0 < wide_lim) v.x = src[0];
                         if (gw + 1 < wide_lim) v.y = src[1];
                         if (gw + 2 < wide_lim) v.z = src[2];
                         if (gw + 3 < wide_lim) v.w = src[3];
                     }
-                }
-            } else {
-                const float *src = p + gw * ld + gk;
-                if (gw < wide_lim) {
-                    if (vec && gk + 3 < klim) {
-                        v = *reinterpret_cast<const float4 *>(src);
-                    } else {
+                } else {
+                    const float *src = p + gw * ld + gk;
+                    if (gw < wide_lim) {
                         if (gk + 0 < klim) v.x = src[0];
                         if (gk + 1 < klim) v.y = src[1];
                         if (gk + 2 < klim) v.z = src[2];
                         if (gk + 3 < klim) v.w = src[3];
                     }
                 }
+                r[i] = v;
             }
-            r[i] = v;
         }
     }
 
@@ -94,8 +98,8 @@ struct SlabLoader {
     }
 };
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g, int vec_a, int vec_b) {
+template <int EPI, int VA, int VB>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     const int tn = blockIdx.x, tm = blockIdx.y, bz = blockIdx.z;
     if (g.upper_only && tm > tn) return;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -113,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g, int vec_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    SlabLoader la{A, g.lda, m0, g.M, g.a_trans, vec_a};
-    SlabLoader lb{B, g.ldb, n0, g.N, g.b_trans ? 0 : 1, vec_b};
+    SlabLoader<VA> la{A, g.lda, m0, g.M, g.a_trans};
+    SlabLoader<VB> lb{B, g.ldb, n0, g.N, g.b_trans ? 0 : 1};
 
     floatx16 acc[2][2];
 #pragma unroll
@@ -155,16 +159,27 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g, int vec_
                 lb.load(k0 + BK, kend, tid, rb);
             }
             const int kr = lane >> 5, c = lane & 31;
+            // Operands (a0, a1, b0, b1) of k-step kk; the next step's are read
+            // from LDS while this step's MFMAs run (the scheduling fences keep
+            // that order).
+            float op[2][4];
+            auto rd = [&](int kk, float(&o)[4]) {
+                o[0] = sm.a[buf][kk + kr][wm * 64 + c];
+                o[1] = sm.a[buf][kk + kr][wm * 64 + 32 + c];
+                o[2] = sm.b[buf][kk + kr][wn * 64 + c];
+                o[3] = sm.b[buf][kk + kr][wn * 64 + 32 + c];
+            };
+            rd(0, op[0]);
 #pragma unroll
             for (int kk = 0; kk < BK; kk += 2) {
-                const float a0 = sm.a[buf][kk + kr][wm * 64 + c];
-                const float a1 = sm.a[buf][kk + kr][wm * 64 + 32 + c];
-                const float b0 = sm.b[buf][kk + kr][wn * 64 + c];
-                const float b1 = sm.b[buf][kk + kr][wn * 64 + 32 + c];
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+                const int cur = (kk >> 1) & 1;
+                if (kk + 2 < BK) rd(kk + 2, op[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][0], op[cur][2], acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][0], op[cur][3], acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][1], op[cur][2], acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][1], op[cur][3], acc[1][1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (more) {
                 la.store(sm.a[buf ^ 1], tid, ra);
@@ -221,16 +236,31 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 int64_t gemm_num_tiles(const GemmDesc &g) { return ceil_div(g.M, BM) * ceil_div(g.N, BN); }
 
+template <int EPI>
+void launch_epi(const GemmDesc &g, dim3 grid, int va, int vb, hipStream_t s) {
+    if (va && vb)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 1>), grid, dim3(kThreads), 0, s, g);
+    else if (va)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 0>), grid, dim3(kThreads), 0, s, g);
+    else if (vb)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 1>), grid, dim3(kThreads), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 0>), grid, dim3(kThreads), 0, s, g);
+}
+
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
     const bool bz = g.batch > 1;
-    const int vec_a = aligned16(g.A) && g.lda % 4 == 0 && (!bz || g.strideA % 4 == 0);
-    const int vec_b = aligned16(g.B) && g.ldb % 4 == 0 && (!bz || g.strideB % 4 == 0);
+    // 16-byte chunks wholly inside or outside: aligned base and stride, and
+    // the contiguous extent (the 128-wide dim, or K) a multiple of 4.
+    const bool k4 = g.K % 4 == 0;
+    const int va = aligned16(g.A) && g.lda % 4 == 0 && (!bz || g.strideA % 4 == 0) && (g.a_trans ? g.M % 4 == 0 : k4);
+    const int vb = aligned16(g.B) && g.ldb % 4 == 0 && (!bz || g.strideB % 4 == 0) && (g.b_trans ? k4 : g.N % 4 == 0);
     dim3 grid((unsigned)ceil_div(g.N, BN), (unsigned)ceil_div(g.M, BM), (unsigned)g.batch);
     if (g.epilogue == EPI_DOT)
-        hipLaunchKernelGGL(gemm_f32_kernel<EPI_DOT>, grid, dim3(kThreads), 0, s, g, vec_a, vec_b);
+        launch_epi<EPI_DOT>(g, grid, va, vb, s);
     else
-        hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, dim3(kThreads), 0, s, g, vec_a, vec_b);
+        launch_epi<EPI_STORE>(g, grid, va, vb, s);
     return hipGetLastError();
 }
 

@@ -4,14 +4,20 @@
 // §二 "方法核心" steps 3-4), and the round-to-nearest baseline.
 //
 // Per batch of B columns [c0, c0+B):
-//   block kernel   one lane per output row: the row's B weights live in
-//                  registers, the B x B block of U in LDS (read as wave-wide
-//                  broadcasts).  Column by column: fit the group grid at a
-//                  group start (from the current weights), quantize,
-//                  e = (w - w_hat) / U[j][j], push -e U[j][k] onto the later
-//                  columns of the batch, store -e into E^T.
-//   trailing GEMM  W[:, c0+B:] += (-E) U[c0:c0+B, c0+B:]  on fp32 matrix cores.
-// Rows are independent, so no lane ever talks to another.
+//   block kernel   four lanes per output row: the row's B weights live in
+//                  registers, the B x B block of U in LDS.  Column by column:
+//                  fit the group grid at a group start (from the current
+//                  weights), quantize, e = (w - w_hat) / U[j][j], push
+//                  -e U[j][k] onto the later columns of the batch, store -e
+//                  into E^T.
+//   batch update   W[:, c0+B:s1] += (-E) U[c0:c0+B, c0+B:s1]  (fp32 matrix cores)
+// The lazy update runs on two levels: the batches of one superblock of
+// kSuperCols columns [s0, s1) update only the rest of that superblock, and
+// when the superblock is done its stacked E updates every later column at
+// once, W[:, s1:] += (-E_s) U[s0:s1, s1:].  Every column still receives the
+// error of every earlier column before it is quantized (the same sums, in a
+// different fp32 order), while the trailing W is read and written once per
+// superblock instead of once per batch.
 #include "block_args.h"
 #include "quant_grid.h"
 
@@ -88,18 +94,55 @@ int group_tile(const gptq_config &c, int64_t d_in) {
 // E^T rows are padded to whole workgroups so the batch kernel stores without a row test.
 int64_t et_ld(int64_t d_out) { return ceil_div(d_out, kBlockThreads) * kBlockThreads; }
 
-// Workspace of the column pass: E^T [B][ldet] and (act-order only) a copy of
-// W for the column gather.
+constexpr int64_t kSuperCols = 1024;  // columns per superblock of the two-level lazy update
+
+// Superblock width: a multiple of the batch and, when a group spans several
+// batches, of the group (a group's grid is fitted from columns that must all
+// be up to date).  At least d_in means one superblock: no deferred update.
+int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
+    const int64_t g = c.group_size > 0 ? c.group_size : d_in;
+    const int64_t unit = gt > 0 ? c.block_size : g;  // g is a multiple of B when gt == 0
+    const int64_t sc = unit >= kSuperCols ? unit : (kSuperCols / unit) * unit;
+    return sc;
+}
+
+// Workspace of the column pass: E^T of a whole superblock [S][ldet] (one batch
+// when there is a single superblock) and (act-order only) a copy of W for the
+// column gather.
 struct QuantLayout {
     size_t et_off, wc_off, total;
+    int64_t sc;       // superblock width
+    int64_t et_rows;  // rows of E^T kept
 };
 
 QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     QuantLayout l;
+    l.sc = super_cols(c, d_in, group_tile(c, d_in));
+    l.et_rows = l.sc < d_in ? l.sc : c.block_size;
     l.et_off = 0;
-    l.wc_off = align_up((size_t)c.block_size * (size_t)et_ld(d_out) * sizeof(float), 256);
+    l.wc_off = align_up((size_t)l.et_rows * (size_t)et_ld(d_out) * sizeof(float), 256);
     l.total = l.wc_off + (c.act_order ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
     return l;
+}
+
+// W[:, c1:c1+n] += (-E) U[k0:k0+k, c1:c1+n] with -E^T stored as Et [k][ldet].
+hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, int64_t ldet, const float *U, int64_t k0,
+                       int64_t k, int64_t c1, int64_t n, hipStream_t s) {
+    if (n <= 0 || k <= 0) return hipSuccess;
+    GemmDesc g;
+    g.M = d_out;
+    g.N = n;
+    g.K = k;
+    g.A = Et;  // A[m][kk] = Et[kk][m]
+    g.lda = ldet;
+    g.a_trans = 1;
+    g.B = U + k0 * d_in + c1;
+    g.ldb = d_in;
+    g.C = W + c1;
+    g.ldc = d_in;
+    g.alpha = 1.0f;
+    g.beta = 1.0f;
+    return launch_gemm_f32(g, s);
 }
 
 }  // namespace
@@ -145,47 +188,54 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     }
     const int64_t ldet = et_ld(d_out);
     const int vec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15) == 0);
-    for (int64_t c0 = 0; c0 < d_in; c0 += B) {
-        const int nc = (int)std::min<int64_t>(B, d_in - c0);
-        if (gt == 0 && c0 % g == 0) {
-            const int64_t waves = d_out;
-            hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W, d_in,
-                               d_out, g, ng, c0 / g, (int64_t)1, c.bits, c.symmetric, (uint8_t *)nullptr, d_in, scales,
-                               zeros);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-        BlockArgs a{};
-        a.W = W;
-        a.ldw = d_in;
-        a.d_out = d_out;
-        a.c0 = c0;
-        a.ncols = nc;
-        a.U = U;
-        a.ldu = d_in;
-        a.Et = Et;
-        a.ldet = ldet;
-        a.codes = codes;
-        a.ldc = d_in;
-        a.perm = pp;
-        a.scales = scales;
-        a.zeros = zeros;
-        a.ng = ng;
-        a.g = g;
-        a.bits = c.bits;
-        a.sym = c.symmetric ? 1 : 0;
-        a.vec = vec;
-        if (B == 32)
-            e = launch_block_32(a, gt, s);
-        else if (B == 64)
-            e = launch_block_64(a, gt, s);
-        else
-            e = launch_block_128(a, gt, s);
-        if (e != hipSuccess) return e;
-        const int64_t c1 = c0 + nc;
-        if (c1 < d_in) {
-            e = launch_trailing_update(W + c1, d_in, d_out, d_in - c1, Et, ldet, nc, U + c0 * d_in + c1, d_in, s);
+    const int64_t sc = lay.sc;
+    const bool deferred = sc < d_in;  // superblocks leave an update for the columns beyond them
+    for (int64_t s0 = 0; s0 < d_in; s0 += sc) {
+        const int64_t s1 = std::min<int64_t>(s0 + sc, d_in);
+        for (int64_t c0 = s0; c0 < s1; c0 += B) {
+            const int nc = (int)std::min<int64_t>(B, s1 - c0);
+            if (gt == 0 && c0 % g == 0) {
+                const int64_t waves = d_out;
+                hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W,
+                                   d_in, d_out, g, ng, c0 / g, (int64_t)1, c.bits, c.symmetric, (uint8_t *)nullptr, d_in,
+                                   scales, zeros);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            float *Eb = Et + (deferred ? (c0 - s0) * ldet : 0);  // this batch's rows of E^T
+            BlockArgs a{};
+            a.W = W;
+            a.ldw = d_in;
+            a.d_out = d_out;
+            a.c0 = c0;
+            a.ncols = nc;
+            a.U = U;
+            a.ldu = d_in;
+            a.Et = Eb;
+            a.ldet = ldet;
+            a.codes = codes;
+            a.ldc = d_in;
+            a.perm = pp;
+            a.scales = scales;
+            a.zeros = zeros;
+            a.ng = ng;
+            a.g = g;
+            a.bits = c.bits;
+            a.sym = c.symmetric ? 1 : 0;
+            a.vec = vec;
+            if (B == 32)
+                e = launch_block_32(a, gt, s);
+            else if (B == 64)
+                e = launch_block_64(a, gt, s);
+            else
+                e = launch_block_128(a, gt, s);
             if (e != hipSuccess) return e;
+            // the rest of the superblock
+            const int64_t c1 = c0 + nc;
+            if ((e = lazy_update(W, d_out, d_in, Eb, ldet, U, c0, nc, c1, s1 - c1, s)) != hipSuccess) return e;
         }
+        // every column beyond the superblock, with the superblock's whole E
+        if (deferred && (e = lazy_update(W, d_out, d_in, Et, ldet, U, s0, s1 - s0, s1, d_in - s1, s)) != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }

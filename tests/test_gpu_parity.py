@@ -164,6 +164,12 @@ PASS_CASES = [
     (2, False, 128, 64, 64, 256),
     (8, True, 128, 128, 64, 256),
     (4, False, 256, 128, 64, 512),
+    # wider than one 1024-column superblock: deferred updates of the later columns
+    (4, False, 128, 128, 64, 2304),   # 1024 + 1024 + a partial 256
+    (4, True, 256, 128, 48, 2560),    # groups spanning two batches
+    (3, True, 32, 32, 40, 1152),      # 32-column batches, a partial last superblock
+    (4, False, 1024, 128, 32, 2048),  # one group per superblock
+    (4, False, 0, 128, 32, 1536),     # per-row grid: one superblock of 1536
 ]
 
 
@@ -242,7 +248,7 @@ E2E = [
     ("q_proj_7b", dict(d_out=256, d_in=1024, n_tok=8192)),
     ("down_proj_7b", dict(d_out=192, d_in=1408, n_tok=4096)),
     ("o_proj_70b", dict(d_out=256, d_in=1024, n_tok=4096)),
-    ("up_proj_70b", dict(d_out=320, d_in=1024, n_tok=4096)),
+    ("up_proj_70b", dict(d_out=320, d_in=1280, n_tok=4096)),  # act-order across a superblock boundary
 ]
 
 
