@@ -81,8 +81,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs GPTQ on one GPU only "
-              f"(the layer's H all-reduce and row sharding are described in DESIGN.md, not built).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: this benchmark runs GPTQ on one GPU only "
+              f"(sharding the layer: an all-reduce of H over token slices, then the column pass split by output rows, is not built).", file=sys.stderr)
         return 2
 
     import torch

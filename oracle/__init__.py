@@ -11,7 +11,7 @@ Steps, in the pages' order:
    方法原理与实现详解", §4.1 GPTQ, the Hessian line of the printed sketch).
 2. ``act_order_perm``: optional column order by descending diag(H) (page
    "量化经典：LLM.int8 / GPTQ / AWQ", §二 "方法核心" step 2 orders columns by the
-   Hessian; the descending direction is this build's workload choice).
+   Hessian; the descending direction is the one the workload definition fixes).
 3. ``damp``: H_d = H + lambda I with lambda = damp_rel * mean(diag H) (not on the
    pages; the standard regulariser that makes H_d positive definite).
 4. ``inv_chol_upper``: U = upper Cholesky factor of H_d^-1 (U^T U = H_d^-1).  The

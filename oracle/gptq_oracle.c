@@ -21,7 +21,7 @@
  * actually gets is (code - zero) * scale rounded to fp32, and the rounding
  * decision is made in the same precision as on the GPU.
  *
- * Readings of points the pages leave open (each listed in the design doc):
+ * Readings of points the pages leave open:
  *  - symmetric grid: q in [-qmax, qmax], qmax = 2^(b-1)-1, scale = max|x|/qmax,
  *    stored code = q + 2^(b-1) with zero point 2^(b-1);
  *  - asymmetric grid: lo = min(min x, 0), hi = max(max x, 0),
