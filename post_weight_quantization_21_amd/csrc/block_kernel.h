@@ -37,82 +37,96 @@ __device__ __forceinline__ float quad_bcast(float v, int src_lane) {
 __device__ __forceinline__ float quad_xor1(float v) { return dpp_f<0xB1>(v); }  // quad_perm(1,0,3,2)
 __device__ __forceinline__ float quad_xor2(float v) { return dpp_f<0x4E>(v); }  // quad_perm(2,3,0,1)
 
-constexpr int kRowLanes = 4;                           // lanes per output row
-constexpr int kBlockRows = kBlockThreads / kRowLanes;  // rows per workgroup
+constexpr int kRowLanes = 4;  // lanes per output row
 
 // Each output row is owned by a quad of lanes; lane q of the quad keeps
 // columns q, q+4, q+8, ... of the batch in registers.  Column j's owner
 // broadcasts the weight to its quad (DPP), all four lanes quantize it (same
 // result), and each lane pushes the error onto its own later columns.
-template <int BT, int GT>
-__global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(BlockArgs a) {
+// NT threads per workgroup (NT / 4 rows).
+template <int BT, int GT, int NT>
+__global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     constexpr int CPL = BT / kRowLanes;
+    constexpr int kRows = NT / kRowLanes;
     __shared__ float us[BT][BT];  // U block, strictly lower part and diagonal zero
     __shared__ float inv_d[BT];
     __shared__ int32_t pcol[BT];
     const int tid = threadIdx.x;
     const int nc = a.ncols;
     const int q = tid & (kRowLanes - 1);
-    const int64_t r = (int64_t)blockIdx.x * kBlockRows + (tid >> 2);
+    const int64_t r = (int64_t)blockIdx.x * kRows + (tid >> 2);
     const bool active = r < a.d_out;
     float *wrow = a.W + r * a.ldw + a.c0;
-    // Every global load of the prologue (the U block, the permutation and the
-    // row's weights) is issued before the first LDS store.
-    constexpr int kUPer = (BT * BT / 4 + kBlockThreads - 1) / kBlockThreads;  // float4 chunks per thread
-    float4 uv[kUPer];
-    {
-        const float *src = a.U + a.c0 * a.ldu + a.c0;
-        const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
-        if (vec) {  // full, aligned batch: 16-byte loads
-#pragma unroll
-            for (int u = 0; u < kUPer; ++u) {
-                const int e4 = tid + u * kBlockThreads;
-                const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-                uv[u] = e4 < BT * BT / 4 ? *reinterpret_cast<const float4 *>(src + i * a.ldu + k)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kUPer; ++u) {
-                const int e4 = tid + u * kBlockThreads;
-                const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-                const bool in = e4 < BT * BT / 4 && i < nc;
-                const float *p = src + i * a.ldu + k;
-                uv[u].x = (in && k + 0 < nc) ? p[0] : 0.0f;
-                uv[u].y = (in && k + 1 < nc) ? p[1] : 0.0f;
-                uv[u].z = (in && k + 2 < nc) ? p[2] : 0.0f;
-                uv[u].w = (in && k + 3 < nc) ? p[3] : 0.0f;
-            }
-        }
-    }
-    int32_t pc = 0;
-    if (tid < BT) {
-        const int64_t k = a.c0 + (tid < nc ? tid : 0);
-        pc = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + tid);
-    }
+    // Global loads of the prologue are issued in batches ahead of their LDS
+    // stores: first the row's weights and the batch's permutation entries,
+    // then the U block in passes of at most 16 16-byte chunks per thread.
     float w[CPL];
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
         const int k = q + kRowLanes * t;
         w[t] = (active && k < nc) ? wrow[k] : 0.0f;
     }
+    constexpr int kPc = (BT + NT - 1) / NT;  // permutation entries per thread
+    int32_t pc[kPc];
 #pragma unroll
-    for (int u = 0; u < kUPer; ++u) {
-        const int e4 = tid + u * kBlockThreads;
-        if (e4 >= BT * BT / 4) break;
-        const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-        float4 v = uv[u];
-        if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
-        if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
-        if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
-        if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
-        v.x = (k + 0 > i) ? v.x : 0.0f;
-        v.y = (k + 1 > i) ? v.y : 0.0f;
-        v.z = (k + 2 > i) ? v.z : 0.0f;
-        v.w = (k + 3 > i) ? v.w : 0.0f;
-        *reinterpret_cast<float4 *>(&us[i][k]) = v;
+    for (int u = 0; u < kPc; ++u) {
+        const int c = tid + u * NT;
+        const int64_t k = a.c0 + (c < nc ? c : 0);
+        pc[u] = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + c);
     }
-    if (tid < BT) pcol[tid] = pc;
+    {
+        constexpr int kChunks = BT * BT / 4;                 // 16-byte chunks of the U block
+        constexpr int kUPer = (kChunks + NT - 1) / NT;       // per thread
+        constexpr int kPass = kUPer < 16 ? kUPer : 16;       // per thread and pass
+        const float *src = a.U + a.c0 * a.ldu + a.c0;
+        const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
+#pragma unroll
+        for (int p0 = 0; p0 < kUPer; p0 += kPass) {
+            float4 uv[kPass];
+            if (vec) {  // full, aligned batch: 16-byte loads
+#pragma unroll
+                for (int u = 0; u < kPass; ++u) {
+                    const int e4 = tid + (p0 + u) * NT;
+                    const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+                    uv[u] = e4 < kChunks ? *reinterpret_cast<const float4 *>(src + i * a.ldu + k)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kPass; ++u) {
+                    const int e4 = tid + (p0 + u) * NT;
+                    const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+                    const bool in = e4 < kChunks && i < nc;
+                    const float *p = src + i * a.ldu + k;
+                    uv[u].x = (in && k + 0 < nc) ? p[0] : 0.0f;
+                    uv[u].y = (in && k + 1 < nc) ? p[1] : 0.0f;
+                    uv[u].z = (in && k + 2 < nc) ? p[2] : 0.0f;
+                    uv[u].w = (in && k + 3 < nc) ? p[3] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                const int e4 = tid + (p0 + u) * NT;
+                if (e4 >= kChunks) break;
+                const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
+                float4 v = uv[u];
+                if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
+                if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
+                if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
+                if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
+                v.x = (k + 0 > i) ? v.x : 0.0f;
+                v.y = (k + 1 > i) ? v.y : 0.0f;
+                v.z = (k + 2 > i) ? v.z : 0.0f;
+                v.w = (k + 3 > i) ? v.w : 0.0f;
+                *reinterpret_cast<float4 *>(&us[i][k]) = v;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPc; ++u) {
+        const int c = tid + u * NT;
+        if (c < BT) pcol[c] = pc[u];  // every entry 0..BT-1 is written
+    }
     __syncthreads();
 
     Grid gr = grid_make(0.0f, 0.0f, 0.0f, a.bits, a.sym);
@@ -186,26 +200,25 @@ __global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(BlockArgs a) 
     }
 }
 
-template <int BT>
-hipError_t launch_block_bt(const BlockArgs &a, int gt, hipStream_t s) {
-    if (!a.Et || !a.W || !a.U || !a.codes) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)ceil_div(a.d_out, kBlockRows);
+template <int BT, int NT>
+hipError_t launch_block_nt(const BlockArgs &a, int gt, hipStream_t s) {
+    const unsigned grid = (unsigned)ceil_div(a.d_out, NT / kRowLanes);
     switch (gt) {
     case 0:
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 0>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT>), dim3(grid), dim3(NT), 0, s, a);
         break;
     case 32:
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 32>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 32, NT>), dim3(grid), dim3(NT), 0, s, a);
         break;
     case 64:
         if constexpr (BT >= 64) {
-            hipLaunchKernelGGL((gptq_block_kernel<BT, 64>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+            hipLaunchKernelGGL((gptq_block_kernel<BT, 64, NT>), dim3(grid), dim3(NT), 0, s, a);
             break;
         }
         return hipErrorInvalidValue;
     case 128:
         if constexpr (BT >= 128) {
-            hipLaunchKernelGGL((gptq_block_kernel<BT, 128>), dim3(grid), dim3(kBlockThreads), 0, s, a);
+            hipLaunchKernelGGL((gptq_block_kernel<BT, 128, NT>), dim3(grid), dim3(NT), 0, s, a);
             break;
         }
         return hipErrorInvalidValue;
@@ -213,6 +226,15 @@ hipError_t launch_block_bt(const BlockArgs &a, int gt, hipStream_t s) {
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Four-wave workgroups (64 rows).  One-wave workgroups (16 rows), which
+// spread a small layer over more CUs, measured slower: each row's column chain,
+// not the CU count, sets the time.
+template <int BT>
+hipError_t launch_block_bt(const BlockArgs &a, int gt, hipStream_t s) {
+    if (!a.Et || !a.W || !a.U || !a.codes) return hipErrorInvalidValue;
+    return launch_block_nt<BT, kBlockThreads>(a, gt, s);
 }
 
 }  // namespace gptq
