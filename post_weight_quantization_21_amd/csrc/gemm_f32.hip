@@ -1,50 +1,54 @@
 // fp32 matrix-core GEMM for gfx950:  C = alpha * op(A) op(B) + beta * C.
 //
 // One kernel serves every dense fp32 contraction of the library: the lazy
-// batch update of GPTQ (W[:, trail] -= E U[block, trail]), the panel solve and
-// symmetric rank-k update of the blocked Cholesky factorization, the
-// triangular products of the triangular inverse, and the layer-loss product
-// D H.  Tiles are 128 x 128 per 256-thread workgroup (4 wave64s, each 64 x 64
-// as 2 x 2 v_mfma_f32_32x32x2f32 tiles), K staged through LDS in slabs of
-// 32, double buffered, one barrier per slab.  Operands are stored K-major in
-// LDS so both matrix-core operands are read as consecutive 4-byte words.
+// batch update of GPTQ (W[:, trail] -= E U[block, trail]), the triangular
+// products of the triangular inverse, and the layer-loss product D H.
+// Tiles are T x T per 256-thread workgroup (4 wave64s in 2 x 2, each
+// T/2 x T/2 as v_mfma_f32_32x32x2f32 blocks), T = 128, or T = 64 when a
+// launch has too few 128-wide tiles to fill the chip (a quarter of the
+// dependent matrix-core chain per wave).  K is staged through LDS in slabs of
+// 32, double buffered through registers, one barrier per slab.  Operands are
+// stored K-major in LDS so both matrix-core operands are read as consecutive
+// 4-byte words; each k-step's operands are read one step ahead of its MFMAs.
 #include "common.h"
 
 namespace gptq {
 namespace {
 
-constexpr int BM = kGemmTile, BN = kGemmTile, BK = 32;
-constexpr int LDS_LD = BM + 4;  // floats per LDS row (keeps float4 alignment)
+constexpr int BK = 32;
 constexpr int kThreads = 256;
 
+template <int T>
 struct GemmSmem {
-    float a[2][BK][LDS_LD];
-    float b[2][BK][LDS_LD];
+    float a[2][BK][T + 4];  // rows of T + 4 floats keep float4 alignment
+    float b[2][BK][T + 4];
 };
 
-// Loads one 128 x 32 (A) or 32 x 128 (B) slab into registers: 4 float4 per thread.
-// `kmajor_src` == 1: the source is contiguous along the 128-wide dimension
+// Loads one T x 32 (A) or 32 x T (B) slab into registers: T/32 float4 per thread.
+// `kmajor_src` == 1: the source is contiguous along the T-wide dimension
 // (A with a_trans, B without b_trans); 0: contiguous along K.
 // VEC: every 16-byte chunk is aligned and lies either wholly inside or
 // wholly outside the matrix (the contiguous extent and the leading dimension
-// are multiples of 4), so the four loads are unconditional 16-byte loads from
+// are multiples of 4), so the loads are unconditional 16-byte loads from
 // clamped addresses, zeroed afterwards when out of range: no branches, so all
-// four stay in flight together.  Otherwise element-wise guarded loads.
-template <int VEC>
+// of them stay in flight together.  Otherwise element-wise guarded loads.
+template <int T, int VEC>
 struct SlabLoader {
+    static constexpr int kPer = T * BK / 4 / kThreads;  // float4 per thread
+    static constexpr int kWideChunks = T / 4;           // float4 per K row (k-major source)
     const float *p;
     int64_t ld;
-    int64_t wide0, wide_lim;  // first row/col of the tile along the 128-wide dim, bound
+    int64_t wide0, wide_lim;  // first row/col of the tile along the T-wide dim, bound
     int kmajor_src;
 
-    __device__ __forceinline__ void load(int64_t k0, int64_t klim, int tid, float4 (&r)[4]) const {
+    __device__ __forceinline__ void load(int64_t k0, int64_t klim, int tid, float4 (&r)[kPer]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kPer; ++i) {
             const int idx = tid + kThreads * i;
             int64_t w, k;
             if (kmajor_src) {
-                k = idx >> 5;
-                w = (idx & 31) * 4;
+                k = idx / kWideChunks;
+                w = (idx % kWideChunks) * 4;
             } else {
                 w = idx >> 3;
                 k = (idx & 7) * 4;
@@ -80,12 +84,12 @@ struct SlabLoader {
     }
 
     // Writes the registers into an LDS slab laid out [k][wide].
-    __device__ __forceinline__ void store(float (*s)[LDS_LD], int tid, const float4 (&r)[4]) const {
+    __device__ __forceinline__ void store(float (*s)[T + 4], int tid, const float4 (&r)[kPer]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kPer; ++i) {
             const int idx = tid + kThreads * i;
             if (kmajor_src) {
-                const int k = idx >> 5, w = (idx & 31) * 4;
+                const int k = idx / kWideChunks, w = (idx % kWideChunks) * 4;
                 *reinterpret_cast<float4 *>(&s[k][w]) = r[i];
             } else {
                 const int w = idx >> 3, k = (idx & 7) * 4;
@@ -98,11 +102,13 @@ struct SlabLoader {
     }
 };
 
-template <int EPI, int VA, int VB>
+template <int EPI, int VA, int VB, int T>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
+    constexpr int QB = T / 64;  // 32x32 MFMA blocks per wave along each dimension
+    constexpr int HW = T / 2;   // wave tile edge
     const int tn = blockIdx.x, tm = blockIdx.y, bz = blockIdx.z;
-    if (g.upper_only && tm > tn) return;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    if (g.upper_only && tm > tn) return;  // strictly below the diagonal: nothing to store
+    const int64_t m0 = (int64_t)tm * T, n0 = (int64_t)tn * T;
 
     const float *A = g.A + bz * g.strideA;
     const float *B = g.B + bz * g.strideB;
@@ -110,42 +116,43 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
 
     int64_t kbeg = 0, kend = g.K;
     if (g.a_upper) kbeg = m0 < kbeg ? kbeg : m0;
-    if (g.b_upper) kend = (n0 + BN) < kend ? (n0 + BN) : kend;
+    if (g.b_upper) kend = (n0 + T) < kend ? (n0 + T) : kend;
     kbeg = (kbeg / BK) * BK;
 
-    __shared__ GemmSmem sm;
+    __shared__ GemmSmem<T> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    SlabLoader<VA> la{A, g.lda, m0, g.M, g.a_trans};
-    SlabLoader<VB> lb{B, g.ldb, n0, g.N, g.b_trans ? 0 : 1};
+    SlabLoader<T, VA> la{A, g.lda, m0, g.M, g.a_trans};
+    SlabLoader<T, VB> lb{B, g.ldb, n0, g.N, g.b_trans ? 0 : 1};
+    constexpr int kPer = SlabLoader<T, VA>::kPer;
 
-    floatx16 acc[2][2];
+    floatx16 acc[QB][QB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < QB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < QB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // C values are fetched before the K loop so their latency hides behind the
     // matrix-core work; every store comes after every load of the tile.
-    float cold[2][2][16];
+    float cold[QB][QB][16];
     if (EPI == EPI_STORE && g.beta != 0.0f) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < QB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < QB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                    const int64_t n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
                     cold[i][j][r] = (m < g.M && n < g.N) ? C[m * g.ldc + n] : 0.0f;
                 }
     }
 
     if (kbeg < kend) {
-        float4 ra[4], rb[4];
+        float4 ra[kPer], rb[kPer];
         la.load(kbeg, kend, tid, ra);
         lb.load(kbeg, kend, tid, rb);
         la.store(sm.a[0], tid, ra);
@@ -159,15 +166,15 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
                 lb.load(k0 + BK, kend, tid, rb);
             }
             const int kr = lane >> 5, c = lane & 31;
-            // Operands (a0, a1, b0, b1) of k-step kk; the next step's are read
-            // from LDS while this step's MFMAs run (the scheduling fences keep
-            // that order).
-            float op[2][4];
-            auto rd = [&](int kk, float(&o)[4]) {
-                o[0] = sm.a[buf][kk + kr][wm * 64 + c];
-                o[1] = sm.a[buf][kk + kr][wm * 64 + 32 + c];
-                o[2] = sm.b[buf][kk + kr][wn * 64 + c];
-                o[3] = sm.b[buf][kk + kr][wn * 64 + 32 + c];
+            // Operands of k-step kk (A blocks, then B blocks); the next step's
+            // are read from LDS while this step's MFMAs run (the scheduling
+            // fences keep that order).
+            float op[2][2 * QB];
+            auto rd = [&](int kk, float(&o)[2 * QB]) {
+#pragma unroll
+                for (int i = 0; i < QB; ++i) o[i] = sm.a[buf][kk + kr][wm * HW + i * 32 + c];
+#pragma unroll
+                for (int j = 0; j < QB; ++j) o[QB + j] = sm.b[buf][kk + kr][wn * HW + j * 32 + c];
             };
             rd(0, op[0]);
 #pragma unroll
@@ -175,10 +182,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
                 const int cur = (kk >> 1) & 1;
                 if (kk + 2 < BK) rd(kk + 2, op[cur ^ 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][0], op[cur][2], acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][0], op[cur][3], acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][1], op[cur][2], acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][1], op[cur][3], acc[1][1], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < QB; ++i)
+#pragma unroll
+                    for (int j = 0; j < QB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][i], op[cur][QB + j], acc[i][j], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (more) {
@@ -192,13 +200,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
 
     if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < QB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < QB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                    const int64_t n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
                     if (m < g.M && n < g.N && (!g.upper_only || m <= n)) {
                         float v = g.alpha * acc[i][j][r];
                         if (g.beta != 0.0f) v += g.beta * cold[i][j][r];
@@ -208,13 +216,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     } else {
         double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < QB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < QB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-                    const int64_t n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
                     if (m < g.M && n < g.N) s += (double)acc[i][j][r] * (double)g.Dm[m * g.ldd + n];
                 }
 #pragma unroll
@@ -232,35 +240,44 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+template <int EPI, int T>
+void launch_tile(const GemmDesc &g, int va, int vb, hipStream_t s) {
+    dim3 grid((unsigned)ceil_div(g.N, T), (unsigned)ceil_div(g.M, T), (unsigned)g.batch);
+    if (va && vb)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 1, T>), grid, dim3(kThreads), 0, s, g);
+    else if (va)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 0, T>), grid, dim3(kThreads), 0, s, g);
+    else if (vb)
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 1, T>), grid, dim3(kThreads), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 0, T>), grid, dim3(kThreads), 0, s, g);
+}
+
+constexpr int kCUs = 256;
+
 }  // namespace
 
-int64_t gemm_num_tiles(const GemmDesc &g) { return ceil_div(g.M, BM) * ceil_div(g.N, BN); }
-
-template <int EPI>
-void launch_epi(const GemmDesc &g, dim3 grid, int va, int vb, hipStream_t s) {
-    if (va && vb)
-        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 1>), grid, dim3(kThreads), 0, s, g);
-    else if (va)
-        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 0>), grid, dim3(kThreads), 0, s, g);
-    else if (vb)
-        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 1>), grid, dim3(kThreads), 0, s, g);
-    else
-        hipLaunchKernelGGL((gemm_f32_kernel<EPI, 0, 0>), grid, dim3(kThreads), 0, s, g);
-}
+// The loss reduction indexes its partial sums by 128-wide tiles: EPI_DOT always uses them.
+int64_t gemm_num_tiles(const GemmDesc &g) { return ceil_div(g.M, kGemmTile) * ceil_div(g.N, kGemmTile); }
 
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
     const bool bz = g.batch > 1;
     // 16-byte chunks wholly inside or outside: aligned base and stride, and
-    // the contiguous extent (the 128-wide dim, or K) a multiple of 4.
+    // the contiguous extent (the tile-wide dim, or K) a multiple of 4.
     const bool k4 = g.K % 4 == 0;
     const int va = aligned16(g.A) && g.lda % 4 == 0 && (!bz || g.strideA % 4 == 0) && (g.a_trans ? g.M % 4 == 0 : k4);
     const int vb = aligned16(g.B) && g.ldb % 4 == 0 && (!bz || g.strideB % 4 == 0) && (g.b_trans ? k4 : g.N % 4 == 0);
-    dim3 grid((unsigned)ceil_div(g.N, BN), (unsigned)ceil_div(g.M, BM), (unsigned)g.batch);
-    if (g.epilogue == EPI_DOT)
-        launch_epi<EPI_DOT>(g, grid, va, vb, s);
-    else
-        launch_epi<EPI_STORE>(g, grid, va, vb, s);
+    if (g.epilogue == EPI_DOT) {
+        launch_tile<EPI_DOT, kGemmTile>(g, va, vb, s);
+    } else {
+        // 64-wide tiles when 128-wide ones would give fewer than two per CU.
+        const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128) * g.batch;
+        if (tiles128 < 2 * kCUs)
+            launch_tile<EPI_STORE, 64>(g, va, vb, s);
+        else
+            launch_tile<EPI_STORE, 128>(g, va, vb, s);
+    }
     return hipGetLastError();
 }
 
