@@ -48,7 +48,12 @@ template <int BT, int GT, int NT>
 __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     constexpr int CPL = BT / kRowLanes;
     constexpr int kRows = NT / kRowLanes;
-    __shared__ float us[BT][BT];  // U block, strictly lower part and diagonal zero
+    // The B x B block of U, strictly upper part (zero on and below the
+    // diagonal), laid out per quad lane: ut[j][p][q][i] = U[j][q + 4 (4p + i)],
+    // so lane q reads its columns of row j as contiguous 16-byte words and the
+    // four lanes of a quad hit four different bank groups.
+    constexpr int NP = CPL / 4;
+    __shared__ __attribute__((aligned(16))) float ut[BT][NP][kRowLanes][4];
     __shared__ float inv_d[BT];
     __shared__ int32_t pcol[BT];
     const int tid = threadIdx.x;
@@ -114,11 +119,12 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                 if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
                 if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
                 if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
-                v.x = (k + 0 > i) ? v.x : 0.0f;
-                v.y = (k + 1 > i) ? v.y : 0.0f;
-                v.z = (k + 2 > i) ? v.z : 0.0f;
-                v.w = (k + 3 > i) ? v.w : 0.0f;
-                *reinterpret_cast<float4 *>(&us[i][k]) = v;
+                // columns k .. k+3 belong to quad lanes 0..3, at t = k / 4
+                const int t = k / kRowLanes;
+                ut[i][t / 4][0][t % 4] = (k + 0 > i) ? v.x : 0.0f;
+                ut[i][t / 4][1][t % 4] = (k + 1 > i) ? v.y : 0.0f;
+                ut[i][t / 4][2][t % 4] = (k + 2 > i) ? v.z : 0.0f;
+                ut[i][t / 4][3][t % 4] = (k + 3 > i) ? v.w : 0.0f;
             }
         }
     }
@@ -143,9 +149,22 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     for (int t = 0; t < (CPL + 3) / 4; ++t) cw[t] = 0u;
     float *et = a.Et + r;  // rows past d_out land in the padding of E^T
 
+    // This lane's part of row j of U (and 1/U_jj) is read one column ahead, so
+    // the LDS reads overlap the previous column's quantization chain.
+    float4 urow[2][NP];
+    float idn[2];
+    auto load_row = [&](int j, float4(&dst)[NP], float &id) {
+#pragma unroll
+        for (int p = (j / kRowLanes) / 4; p < NP; ++p) dst[p] = *reinterpret_cast<const float4 *>(&ut[j][p][q][0]);
+        id = inv_d[j];
+    };
+    load_row(0, urow[0], idn[0]);
+
 #pragma unroll
     for (int j = 0; j < BT; ++j) {
         const int oq = j & (kRowLanes - 1), ot = j / kRowLanes;
+        const int cur = j & 1;
+        if (j + 1 < BT) load_row(j + 1, urow[cur ^ 1], idn[cur ^ 1]);
         if constexpr (GT > 0) {
             if (j % GT == 0) {
                 float amax = 0.0f, lo = 0.0f, hi = 0.0f;
@@ -169,11 +188,17 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         const float wj = quad_bcast(w[ot], oq);
         const float code = grid_code(wj, gr);
         const float wh = grid_dequant(code, gr);
-        const float e = (wj - wh) * inv_d[j];
+        const float e = (wj - wh) * idn[cur];
         cw[ot / 4] |= (q == oq ? (uint32_t)code : 0u) << (8 * (ot & 3));
         et[(int64_t)j * a.ldet] = -e;
 #pragma unroll
-        for (int t = ot; t < CPL; ++t) w[t] = fmaf(-e, us[j][q + kRowLanes * t], w[t]);
+        for (int p = ot / 4; p < NP; ++p) {
+            const float4 u = urow[cur][p];
+            const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * p + i >= ot) w[4 * p + i] = fmaf(-e, uu[i], w[4 * p + i]);
+        }
     }
 
     if (!active) return;
