@@ -241,10 +241,13 @@ __device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) 
     tj = i + (int)(t - before);
 }
 
-template <int FT>
+// PRE: P was computed for every row block by p_kernel; the tiles load P_i^T
+// and P_j^T from its k-major copy Tw instead of forming them.
+template <int FT, bool PRE>
 __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, float *__restrict__ Tf,
-                                                         float *__restrict__ U, int64_t d, int64_t lda, int64_t k0,
-                                                         int nb, int nt, int32_t *__restrict__ info) {
+                                                         const float *__restrict__ Tw, float *__restrict__ U, int64_t d,
+                                                         int64_t lda, int64_t k0, int nb, int nt,
+                                                         int32_t *__restrict__ info) {
     constexpr int QB = FT / 64;  // 32-row MFMA blocks per wave quadrant edge
     constexpr int FLD = FT + 4;
     // Tiles in reverse order: workgroup 0 takes the last diagonal tile, whose
@@ -275,96 +278,116 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
                 cold[si][ri][g] = (r < k0 && sc < k0) ? *reinterpret_cast<const float4 *>(A + r * lda + sc)
                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-    // (2) panel rows i and j (columns past the block's nb are zero) and V.
+    // (2) panel rows i and j -- columns past the block's nb are zero -- and V;
+    // with PRE, the k-major P^T columns of rows i and j instead.
     constexpr int kPer = FT * NB / 4 / kFThreads;
     float4 av[kPer], bv[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e4 = tid + q * kFThreads;
-        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-        // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
-        const bool in = m < nb;
-        av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-        bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
-                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (PRE) {
+            // Pt[c][r]: float4 along r; rows past k0 do not occur (k0 is a multiple of FT)
+            const int c = e4 / (FT / 4), r = (e4 % (FT / 4)) * 4;
+            av[q] = *reinterpret_cast<const float4 *>(Tw + c * lda + r0 + r);
+            bv[q] = diag ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4 *>(Tw + c * lda + s0 + r);
+        } else {
+            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+            // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
+            const bool in = m < nb;
+            av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
-    constexpr int kVPer = NB * NB / kFThreads;
+    constexpr int kVPer = PRE ? 1 : NB * NB / kFThreads;
     float vv[kVPer];
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int q = 0; q < kVPer; ++q) {
-        const int e = tid + q * kFThreads;
-        const int c = e / NB, m = e % NB;
-        vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + q * kFThreads;
+            const int c = e / NB, m = e % NB;
+            vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+        }
     }
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e4 = tid + q * kFThreads;
-        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-        float4 a = av[q], b = bv[q];
-        if (m + 1 >= nb) a.y = b.y = 0.0f;
-        if (m + 2 >= nb) a.z = b.z = 0.0f;
-        if (m + 3 >= nb) a.w = b.w = 0.0f;
-        sm.pi[m + 0][r] = a.x;
-        sm.pi[m + 1][r] = a.y;
-        sm.pi[m + 2][r] = a.z;
-        sm.pi[m + 3][r] = a.w;
-        if (!diag) {
-            sm.pj[m + 0][r] = b.x;
-            sm.pj[m + 1][r] = b.y;
-            sm.pj[m + 2][r] = b.z;
-            sm.pj[m + 3][r] = b.w;
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kVPer; ++q) {
-        const int e = tid + q * kFThreads;
-        const int c = e / NB, m = e % NB;
-        sm.vb[m][c] = vv[q];
-    }
-    __syncthreads();
-
-    // P^T[c][r] = sum_m V[c][m] panel[r][m]: 2 x FT/32 output blocks of 32x32,
-    // FT/64 per wave; block b = wave * QB + t covers c-block b % 2, r-block b / 2.
-    floatx16 pa[QB], pb[QB];
-#pragma unroll
-    for (int t = 0; t < QB; ++t)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) pa[t][q] = pb[t][q] = 0.0f;
-#pragma unroll 8
-    for (int m = 0; m < NB; m += 2) {
-#pragma unroll
-        for (int t = 0; t < QB; ++t) {
-            const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
-            const float v0 = sm.vb[m + hi][cb * 32 + lo];
-            const float xa = sm.pi[m + hi][rb * 32 + lo];
-            pa[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[t], 0, 0, 0);
+        if constexpr (PRE) {
+            const int c = e4 / (FT / 4), r = (e4 % (FT / 4)) * 4;
+            *reinterpret_cast<float4 *>(&sm.pi[c][r]) = av[q];
+            if (!diag) *reinterpret_cast<float4 *>(&sm.pj[c][r]) = bv[q];
+        } else {
+            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+            float4 a = av[q], b = bv[q];
+            if (m + 1 >= nb) a.y = b.y = 0.0f;
+            if (m + 2 >= nb) a.z = b.z = 0.0f;
+            if (m + 3 >= nb) a.w = b.w = 0.0f;
+            sm.pi[m + 0][r] = a.x;
+            sm.pi[m + 1][r] = a.y;
+            sm.pi[m + 2][r] = a.z;
+            sm.pi[m + 3][r] = a.w;
             if (!diag) {
-                const float xb = sm.pj[m + hi][rb * 32 + lo];
-                pb[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[t], 0, 0, 0);
+                sm.pj[m + 0][r] = b.x;
+                sm.pj[m + 1][r] = b.y;
+                sm.pj[m + 2][r] = b.z;
+                sm.pj[m + 3][r] = b.w;
             }
         }
     }
-    __syncthreads();  // every wave is done reading the panels
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int t = 0; t < QB; ++t) {
-        const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int c = cb * 32 + mfma32_row(q, lane);
-            sm.pi[c][rb * 32 + lo] = pa[t][q];
-            if (!diag) sm.pj[c][rb * 32 + lo] = pb[t][q];
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + q * kFThreads;
+            const int c = e / NB, m = e % NB;
+            sm.vb[m][c] = vv[q];
         }
     }
     __syncthreads();
-    float(*pjs)[FLD] = diag ? sm.pi : sm.pj;
 
-    if (diag) {  // this row block's P goes into the factor
-        for (int e = tid; e < FT * NB; e += kFThreads) {
-            const int r = e / NB, c = e % NB;
-            if (r0 + r < k0 && c < nb) Tf[(r0 + r) * lda + k0 + c] = sm.pi[c][r];
+    if constexpr (!PRE) {
+        // P^T[c][r] = sum_m V[c][m] panel[r][m]: 2 x FT/32 output blocks of 32x32,
+        // FT/64 per wave; block b = wave * QB + t covers c-block b % 2, r-block b / 2.
+        floatx16 pa[QB], pb[QB];
+#pragma unroll
+        for (int t = 0; t < QB; ++t)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) pa[t][q] = pb[t][q] = 0.0f;
+#pragma unroll 8
+        for (int m = 0; m < NB; m += 2) {
+#pragma unroll
+            for (int t = 0; t < QB; ++t) {
+                const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
+                const float v0 = sm.vb[m + hi][cb * 32 + lo];
+                const float xa = sm.pi[m + hi][rb * 32 + lo];
+                pa[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[t], 0, 0, 0);
+                if (!diag) {
+                    const float xb = sm.pj[m + hi][rb * 32 + lo];
+                    pb[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[t], 0, 0, 0);
+                }
+            }
         }
-    }
+        __syncthreads();  // every wave is done reading the panels
+#pragma unroll
+        for (int t = 0; t < QB; ++t) {
+            const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int c = cb * 32 + mfma32_row(q, lane);
+                sm.pi[c][rb * 32 + lo] = pa[t][q];
+                if (!diag) sm.pj[c][rb * 32 + lo] = pb[t][q];
+            }
+        }
+        __syncthreads();
+
+        if (diag) {  // this row block's P goes into the factor
+            for (int e = tid; e < FT * NB; e += kFThreads) {
+                const int r = e / NB, c = e % NB;
+                if (r0 + r < k0 && c < nb) Tf[(r0 + r) * lda + k0 + c] = sm.pi[c][r];
+            }
+        }
+    }  // !PRE
+    float(*pjs)[FLD] = diag ? sm.pi : sm.pj;
 
     // A[r][s] -= sum_c P_i[r][c] P_j[s][c], as D[s][r] = sum_c P_j^T[c][s] P_i^T[c][r].
     floatx16 acc[QB][QB];
@@ -440,6 +463,74 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
                         reinterpret_cast<float(*)[NB + 4]>(&sm.vb[0][0]));
 }
 
+// P = panel V^T for one 64-row block [r0, r0+64) of the leading rows [0, k0):
+// the block's rows of the factor, T[rows, k0:k0+nb] (the panel solve of the
+// step, done once per row block), and P^T [NB][k0] (row stride lda), which the
+// tiles of the step load as k-major operands.
+__global__ __launch_bounds__(kFThreads) void p_kernel(const float *__restrict__ A, float *__restrict__ Tf,
+                                                      float *__restrict__ Pt, const float *__restrict__ U, int64_t d,
+                                                      int64_t lda, int64_t k0, int nb) {
+    const int64_t r0 = (int64_t)blockIdx.x * NB;
+    __shared__ float pan[NB][NB + 4];  // pan[m][r] = A[r0 + r][k0 + m]
+    __shared__ float vb[NB][NB + 4];   // vb[m][c] = V[c][m]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hi = lane >> 5, lo = lane & 31;
+    constexpr int kPer = NB * NB / 4 / kFThreads;
+    float4 av[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e4 = tid + q * kFThreads;
+        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+        av[q] = (m < nb && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    constexpr int kVPer = NB * NB / kFThreads;
+    float vv[kVPer];
+#pragma unroll
+    for (int q = 0; q < kVPer; ++q) {
+        const int e = tid + q * kFThreads;
+        const int c = e / NB, m = e % NB;
+        vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e4 = tid + q * kFThreads;
+        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
+        float4 a = av[q];
+        if (m + 1 >= nb) a.y = 0.0f;
+        if (m + 2 >= nb) a.z = 0.0f;
+        if (m + 3 >= nb) a.w = 0.0f;
+        pan[m + 0][r] = a.x;
+        pan[m + 1][r] = a.y;
+        pan[m + 2][r] = a.z;
+        pan[m + 3][r] = a.w;
+    }
+#pragma unroll
+    for (int q = 0; q < kVPer; ++q) {
+        const int e = tid + q * kFThreads;
+        const int c = e / NB, m = e % NB;
+        vb[m][c] = vv[q];
+    }
+    __syncthreads();
+    // P^T[c][r] = sum_m V[c][m] panel[r][m]: wave w takes the 32x32 block
+    // (c-block w % 2, r-block w / 2).
+    const int cb = wave & 1, rb = wave >> 1;
+    floatx16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll 8
+    for (int m = 0; m < NB; m += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(vb[m + hi][cb * 32 + lo], pan[m + hi][rb * 32 + lo], acc, 0, 0, 0);
+    const int64_t r = r0 + rb * 32 + lo;
+    if (r >= k0) return;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int c = cb * 32 + mfma32_row(q, lane);
+        Pt[c * lda + r] = acc[q];  // P^T, k-major for the step's tiles (zero past nb)
+        if (c < nb) Tf[r * lda + k0 + c] = acc[q];
+    }
+}
+
 // Pairwise merge of inverted diagonal blocks at one level (block size sz):
 //   U12 = -U11 T12 U22   for pairs p_first .. p_first+npairs-1 of (ni x nj) blocks,
 // with T12 read from the factor Tf and the product U11 T12 staged in Tw.
@@ -484,6 +575,9 @@ hipError_t merge_level(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
 int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
 
 constexpr int kStepTile = 64;  // tile edge of the fused step
+// From this leading size on, P is formed once per row block (p_kernel) rather
+// than by every tile of its row and column.
+constexpr int64_t kPrecomputeP = 2048;
 
 }  // namespace
 
@@ -533,8 +627,17 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
         const int nt = (int)ceil_div(k0, kStepTile);
-        hipLaunchKernelGGL(step_kernel<kStepTile>, dim3((unsigned)((int64_t)nt * (nt + 1) / 2)), dim3(kFThreads), 0,
-                           s, A, Tf, U, d, lda, k0, nb, nt, info);
+        const dim3 grid((unsigned)((int64_t)nt * (nt + 1) / 2));
+        if (k0 >= kPrecomputeP) {
+            // many tiles: solve the panel once per row block, then update
+            hipLaunchKernelGGL(p_kernel, dim3((unsigned)kb), dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0, nb);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL((step_kernel<kStepTile, true>), grid, dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0,
+                               nb, nt, info);
+        } else {
+            hipLaunchKernelGGL((step_kernel<kStepTile, false>), grid, dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0,
+                               nb, nt, info);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // U = T^-1: pairwise merges of the inverted diagonal blocks.
