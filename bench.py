@@ -49,8 +49,8 @@ def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
     """The oracle as it stands, timed on a bounded sample of the same workload."""
     import oracle
     d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
-    n_s = min(n, 131072)
-    rows = min(d_out, 512)
+    n_s = min(n, 262144)
+    rows = min(d_out, 1024)
     t0 = time.perf_counter()
     H = oracle.hessian(lay["X"][:, :n_s])
     t_h = time.perf_counter() - t0
