@@ -16,26 +16,10 @@
 #pragma once
 
 #include "block_args.h"
+#include "quad.h"
 #include "quant_grid.h"
 
 namespace gptq {
-
-// Quad helpers (4 consecutive lanes own one row).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-// Value of lane `src_lane` of each quad (src_lane is a constant after unrolling).
-__device__ __forceinline__ float quad_bcast(float v, int src_lane) {
-    switch (src_lane) {
-    case 0: return dpp_f<0x00>(v);
-    case 1: return dpp_f<0x55>(v);
-    case 2: return dpp_f<0xAA>(v);
-    default: return dpp_f<0xFF>(v);
-    }
-}
-__device__ __forceinline__ float quad_xor1(float v) { return dpp_f<0xB1>(v); }  // quad_perm(1,0,3,2)
-__device__ __forceinline__ float quad_xor2(float v) { return dpp_f<0x4E>(v); }  // quad_perm(2,3,0,1)
 
 constexpr int kRowLanes = 4;  // lanes per output row
 

@@ -106,7 +106,11 @@ template <int EPI, int VA, int VB, int T>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     constexpr int QB = T / 64;  // 32x32 MFMA blocks per wave along each dimension
     constexpr int HW = T / 2;   // wave tile edge
-    const int tn = blockIdx.x, tm = blockIdx.y, bz = blockIdx.z;
+    // With B upper triangular the tiles of the last columns have the longest K:
+    // they are dispatched first (with A upper, the first rows are the longest,
+    // and they already come first).
+    const int tn = g.b_upper ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int tm = blockIdx.y, bz = blockIdx.z;
     if (g.upper_only && tm > tn) return;  // strictly below the diagonal: nothing to store
     const int64_t m0 = (int64_t)tm * T, n0 = (int64_t)tn * T;
 

@@ -7,15 +7,17 @@
 // of U.  Route (2/3 d^3 flops, fp32):
 //   1. H_d = P H P^T + lambda I           (gather + one-workgroup damping)
 //   2. UL-Cholesky H_d = T T^T, T upper   (blocked, from the bottom-right
-//      corner, blocks of 64: one wave factors the diagonal block and inverts
-//      its factor; one fused kernel then solves the block's panel and applies
-//      the rank-64 update to the leading block on matrix cores)
-//   3. U = T^-1                           (the off-diagonal blocks are merged
+//      corner, blocks of 64: one fused kernel per block solves the block's
+//      panel by back substitution, applies the rank-64 update to the leading
+//      block on matrix cores, and factors the next diagonal block on one wave)
+//   3. U = T^-1                           (the diagonal blocks are inverted
+//      all at once after the factorization; the off-diagonal blocks are merged
 //      pairwise by the block formula inv([[A, B], [0, C]]) =
 //      [[A^-1, -A^-1 B C^-1], [0, C^-1]], one batched matrix-core product
 //      pair per level.)
 // Indeed T T^T = H_d gives H_d^-1 = T^-T T^-1 = U^T U with U = T^-1 upper.
 #include "common.h"
+#include "quad.h"
 
 namespace gptq {
 namespace {
@@ -85,26 +87,31 @@ __global__ __launch_bounds__(kThreads) void iota_kernel(int32_t *__restrict__ p,
     if (i < n) p[i] = (int32_t)i;
 }
 
-// UL-Cholesky of one diagonal block and the inverse of its factor, on one
-// wave64 with no workgroup barriers (the other waves of the workgroup, if any,
-// have left).  On entry lane i holds row i of the block in c (upper part;
-// rows and columns past nb padded with the identity).
-//   factor:  for j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
-//            c_ii' -= t_ij t_i'j (i' < j)  -- column j is shared through LDS.
-//   inverse: lane c holds column c of V = T^-1.  For i = NB-1..0:
-//            V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
-//            reading row i of T from LDS with wave-uniform addresses.
-// Writes V into U's block at (kb, kb) (strictly lower part = 0); T's diagonal
-// blocks themselves are not needed later.  A non-positive pivot j sets
-// *info = kb + j + 1 (first one wins).
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ void factor_invert_block(float (&c)[NB], int lane, int nb, int64_t kb, float *__restrict__ U,
-                                                    int64_t d, int32_t *__restrict__ info, float *col,
-                                                    float (*tr)[NB + 4]) {
+// Rows past nb (and columns past nb) of a block row become the identity; the
+// strictly lower part is cleared.
+__device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const bool in = lane < nb && m < nb;
+        c[m] = in ? (m >= lane ? c[m] : 0.0f) : (m == lane ? 1.0f : 0.0f);
+    }
+}
+
+// UL-Cholesky of one diagonal block on one wave64 with no workgroup barriers
+// (the other waves of the workgroup, if any, have left).  On entry lane i holds
+// row i of the block in c (upper part, padded with the identity past nb).  For
+// j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
+// c_ii' -= t_ij t_i'j (i' < j) -- column j is shared through LDS (`col`).
+// On exit c holds row i of T (upper).  A non-positive pivot j sets
+// *info = kb + j + 1 (first one wins).  T goes into the factor's diagonal
+// block Tf[kb:kb+nb, kb:kb+nb] (upper part).
+__device__ __forceinline__ void factor_block(float (&c)[NB], int lane, int nb, int64_t kb, float *__restrict__ Tf,
+                                             int64_t lda, int32_t *__restrict__ info, float *col) {
     int32_t first_bad = 0;
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
@@ -131,15 +138,79 @@ __device__ __forceinline__ void factor_invert_block(float (&c)[NB], int lane, in
         __builtin_amdgcn_wave_barrier();
     }
     if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
-    // Rows of T (upper part) to LDS for the inverse.
+    if (lane < nb) {
+        float *dst = Tf + (kb + lane) * lda + kb;
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q) {
+            if (4 * q + 3 < lane) continue;  // wholly below the diagonal
+            float4 v;
+            v.x = (4 * q + 0 >= lane) ? c[4 * q + 0] : 0.0f;
+            v.y = (4 * q + 1 >= lane) ? c[4 * q + 1] : 0.0f;
+            v.z = (4 * q + 2 >= lane) ? c[4 * q + 2] : 0.0f;
+            v.w = (4 * q + 3 >= lane) ? c[4 * q + 3] : 0.0f;
+            if (4 * q + 3 < nb) {
+                *reinterpret_cast<float4 *>(dst + 4 * q) = v;
+            } else {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q + e < nb) dst[4 * q + e] = vv[e];
+            }
+        }
+    }
+}
+
+// The first (bottom-right) diagonal block A[k0:k0+nb, k0:k0+nb], read from the
+// working matrix and factored by one wave.
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void panel_kernel(const float *__restrict__ A, float *__restrict__ Tf, int64_t lda, int64_t k0, int nb,
+                  int32_t *__restrict__ info) {
+    __shared__ __attribute__((aligned(16))) float col[NB];
+    const int lane = threadIdx.x;
+    // Row `lane` of the block straight into registers (16-byte loads, all in flight at once).
+    float c[NB];
+    const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
-        float4 v;
-        v.x = (4 * q + 0 >= lane) ? c[4 * q + 0] : 0.0f;
-        v.y = (4 * q + 1 >= lane) ? c[4 * q + 1] : 0.0f;
-        v.z = (4 * q + 2 >= lane) ? c[4 * q + 2] : 0.0f;
-        v.w = (4 * q + 3 >= lane) ? c[4 * q + 3] : 0.0f;
-        *reinterpret_cast<float4 *>(&tr[lane][4 * q]) = v;
+        // chunks past nb are not read (lda is a multiple of 4, so a chunk
+        // that starts below nb ends inside the row)
+        const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        c[4 * q + 0] = v.x;
+        c[4 * q + 1] = v.y;
+        c[4 * q + 2] = v.z;
+        c[4 * q + 3] = v.w;
+    }
+    mask_block_row(c, lane, nb);
+    factor_block(c, lane, nb, k0, Tf, lda, info, col);
+}
+
+// V = T_bb^-1 of every diagonal block b (one wave each, all blocks at once,
+// after the factorization): lane c holds column c of V.  For i = NB-1..0:
+//   V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
+// reading row i of T from LDS with wave-uniform addresses.  V goes into U's
+// diagonal block (zero below the diagonal).
+__global__ __launch_bounds__(kWave) void invert_blocks_kernel(const float *__restrict__ Tf, float *__restrict__ U,
+                                                              int64_t d, int64_t lda) {
+    __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
+    const int64_t kb = (int64_t)blockIdx.x * NB;
+    const int nb = (int)(d - kb < NB ? d - kb : NB);
+    const int lane = threadIdx.x;
+    {
+        float c[NB];
+        const float *src = Tf + (kb + (lane < nb ? lane : 0)) * lda + kb;
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q) {
+            const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            c[4 * q + 0] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
+        mask_block_row(c, lane, nb);
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q)
+            *reinterpret_cast<float4 *>(&tr[lane][4 * q]) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
     }
     wave_sync_lds();
     float v[NB];
@@ -163,8 +234,8 @@ __device__ __forceinline__ void factor_invert_block(float (&c)[NB], int lane, in
         x = lane == i ? rii : x;
         v[i] = lane < i ? 0.0f : x;
     }
-    // Column `lane` of V into U's block (zero below the diagonal): each store
-    // instruction writes one row, lanes along the columns.
+    // Column `lane` of V into U's block: each store instruction writes one row,
+    // lanes along the columns.
     if (lane < nb) {
         float *dst = U + kb * d + kb + lane;
 #pragma unroll
@@ -173,61 +244,103 @@ __device__ __forceinline__ void factor_invert_block(float (&c)[NB], int lane, in
     }
 }
 
-// Rows past nb (and columns past nb) of a block row become the identity; the
-// strictly lower part is cleared.
-__device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb) {
+// The panel solve of one step, P = panel T_kk^-T (so that P P^T is the
+// update), row by row on four lanes per row: lane q of a quad holds columns
+// q + 4t (t = 0..15) of its row.  Back substitution over the columns c =
+// NB-1..0: p_c = a_c / t_cc, then a_c' -= t_c'c p_c for c' < c.
+//   tq[c][p][q][i] = T_kk[q + 16p + 4i][c] strictly above the diagonal (zero
+//   on and below it), rinv[c] = 1 / t_cc; columns past nb are the identity.
+struct TkkSmem {
+    float tq[NB][NB / 16][4][4];
+    float rinv[NB];
+};
+
+// All kFThreads threads: T_kk (upper, Tf's diagonal block at k0) into the
+// layout above.  Global reads are row-wise (coalesced).
+constexpr int kFThreads = 256;
+__device__ __forceinline__ void load_tkk(TkkSmem &s, const float *__restrict__ Tf, int64_t lda, int64_t k0, int nb,
+                                         int tid) {
+    constexpr int kPer = NB * NB / kFThreads;
+    float tv[kPer];
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {
-        const bool in = lane < nb && m < nb;
-        c[m] = in ? (m >= lane ? c[m] : 0.0f) : (m == lane ? 1.0f : 0.0f);
+    for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kFThreads;
+        const int r = e / NB, c = e % NB;  // T[r][c]
+        tv[u] = (r <= c && c < nb) ? Tf[(k0 + r) * lda + k0 + c] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kFThreads;
+        const int r = e / NB, c = e % NB;
+        s.tq[c][r / 16][r % 4][(r / 4) % 4] = r < c ? tv[u] : 0.0f;
+        if (r == c) s.rinv[c] = c < nb ? 1.0f / tv[u] : 1.0f;
     }
 }
 
-// The first (bottom-right) diagonal block A[k0:k0+nb, k0:k0+nb], read from the
-// working matrix.  The wave is alone on its CU, so it may take every register;
-// that lets the scheduler keep a whole column of LDS reads in flight.
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void panel_kernel(const float *__restrict__ A, float *__restrict__ U, int64_t d, int64_t lda, int64_t k0, int nb,
-                  int32_t *__restrict__ info) {
-    __shared__ __attribute__((aligned(16))) float col[NB];
-    __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
-    const int lane = threadIdx.x;
-    // Row `lane` of the block straight into registers (16-byte loads, all in flight at once).
-    float c[NB];
-    const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
+// One row (TWO: two rows, a and b, sharing each step's reads of T_kk).
+template <bool TWO>
+__device__ __forceinline__ void trsm_rows(float (&a)[NB / 4], float (&b)[NB / 4], int q, const TkkSmem &s) {
 #pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-        // chunks past nb are not read (lda is a multiple of 4, so a chunk
-        // that starts below nb ends inside the row)
-        const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-        c[4 * q + 0] = v.x;
-        c[4 * q + 1] = v.y;
-        c[4 * q + 2] = v.z;
-        c[4 * q + 3] = v.w;
+    for (int c = NB - 1; c >= 0; --c) {
+        const int qo = c & 3, to = c >> 2;
+        const float rc = s.rinv[c];
+        const float pa = quad_bcast(a[to], qo) * rc;
+        a[to] = q == qo ? pa : a[to];
+        float pb = 0.0f;
+        if constexpr (TWO) {
+            pb = quad_bcast(b[to], qo) * rc;
+            b[to] = q == qo ? pb : b[to];
+        }
+        // columns q + 4t < c lie in t <= to; the rest of tq's column is zero
+#pragma unroll
+        for (int p = 0; p <= to / 4; ++p) {
+            const float4 u = *reinterpret_cast<const float4 *>(&s.tq[c][p][q][0]);
+            const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * p + i <= to) {
+                    a[4 * p + i] = fmaf(-uu[i], pa, a[4 * p + i]);
+                    if constexpr (TWO) b[4 * p + i] = fmaf(-uu[i], pb, b[4 * p + i]);
+                }
+        }
+        // keep each step's LDS reads next to their use
+        __builtin_amdgcn_sched_barrier(0);
     }
-    mask_block_row(c, lane, nb);
-    factor_invert_block(c, lane, nb, k0, U, d, info, col, tr);
+}
+
+// Row r0 + (tid / 4) of the panel A[:, k0:k0+nb], lane q's columns (zero past nb
+// and past the leading rows k0).
+__device__ __forceinline__ void load_panel_row(float (&a)[NB / 4], const float *__restrict__ A, int64_t lda, int64_t k0,
+                                               int nb, int64_t row, int q) {
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t) {
+        const int c = q + 4 * t;
+        a[t] = (row < k0 && c < nb) ? A[row * lda + k0 + c] : 0.0f;
+    }
 }
 
 // One step of the blocked factorization, fused.  Block k0 (columns k0..k0+nb)
-// has been factored and V = T_kk^-1 sits in U's block.  Each workgroup takes
-// one FT x FT upper tile (i, j) of the leading matrix A[0:k0, 0:k0]:
-//   P_i = A[rows i, k0:k0+nb] V^T        (so P = panel T_kk^-T)
-//   A[i, j] -= P_i P_j^T                  (upper part)
+// has been factored: T_kk sits in Tf's diagonal block.  Each workgroup takes
+// one 64 x 64 upper tile (i, j) of the leading matrix A[0:k0, 0:k0]:
+//   P_i = A[rows i, k0:k0+nb] T_kk^-T    (back substitution, above)
+//   A[i, j] -= P_i P_j^T                  (upper part, fp32 matrix cores)
 // and a diagonal tile also writes P_i into the factor T (Tf[rows i, k0:k0+nb]).
 // The workgroup of the last diagonal tile, which holds the next block
-// A[k0-NB:k0, k0-NB:k0] at its bottom-right corner, then factors and inverts
-// that block from its updated values: the next step's V is ready when the
-// kernel ends, with no launch and no HBM round trip in between.
-// Products run on fp32 matrix cores in transposed form, D[col][row], so each
+// A[k0-NB:k0, k0-NB:k0], is dispatched first; after its update it factors
+// that block from its updated values, so the next step's T_kk exists when the
+// kernel ends, with no launch and no HBM round trip in between.  The inverses
+// of the diagonal blocks are not on this chain (invert_blocks_kernel).
+// PRE: P was formed once per row block by p_kernel; the tiles load P_i^T and
+// P_j^T from its k-major copy Pt instead.
+// The update runs on fp32 matrix cores in transposed form, D[col][row], so each
 // lane's accumulators hold four consecutive columns of one row of A.
-constexpr int kFThreads = 256;
+constexpr int FT = 64;   // tile edge
+constexpr int FLD = FT + 4;
 
-template <int FT>
 struct StepSmem {
-    float pi[NB][FT + 4];  // panel rows i, k-major (later P_i^T)
-    float pj[NB][FT + 4];  // panel rows j, k-major (later P_j^T; then the next block)
-    float vb[NB][NB + 4];  // vb[m][c] = V[c][m]  (later rows of T for the inverse)
+    float pi[NB][FLD];  // P_i^T (k-major)
+    float pj[NB][FLD];  // P_j^T (k-major); later the next block
+    TkkSmem tk;
 };
 
 __device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) {
@@ -241,15 +354,10 @@ __device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) 
     tj = i + (int)(t - before);
 }
 
-// PRE: P was computed for every row block by p_kernel; the tiles load P_i^T
-// and P_j^T from its k-major copy Tw instead of forming them.
-template <int FT, bool PRE>
+template <bool PRE>
 __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, float *__restrict__ Tf,
-                                                         const float *__restrict__ Tw, float *__restrict__ U, int64_t d,
-                                                         int64_t lda, int64_t k0, int nb, int nt,
-                                                         int32_t *__restrict__ info) {
-    constexpr int QB = FT / 64;  // 32-row MFMA blocks per wave quadrant edge
-    constexpr int FLD = FT + 4;
+                                                         const float *__restrict__ Pt, int64_t lda, int64_t k0, int nb,
+                                                         int nt, int32_t *__restrict__ info) {
     // Tiles in reverse order: workgroup 0 takes the last diagonal tile, whose
     // factorization of the next block is the step's longest chain.
     int ti, tj;
@@ -257,277 +365,140 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
     const bool diag = ti == tj;
     const bool last = diag && ti == nt - 1;
     const int64_t r0 = (int64_t)ti * FT, s0 = (int64_t)tj * FT;
-    __shared__ __attribute__((aligned(16))) StepSmem<FT> sm;
+    __shared__ __attribute__((aligned(16))) StepSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, lo = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
+    const int q = tid & 3, rr = tid >> 2;  // quad lane and row of the panel solve
 
-    // Every global load of a thread is issued before the first LDS store.
-    // (1) This tile's A values in the transposed accumulator layout: for each
-    //     32x32 block (si, ri) and g = 0..3, A[r][s .. s+3] with
-    //     r = r0 + wm*FT/2 + ri*32 + lo, s = s0 + wn*FT/2 + si*32 + 8g + 4*hi.
-    float4 cold[QB][QB][4];
+    // Every global load is issued before the first LDS store.
+    // (1) This tile's A values in the transposed accumulator layout: for
+    //     g = 0..3, A[r][s .. s+3] with r = r0 + wm*32 + lo, s = s0 + wn*32 + 8g + 4*hi.
+    float4 cold[4];
 #pragma unroll
-    for (int si = 0; si < QB; ++si)
-#pragma unroll
-        for (int ri = 0; ri < QB; ++ri)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t r = r0 + wm * (FT / 2) + ri * 32 + lo;
-                const int64_t sc = s0 + wn * (FT / 2) + si * 32 + 8 * g + 4 * hi;
-                cold[si][ri][g] = (r < k0 && sc < k0) ? *reinterpret_cast<const float4 *>(A + r * lda + sc)
-                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-    // (2) panel rows i and j -- columns past the block's nb are zero -- and V;
-    // with PRE, the k-major P^T columns of rows i and j instead.
+    for (int g = 0; g < 4; ++g) {
+        const int64_t r = r0 + wm * 32 + lo;
+        const int64_t sc = s0 + wn * 32 + 8 * g + 4 * hi;
+        cold[g] = (r < k0 && sc < k0) ? *reinterpret_cast<const float4 *>(A + r * lda + sc)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // (2) the rows of P (PRE: k-major P^T, float4 along the rows) or of the panel.
+    float ai[NB / 4], aj[NB / 4];
     constexpr int kPer = FT * NB / 4 / kFThreads;
-    float4 av[kPer], bv[kPer];
+    float4 pv[kPer], qv[kPer];
+    if constexpr (PRE) {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e4 = tid + q * kFThreads;
-        if constexpr (PRE) {
-            // Pt[c][r]: float4 along r; rows past k0 do not occur (k0 is a multiple of FT)
+        for (int u = 0; u < kPer; ++u) {
+            const int e4 = tid + u * kFThreads;
+            const int c = e4 / (FT / 4), r = (e4 % (FT / 4)) * 4;  // k0 is a multiple of FT: rows in range
+            pv[u] = *reinterpret_cast<const float4 *>(Pt + c * lda + r0 + r);
+            qv[u] = diag ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4 *>(Pt + c * lda + s0 + r);
+        }
+    } else {
+        load_panel_row(ai, A, lda, k0, nb, r0 + rr, q);
+        if (!diag) load_panel_row(aj, A, lda, k0, nb, s0 + rr, q);
+        load_tkk(sm.tk, Tf, lda, k0, nb, tid);
+    }
+    if constexpr (PRE) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e4 = tid + u * kFThreads;
             const int c = e4 / (FT / 4), r = (e4 % (FT / 4)) * 4;
-            av[q] = *reinterpret_cast<const float4 *>(Tw + c * lda + r0 + r);
-            bv[q] = diag ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4 *>(Tw + c * lda + s0 + r);
-        } else {
-            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-            // the row padding to lda keeps m..m+3 in bounds; lanes past nb are zeroed below
-            const bool in = m < nb;
-            av[q] = (in && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-            bv[q] = (in && !diag && s0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (s0 + r) * lda + k0 + m)
-                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    constexpr int kVPer = PRE ? 1 : NB * NB / kFThreads;
-    float vv[kVPer];
-    if constexpr (!PRE) {
-#pragma unroll
-        for (int q = 0; q < kVPer; ++q) {
-            const int e = tid + q * kFThreads;
-            const int c = e / NB, m = e % NB;
-            vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e4 = tid + q * kFThreads;
-        if constexpr (PRE) {
-            const int c = e4 / (FT / 4), r = (e4 % (FT / 4)) * 4;
-            *reinterpret_cast<float4 *>(&sm.pi[c][r]) = av[q];
-            if (!diag) *reinterpret_cast<float4 *>(&sm.pj[c][r]) = bv[q];
-        } else {
-            const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-            float4 a = av[q], b = bv[q];
-            if (m + 1 >= nb) a.y = b.y = 0.0f;
-            if (m + 2 >= nb) a.z = b.z = 0.0f;
-            if (m + 3 >= nb) a.w = b.w = 0.0f;
-            sm.pi[m + 0][r] = a.x;
-            sm.pi[m + 1][r] = a.y;
-            sm.pi[m + 2][r] = a.z;
-            sm.pi[m + 3][r] = a.w;
-            if (!diag) {
-                sm.pj[m + 0][r] = b.x;
-                sm.pj[m + 1][r] = b.y;
-                sm.pj[m + 2][r] = b.z;
-                sm.pj[m + 3][r] = b.w;
-            }
-        }
-    }
-    if constexpr (!PRE) {
-#pragma unroll
-        for (int q = 0; q < kVPer; ++q) {
-            const int e = tid + q * kFThreads;
-            const int c = e / NB, m = e % NB;
-            sm.vb[m][c] = vv[q];
-        }
-    }
-    __syncthreads();
-
-    if constexpr (!PRE) {
-        // P^T[c][r] = sum_m V[c][m] panel[r][m]: 2 x FT/32 output blocks of 32x32,
-        // FT/64 per wave; block b = wave * QB + t covers c-block b % 2, r-block b / 2.
-        floatx16 pa[QB], pb[QB];
-#pragma unroll
-        for (int t = 0; t < QB; ++t)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) pa[t][q] = pb[t][q] = 0.0f;
-#pragma unroll 8
-        for (int m = 0; m < NB; m += 2) {
-#pragma unroll
-            for (int t = 0; t < QB; ++t) {
-                const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
-                const float v0 = sm.vb[m + hi][cb * 32 + lo];
-                const float xa = sm.pi[m + hi][rb * 32 + lo];
-                pa[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xa, pa[t], 0, 0, 0);
-                if (!diag) {
-                    const float xb = sm.pj[m + hi][rb * 32 + lo];
-                    pb[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, xb, pb[t], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();  // every wave is done reading the panels
-#pragma unroll
-        for (int t = 0; t < QB; ++t) {
-            const int b = wave * QB + t, cb = b & 1, rb = b >> 1;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int c = cb * 32 + mfma32_row(q, lane);
-                sm.pi[c][rb * 32 + lo] = pa[t][q];
-                if (!diag) sm.pj[c][rb * 32 + lo] = pb[t][q];
-            }
+            *reinterpret_cast<float4 *>(&sm.pi[c][r]) = pv[u];
+            if (!diag) *reinterpret_cast<float4 *>(&sm.pj[c][r]) = qv[u];
         }
         __syncthreads();
-
-        if (diag) {  // this row block's P goes into the factor
-            for (int e = tid; e < FT * NB; e += kFThreads) {
-                const int r = e / NB, c = e % NB;
-                if (r0 + r < k0 && c < nb) Tf[(r0 + r) * lda + k0 + c] = sm.pi[c][r];
-            }
+    } else {
+        __syncthreads();  // T_kk in LDS
+        if (diag)
+            trsm_rows<false>(ai, aj, q, sm.tk);
+        else
+            trsm_rows<true>(ai, aj, q, sm.tk);
+#pragma unroll
+        for (int t = 0; t < NB / 4; ++t) {
+            sm.pi[q + 4 * t][rr] = ai[t];
+            if (!diag) sm.pj[q + 4 * t][rr] = aj[t];
         }
-    }  // !PRE
+        if (diag && r0 + rr < k0) {  // this row block's P goes into the factor
+#pragma unroll
+            for (int t = 0; t < NB / 4; ++t)
+                if (q + 4 * t < nb) Tf[(r0 + rr) * lda + k0 + q + 4 * t] = ai[t];
+        }
+        __syncthreads();
+    }
     float(*pjs)[FLD] = diag ? sm.pi : sm.pj;
 
     // A[r][s] -= sum_c P_i[r][c] P_j[s][c], as D[s][r] = sum_c P_j^T[c][s] P_i^T[c][r].
-    floatx16 acc[QB][QB];
+    floatx16 acc;
 #pragma unroll
-    for (int i = 0; i < QB; ++i)
-#pragma unroll
-        for (int j = 0; j < QB; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll 8
-    for (int c = 0; c < NB; c += 2) {
-        float y[QB], x[QB];
-#pragma unroll
-        for (int t = 0; t < QB; ++t) {
-            y[t] = pjs[c + hi][wn * (FT / 2) + t * 32 + lo];
-            x[t] = sm.pi[c + hi][wm * (FT / 2) + t * 32 + lo];
-        }
-#pragma unroll
-        for (int si = 0; si < QB; ++si)
-#pragma unroll
-            for (int ri = 0; ri < QB; ++ri)
-                acc[si][ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[si], x[ri], acc[si][ri], 0, 0, 0);
-    }
+    for (int c = 0; c < NB; c += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pjs[c + hi][wn * 32 + lo], sm.pi[c + hi][wm * 32 + lo], acc, 0, 0, 0);
     if (last) __syncthreads();  // pj is about to hold the next block: every wave is done reading it
-    // The next block's first row/column in tile coordinates (it is the
-    // tile's bottom-right NB x NB corner).
-    const int64_t nb0 = k0 - NB;
+    const int64_t nb0 = k0 - NB;  // the next block's first row/column
     float(*blk)[NB + 4] = reinterpret_cast<float(*)[NB + 4]>(&sm.pj[0][0]);
 #pragma unroll
-    for (int si = 0; si < QB; ++si)
-#pragma unroll
-        for (int ri = 0; ri < QB; ++ri)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t r = r0 + wm * (FT / 2) + ri * 32 + lo;
-                const int64_t sc = s0 + wn * (FT / 2) + si * 32 + 8 * g + 4 * hi;
-                if (r >= k0 || sc >= k0) continue;
-                float4 v = cold[si][ri][g];
-                v.x -= acc[si][ri][4 * g + 0];
-                v.y -= acc[si][ri][4 * g + 1];
-                v.z -= acc[si][ri][4 * g + 2];
-                v.w -= acc[si][ri][4 * g + 3];
-                if (last && r >= nb0 && sc >= nb0) {
-                    // the next block: kept in LDS for this workgroup's factorization
-                    *reinterpret_cast<float4 *>(&blk[r - nb0][sc - nb0]) = v;
-                    continue;
-                }
-                float *dst = A + r * lda + sc;
-                if (!diag || r <= sc) {
-                    *reinterpret_cast<float4 *>(dst) = v;
-                } else {  // diagonal tile: keep only r <= s
-                    if (r <= sc + 0) dst[0] = v.x;
-                    if (r <= sc + 1) dst[1] = v.y;
-                    if (r <= sc + 2) dst[2] = v.z;
-                    if (r <= sc + 3) dst[3] = v.w;
-                }
-            }
+    for (int g = 0; g < 4; ++g) {
+        const int64_t r = r0 + wm * 32 + lo;
+        const int64_t sc = s0 + wn * 32 + 8 * g + 4 * hi;
+        if (r >= k0 || sc >= k0) continue;
+        float4 v = cold[g];
+        v.x -= acc[4 * g + 0];
+        v.y -= acc[4 * g + 1];
+        v.z -= acc[4 * g + 2];
+        v.w -= acc[4 * g + 3];
+        if (last && r >= nb0 && sc >= nb0) {
+            // the next block: kept in LDS for this workgroup's factorization
+            *reinterpret_cast<float4 *>(&blk[r - nb0][sc - nb0]) = v;
+            continue;
+        }
+        float *dst = A + r * lda + sc;
+        if (!diag || r <= sc) {
+            *reinterpret_cast<float4 *>(dst) = v;
+        } else {  // diagonal tile: keep only r <= s
+            if (r <= sc + 0) dst[0] = v.x;
+            if (r <= sc + 1) dst[1] = v.y;
+            if (r <= sc + 2) dst[2] = v.z;
+            if (r <= sc + 3) dst[3] = v.w;
+        }
+    }
     if (!last) return;
     __syncthreads();  // the next block is complete in LDS
     if (wave != 0) return;
     float c[NB];
 #pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(&blk[lane][4 * q]);
-        c[4 * q + 0] = v.x;
-        c[4 * q + 1] = v.y;
-        c[4 * q + 2] = v.z;
-        c[4 * q + 3] = v.w;
+    for (int e = 0; e < NB / 4; ++e) {
+        const float4 v = *reinterpret_cast<const float4 *>(&blk[lane][4 * e]);
+        c[4 * e + 0] = v.x;
+        c[4 * e + 1] = v.y;
+        c[4 * e + 2] = v.z;
+        c[4 * e + 3] = v.w;
     }
     mask_block_row(c, lane, NB);
-    // scratch for the factorization: V's LDS copy and the first panel row are dead
-    factor_invert_block(c, lane, NB, nb0, U, d, info, &sm.pi[0][0],
-                        reinterpret_cast<float(*)[NB + 4]>(&sm.vb[0][0]));
+    factor_block(c, lane, NB, nb0, Tf, lda, info, &sm.pi[0][0]);  // P_i^T is dead: its first row is scratch
 }
 
-// P = panel V^T for one 64-row block [r0, r0+64) of the leading rows [0, k0):
-// the block's rows of the factor, T[rows, k0:k0+nb] (the panel solve of the
-// step, done once per row block), and P^T [NB][k0] (row stride lda), which the
-// tiles of the step load as k-major operands.
+// P = panel T_kk^-T for one 64-row block [r0, r0+64) of the leading rows
+// [0, k0): the block's rows of the factor, T[rows, k0:k0+nb] (the step's panel
+// solve, done once per row block), and P^T [NB][k0] (row stride lda), which
+// the tiles of the step load as k-major operands.
 __global__ __launch_bounds__(kFThreads) void p_kernel(const float *__restrict__ A, float *__restrict__ Tf,
-                                                      float *__restrict__ Pt, const float *__restrict__ U, int64_t d,
-                                                      int64_t lda, int64_t k0, int nb) {
+                                                      float *__restrict__ Pt, int64_t lda, int64_t k0, int nb) {
+    __shared__ __attribute__((aligned(16))) TkkSmem tk;
     const int64_t r0 = (int64_t)blockIdx.x * NB;
-    __shared__ float pan[NB][NB + 4];  // pan[m][r] = A[r0 + r][k0 + m]
-    __shared__ float vb[NB][NB + 4];   // vb[m][c] = V[c][m]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hi = lane >> 5, lo = lane & 31;
-    constexpr int kPer = NB * NB / 4 / kFThreads;
-    float4 av[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e4 = tid + q * kFThreads;
-        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-        av[q] = (m < nb && r0 + r < k0) ? *reinterpret_cast<const float4 *>(A + (r0 + r) * lda + k0 + m)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    constexpr int kVPer = NB * NB / kFThreads;
-    float vv[kVPer];
-#pragma unroll
-    for (int q = 0; q < kVPer; ++q) {
-        const int e = tid + q * kFThreads;
-        const int c = e / NB, m = e % NB;
-        vv[q] = (c < nb && m < nb) ? U[(k0 + c) * d + k0 + m] : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e4 = tid + q * kFThreads;
-        const int r = e4 / (NB / 4), m = (e4 % (NB / 4)) * 4;
-        float4 a = av[q];
-        if (m + 1 >= nb) a.y = 0.0f;
-        if (m + 2 >= nb) a.z = 0.0f;
-        if (m + 3 >= nb) a.w = 0.0f;
-        pan[m + 0][r] = a.x;
-        pan[m + 1][r] = a.y;
-        pan[m + 2][r] = a.z;
-        pan[m + 3][r] = a.w;
-    }
-#pragma unroll
-    for (int q = 0; q < kVPer; ++q) {
-        const int e = tid + q * kFThreads;
-        const int c = e / NB, m = e % NB;
-        vb[m][c] = vv[q];
-    }
+    const int tid = threadIdx.x, q = tid & 3, rr = tid >> 2;
+    float a[NB / 4];
+    load_panel_row(a, A, lda, k0, nb, r0 + rr, q);
+    load_tkk(tk, Tf, lda, k0, nb, tid);
     __syncthreads();
-    // P^T[c][r] = sum_m V[c][m] panel[r][m]: wave w takes the 32x32 block
-    // (c-block w % 2, r-block w / 2).
-    const int cb = wave & 1, rb = wave >> 1;
-    floatx16 acc;
+    trsm_rows<false>(a, a, q, tk);
+    const int64_t r = r0 + rr;  // < k0: k0 is a multiple of NB
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-#pragma unroll 8
-    for (int m = 0; m < NB; m += 2)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(vb[m + hi][cb * 32 + lo], pan[m + hi][rb * 32 + lo], acc, 0, 0, 0);
-    const int64_t r = r0 + rb * 32 + lo;
-    if (r >= k0) return;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int c = cb * 32 + mfma32_row(q, lane);
-        Pt[c * lda + r] = acc[q];  // P^T, k-major for the step's tiles (zero past nb)
-        if (c < nb) Tf[r * lda + k0 + c] = acc[q];
+    for (int t = 0; t < NB / 4; ++t) {
+        const int c = q + 4 * t;
+        Pt[c * lda + r] = a[t];  // zero past nb
+        if (c < nb) Tf[r * lda + k0 + c] = a[t];
     }
 }
 
@@ -574,7 +545,6 @@ hipError_t merge_level(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
 
 int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
 
-constexpr int kStepTile = 64;  // tile edge of the fused step
 // From this leading size on, P is formed once per row block (p_kernel) rather
 // than by every tile of its row and column.
 constexpr int64_t kPrecomputeP = 2048;
@@ -612,34 +582,33 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                        U, nU, 0.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // UL-Cholesky from the bottom-right corner: factor (and invert) the last
-    // diagonal block, then one fused step per block: solve its panel, update
-    // the leading block and factor the next diagonal block.  64-wide tiles
-    // keep each workgroup's matrix-core chains short (measured faster than
-    // 128-wide tiles for leading blocks up to 8192).
+    // UL-Cholesky from the bottom-right corner: factor the last diagonal block,
+    // then one fused step per block: solve its panel, update the leading
+    // block and factor the next diagonal block.  For large leading blocks the
+    // panel solve runs first, once per row block (p_kernel).
     const int64_t nblk = ceil_div(d, NB);
     {
         const int64_t k0 = (nblk - 1) * NB;
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, U, d, lda, k0, (int)(d - k0), info);
+        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, Tf, lda, k0, (int)(d - k0), info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     for (int64_t kb = nblk - 1; kb >= 1; --kb) {
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
-        const int nt = (int)ceil_div(k0, kStepTile);
+        const int nt = (int)ceil_div(k0, FT);
         const dim3 grid((unsigned)((int64_t)nt * (nt + 1) / 2));
         if (k0 >= kPrecomputeP) {
-            // many tiles: solve the panel once per row block, then update
-            hipLaunchKernelGGL(p_kernel, dim3((unsigned)kb), dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0, nb);
+            hipLaunchKernelGGL(p_kernel, dim3((unsigned)kb), dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL((step_kernel<kStepTile, true>), grid, dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0,
-                               nb, nt, info);
+            hipLaunchKernelGGL(step_kernel<true>, grid, dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb, nt, info);
         } else {
-            hipLaunchKernelGGL((step_kernel<kStepTile, false>), grid, dim3(kFThreads), 0, s, A, Tf, Tw, U, d, lda, k0,
-                               nb, nt, info);
+            hipLaunchKernelGGL(step_kernel<false>, grid, dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb, nt, info);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    // The inverses of the diagonal blocks of T: U's diagonal blocks.
+    hipLaunchKernelGGL(invert_blocks_kernel, dim3((unsigned)nblk), dim3(kWave), 0, s, Tf, U, d, lda);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     // U = T^-1: pairwise merges of the inverted diagonal blocks.
     for (int64_t sz = NB; sz < d; sz *= 2) {
         const int64_t npairs_total = ceil_div(d, 2 * sz);
