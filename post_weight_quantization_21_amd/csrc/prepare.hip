@@ -106,36 +106,57 @@ __device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb)
 // (the other waves of the workgroup, if any, have left).  On entry lane i holds
 // row i of the block in c (upper part, padded with the identity past nb).  For
 // j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
-// c_ii' -= t_ij t_i'j (i' < j) -- column j is shared through LDS (`col`).
+// c_ii' -= t_ij t_i'j (i' < j).  The pivot is the step's only serial
+// dependence.  So step j updates the next kEager columns at once, from column
+// j's entries read out of their lanes (readlane), and writes column j to LDS
+// and reads it back for the remaining columns; those updates run one step
+// later, after the next pivot, so neither the LDS latency nor their issue
+// time sits on the chain of pivots.  (LDS operations of one wave complete in
+// issue order, so the reads see the write without a wait.)
 // On exit c holds row i of T (upper).  A non-positive pivot j sets
 // *info = kb + j + 1 (first one wins).  T goes into the factor's diagonal
 // block Tf[kb:kb+nb, kb:kb+nb] (upper part).
+constexpr int kEager = 4;
 __device__ __forceinline__ void factor_block(float (&c)[NB], int lane, int nb, int64_t kb, float *__restrict__ Tf,
                                              int64_t lda, int32_t *__restrict__ info, float *col) {
     int32_t first_bad = 0;
+    float tp = 0.0f;        // column j+1 of T (this lane's entry), for the deferred updates
+    float4 cv[NB / 4];      // column j+1 of T from LDS
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
         const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));  // pivot, from lane j
         const bool bad = !(p0 > 0.0f);
         first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(kb + j + 1) : first_bad;
-        // hardware sqrt / reciprocal (about 1 ulp): the factor only has to be
-        // accurate; branch-free selects keep the wave on one path.
-        const float tjj = __builtin_amdgcn_sqrtf(bad ? 1.0f : p0);
-        const float inv = __builtin_amdgcn_rcpf(tjj);
-        float t = c[j] * inv;
-        t = lane == j ? tjj : t;
+        // hardware reciprocal square root / square root (about 1 ulp): the
+        // factor only has to be accurate; branch-free selects keep the wave on
+        // one path.
+        const float pv = bad ? 1.0f : p0;
+        float t = c[j] * __builtin_amdgcn_rsqf(pv);
+        t = lane == j ? __builtin_amdgcn_sqrtf(pv) : t;
         t = lane > j ? 0.0f : t;
         c[j] = t;
-        if (j == 0) break;
-        col[lane] = t;  // column j of the factor, shared through LDS
-        wave_sync_lds();
-        float4 cv[NB / 4];
 #pragma unroll
-        for (int q = 0; q < (j + 3) / 4; ++q) cv[q] = *reinterpret_cast<const float4 *>(&col[4 * q]);
-        // c[j-1] first: it is the next step's pivot.
+        for (int m = 1; m <= kEager; ++m) {
+            if (j - m < 0) break;
+            const float tm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), j - m));
+            c[j - m] = fmaf(-t, tm, c[j - m]);
+        }
+        // step j+1's remaining columns 0 .. j-kEager, in the order of their LDS reads
 #pragma unroll
-        for (int i2 = j - 1; i2 >= 0; --i2) c[i2] = fmaf(-t, cv[i2 / 4][i2 % 4], c[i2]);
-        __builtin_amdgcn_wave_barrier();
+        for (int i2 = 0; i2 <= j - kEager; ++i2) {
+            if (j == NB - 1) break;
+            c[i2] = fmaf(-tp, cv[i2 / 4][i2 % 4], c[i2]);
+        }
+        const int nbulk = j - kEager;  // step j's remaining columns 0 .. nbulk-1
+        if (nbulk > 0) {
+            col[lane] = t;
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < (nbulk + 3) / 4; ++q) cv[q] = *reinterpret_cast<const float4 *>(&col[4 * q]);
+            __builtin_amdgcn_wave_barrier();
+        }
+        tp = t;
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
     if (lane < nb) {
@@ -247,64 +268,80 @@ __global__ __launch_bounds__(kWave) void invert_blocks_kernel(const float *__res
 // The panel solve of one step, P = panel T_kk^-T (so that P P^T is the
 // update), row by row on four lanes per row: lane q of a quad holds columns
 // q + 4t (t = 0..15) of its row.  Back substitution over the columns c =
-// NB-1..0: p_c = a_c / t_cc, then a_c' -= t_c'c p_c for c' < c.
-//   tq[c][p][q][i] = T_kk[q + 16p + 4i][c] strictly above the diagonal (zero
-//   on and below it), rinv[c] = 1 / t_cc; columns past nb are the identity.
+// NB-1..0 on the unscaled values: with n_c'c = -t_c'c / t_cc,
+//   a_c' += n_c'c a_c  (c' < c),  and at the end p_c = a_c / t_cc,
+// which is p_c = (a_c - sum_{m>c} t_cm p_m) / t_cc.  Each update is one FMA
+// whose a_c comes straight from its quad lane (DPP); the next column's operands
+// are read from LDS one step ahead.
+//   nq[c][p][q][i] = n_c'c for c' = q + 16p + 4i < c (zero on and below the
+//   diagonal), rq[q][t] = 1 / t_cc for c = q + 4t; columns past nb are the
+//   identity.
 struct TkkSmem {
-    float tq[NB][NB / 16][4][4];
-    float rinv[NB];
+    float nq[NB][NB / 16][4][4];
+    float rq[4][NB / 4];
 };
 
 // All kFThreads threads: T_kk (upper, Tf's diagonal block at k0) into the
-// layout above.  Global reads are row-wise (coalesced).
+// layout above; thread tid takes column tid % NB.  Global reads are row-wise
+// (coalesced).
 constexpr int kFThreads = 256;
 __device__ __forceinline__ void load_tkk(TkkSmem &s, const float *__restrict__ Tf, int64_t lda, int64_t k0, int nb,
                                          int tid) {
     constexpr int kPer = NB * NB / kFThreads;
+    const int c = tid % NB, rb = tid / NB;  // rows rb + 4u
     float tv[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-        const int e = tid + u * kFThreads;
-        const int r = e / NB, c = e % NB;  // T[r][c]
-        tv[u] = (r <= c && c < nb) ? Tf[(k0 + r) * lda + k0 + c] : 0.0f;
+        const int r = rb + 4 * u;
+        tv[u] = (r < c && c < nb) ? Tf[(k0 + r) * lda + k0 + c] : 0.0f;
     }
+    const float rc = c < nb ? 1.0f / Tf[(k0 + c) * lda + k0 + c] : 1.0f;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-        const int e = tid + u * kFThreads;
-        const int r = e / NB, c = e % NB;
-        s.tq[c][r / 16][r % 4][(r / 4) % 4] = r < c ? tv[u] : 0.0f;
-        if (r == c) s.rinv[c] = c < nb ? 1.0f / tv[u] : 1.0f;
+        const int r = rb + 4 * u;
+        s.nq[c][r / 16][r % 4][(r / 4) % 4] = r < c ? -tv[u] * rc : 0.0f;
     }
+    if (rb == 0) s.rq[c % 4][c / 4] = rc;
 }
 
 // One row (TWO: two rows, a and b, sharing each step's reads of T_kk).
 template <bool TWO>
 __device__ __forceinline__ void trsm_rows(float (&a)[NB / 4], float (&b)[NB / 4], int q, const TkkSmem &s) {
+    float4 nu[2][NB / 16];
+    auto load_col = [&](int c, float4(&dst)[NB / 16]) {
+#pragma unroll
+        for (int p = 0; p <= (c >> 2) / 4; ++p) dst[p] = *reinterpret_cast<const float4 *>(&s.nq[c][p][q][0]);
+    };
+    load_col(NB - 1, nu[(NB - 1) & 1]);
 #pragma unroll
     for (int c = NB - 1; c >= 0; --c) {
-        const int qo = c & 3, to = c >> 2;
-        const float rc = s.rinv[c];
-        const float pa = quad_bcast(a[to], qo) * rc;
-        a[to] = q == qo ? pa : a[to];
-        float pb = 0.0f;
-        if constexpr (TWO) {
-            pb = quad_bcast(b[to], qo) * rc;
-            b[to] = q == qo ? pb : b[to];
-        }
-        // columns q + 4t < c lie in t <= to; the rest of tq's column is zero
+        const int qo = c & 3, to = c >> 2, cur = c & 1;
+        if (c > 0) load_col(c - 1, nu[cur ^ 1]);
+        const float pa = quad_bcast(a[to], qo);
+        const float pb = TWO ? quad_bcast(b[to], qo) : 0.0f;
+        auto upd = [&](int t) {
+            const float4 u4 = nu[cur][t / 4];
+            const float u = (t % 4 == 0) ? u4.x : (t % 4 == 1) ? u4.y : (t % 4 == 2) ? u4.z : u4.w;
+            a[t] = fmaf(pa, u, a[t]);
+            if constexpr (TWO) b[t] = fmaf(pb, u, b[t]);
+        };
+        // the next column's element first: it is the next step's pivot
+        const int tn = c > 0 ? (c - 1) >> 2 : 0;
+        upd(tn);
 #pragma unroll
-        for (int p = 0; p <= to / 4; ++p) {
-            const float4 u = *reinterpret_cast<const float4 *>(&s.tq[c][p][q][0]);
-            const float uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * p + i <= to) {
-                    a[4 * p + i] = fmaf(-uu[i], pa, a[4 * p + i]);
-                    if constexpr (TWO) b[4 * p + i] = fmaf(-uu[i], pb, b[4 * p + i]);
-                }
-        }
-        // keep each step's LDS reads next to their use
+        for (int t = 0; t <= to; ++t)
+            if (t != tn) upd(t);
         __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int p = 0; p < NB / 16; ++p) {
+        const float4 r4 = *reinterpret_cast<const float4 *>(&s.rq[q][4 * p]);
+        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[4 * p + i] *= rr[i];
+            if constexpr (TWO) b[4 * p + i] *= rr[i];
+        }
     }
 }
 

@@ -14,6 +14,17 @@
 // asymmetric: zoff = zero, [qlo, qhi] = [0, 2^b - 1], zadd = 0.
 // (x/s + 0 equals x/s, and a -0 that would become +0 is clamped and shifted to
 // the same code, so the symmetric case is exactly the printed rint(x/s).)
+//
+// x / s is the correctly rounded binary32 quotient, formed without a division
+// per element by Markstein's correction (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990): with r = RN(1/s) and q0 = RN(x r), the remainder
+// x - q0 s is exact and RN(q0 + (x - q0 s) r) = RN(x / s), provided nothing
+// over- or underflows.  That is arranged per group: s = s' 2^-k with s' in
+// [1, 2) (exact), x' = x 2^k (exact unless x / s is tiny or huge), and
+// x' / s' = x / s.  |x'| is clamped to 2^21: beyond it |x / s| > 2^20 and the
+// code saturates either way; if x' is tiny, so is x / s, and
+// rint(x / s + zoff) = zoff either way.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,7 +33,17 @@ namespace gptq {
 
 struct Grid {
     float s, zoff, qlo, qhi, zadd, zero;
+    float ss, rs;  // s' = s 2^k in [1, 2) and RN(1 / s')
+    int k;
 };
+
+__device__ __forceinline__ void grid_scale(Grid &g) {
+    int e;
+    const float m = frexpf(g.s, &e);  // s = m 2^e, m in [0.5, 1)
+    g.ss = 2.0f * m;
+    g.k = 1 - e;
+    g.rs = 1.0f / g.ss;  // IEEE division, once per group
+}
 
 // Grid of a group from its statistics: amax = max|x|, lo = min(min x, 0), hi = max(max x, 0).
 __device__ __forceinline__ Grid grid_make(float amax, float lo, float hi, int bits, int sym) {
@@ -45,6 +66,7 @@ __device__ __forceinline__ Grid grid_make(float amax, float lo, float hi, int bi
     g.qhi = sym ? qmax_s : maxq;
     g.zadd = sym ? half : 0.0f;
     g.zero = sym ? half : z;
+    grid_scale(g);
     return g;
 }
 
@@ -58,13 +80,17 @@ __device__ __forceinline__ Grid grid_from_stored(float s, float zero, int bits, 
     g.qhi = sym ? (half - 1.0f) : (float)((1 << bits) - 1);
     g.zadd = sym ? half : 0.0f;
     g.zero = zero;
+    grid_scale(g);
     return g;
 }
 
 // Stored code (as a float holding a small integer).
 __device__ __forceinline__ float grid_code(float x, const Grid &g) {
 #pragma clang fp contract(off)
-    const float q = rintf(x / g.s + g.zoff);
+    const float xs = __builtin_amdgcn_fmed3f(ldexpf(x, g.k), -2097152.0f, 2097152.0f);
+    const float q0 = xs * g.rs;
+    const float qd = fmaf(fmaf(-q0, g.ss, xs), g.rs, q0);  // RN(x / s)
+    const float q = rintf(qd + g.zoff);
     return fminf(fmaxf(q, g.qlo), g.qhi) + g.zadd;
 }
 
