@@ -46,26 +46,50 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     const int64_t r = (int64_t)blockIdx.x * kRows + (tid >> 2);
     const bool active = r < a.d_out;
     float *wrow = a.W + r * a.ldw + a.c0;
-    // Global loads of the prologue are issued in batches ahead of their LDS
-    // stores: first the row's weights and the batch's permutation entries,
-    // then the U block in passes of at most 16 16-byte chunks per thread.
-    float w[CPL];
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-        const int k = q + kRowLanes * t;
-        w[t] = (active && k < nc) ? wrow[k] : 0.0f;
-    }
+    // Global loads of the prologue are all issued before the first wait: the
+    // permutation entries, the row's weights, then the U block in passes of at
+    // most 16 16-byte chunks per thread.  The first two read clamped addresses
+    // and mask the values afterwards; the masks are opaque to the compiler, so
+    // it cannot move a load under a branch and wait for it there.
     constexpr int kPc = (BT + NT - 1) / NT;  // permutation entries per thread
     int32_t pc[kPc];
+    {
+        // with no permutation, U stands in as a readable address; the value is masked off
+        const int32_t *pp = a.perm ? a.perm : reinterpret_cast<const int32_t *>(a.U);
+        uint32_t mp = a.perm ? ~0u : 0u;
+        asm volatile("" : "+v"(mp));
 #pragma unroll
-    for (int u = 0; u < kPc; ++u) {
+        for (int u = 0; u < kPc; ++u) {
+            const int c = tid + u * NT;
+            const int64_t k = a.c0 + (c < nc ? c : 0);
+            const uint32_t v = (uint32_t)clamp_col(pp[k], a.ldc);
+            pc[u] = (int32_t)((v & mp) | ((uint32_t)(a.c0 + c) & ~mp));
+        }
+    }
+    float w[CPL];
+    {
+        const float *wsrc = a.W + (active ? r : a.d_out - 1) * a.ldw + a.c0;
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+            const int k = q + kRowLanes * t;
+            uint32_t m = (active && k < nc) ? ~0u : 0u;
+            asm volatile("" : "+v"(m));
+            w[t] = __uint_as_float(__float_as_uint(wsrc[k < nc ? k : nc - 1]) & m);
+        }
+    }
+    // 1 / U_jj of the batch's columns (zero past the batch end)
+    constexpr int kDg = (BT + NT - 1) / NT;
+    float dg[kDg];
+#pragma unroll
+    for (int u = 0; u < kDg; ++u) {
         const int c = tid + u * NT;
-        const int64_t k = a.c0 + (c < nc ? c : 0);
-        pc[u] = a.perm ? clamp_col(a.perm[k], a.ldc) : (int32_t)(a.c0 + c);
+        const int64_t cc = a.c0 + (c < nc ? c : nc - 1);
+        dg[u] = a.U[cc * a.ldu + cc];
     }
     {
-        constexpr int kChunks = BT * BT / 4;                 // 16-byte chunks of the U block
-        constexpr int kUPer = (kChunks + NT - 1) / NT;       // per thread
+        constexpr int kChunks = BT * BT / 4;  // 16-byte chunks of the U block
+        static_assert(kChunks % NT == 0, "U block chunks must split evenly over the threads");
+        constexpr int kUPer = kChunks / NT;                  // per thread
         constexpr int kPass = kUPer < 16 ? kUPer : 16;       // per thread and pass
         const float *src = a.U + a.c0 * a.ldu + a.c0;
         const bool vec = a.vec && (a.ldu % 4 == 0) && (a.c0 % 4 == 0) && nc == BT;
@@ -77,32 +101,29 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                 for (int u = 0; u < kPass; ++u) {
                     const int e4 = tid + (p0 + u) * NT;
                     const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-                    uv[u] = e4 < kChunks ? *reinterpret_cast<const float4 *>(src + i * a.ldu + k)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                    uv[u] = *reinterpret_cast<const float4 *>(src + i * a.ldu + k);
                 }
-            } else {
+            } else {  // partial or unaligned batch: clamped scalar loads, masked
 #pragma unroll
                 for (int u = 0; u < kPass; ++u) {
                     const int e4 = tid + (p0 + u) * NT;
                     const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-                    const bool in = e4 < kChunks && i < nc;
-                    const float *p = src + i * a.ldu + k;
-                    uv[u].x = (in && k + 0 < nc) ? p[0] : 0.0f;
-                    uv[u].y = (in && k + 1 < nc) ? p[1] : 0.0f;
-                    uv[u].z = (in && k + 2 < nc) ? p[2] : 0.0f;
-                    uv[u].w = (in && k + 3 < nc) ? p[3] : 0.0f;
+                    const float *p = src + (int64_t)(i < nc ? i : nc - 1) * a.ldu;
+                    float v4[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        uint32_t m = (i < nc && k + x < nc) ? ~0u : 0u;
+                        asm volatile("" : "+v"(m));
+                        v4[x] = __uint_as_float(__float_as_uint(p[k + x < nc ? k + x : nc - 1]) & m);
+                    }
+                    uv[u] = make_float4(v4[0], v4[1], v4[2], v4[3]);
                 }
             }
 #pragma unroll
             for (int u = 0; u < kPass; ++u) {
                 const int e4 = tid + (p0 + u) * NT;
-                if (e4 >= kChunks) break;
                 const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
-                float4 v = uv[u];
-                if (k + 0 == i) inv_d[i] = i < nc ? 1.0f / v.x : 0.0f;
-                if (k + 1 == i) inv_d[i] = i < nc ? 1.0f / v.y : 0.0f;
-                if (k + 2 == i) inv_d[i] = i < nc ? 1.0f / v.z : 0.0f;
-                if (k + 3 == i) inv_d[i] = i < nc ? 1.0f / v.w : 0.0f;
+                const float4 v = uv[u];
                 // columns k .. k+3 belong to quad lanes 0..3, at t = k / 4
                 const int t = k / kRowLanes;
                 ut[i][t / 4][0][t % 4] = (k + 0 > i) ? v.x : 0.0f;
@@ -111,6 +132,11 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                 ut[i][t / 4][3][t % 4] = (k + 3 > i) ? v.w : 0.0f;
             }
         }
+    }
+#pragma unroll
+    for (int u = 0; u < kDg; ++u) {
+        const int c = tid + u * NT;
+        if (c < BT) inv_d[c] = c < nc ? 1.0f / dg[u] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kPc; ++u) {
@@ -149,6 +175,8 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         const int oq = j & (kRowLanes - 1), ot = j / kRowLanes;
         const int cur = j & 1;
         if (j + 1 < BT) load_row(j + 1, urow[cur ^ 1], idn[cur ^ 1]);
+        // the reads stay here, a column ahead of their use
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (GT > 0) {
             if (j % GT == 0) {
                 float amax = 0.0f, lo = 0.0f, hi = 0.0f;
@@ -170,9 +198,11 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             }
         }
         const float wj = quad_bcast(w[ot], oq);
-        const float code = grid_code(wj, gr);
-        const float wh = grid_dequant(code, gr);
-        const float e = (wj - wh) * idn[cur];
+        const float ql = grid_level(wj, gr);
+        const float code = ql + gr.zadd;
+        // e = (w_j - (code - zero) s) / U_jj, with code - zero = ql - zd exact;
+        // w_j / U_jj and s / U_jj are formed beside the quantization
+        const float e = fmaf(-(ql - gr.zd), gr.s * idn[cur], wj * idn[cur]);
         cw[ot / 4] |= (q == oq ? (uint32_t)code : 0u) << (8 * (ot & 3));
         et[(int64_t)j * a.ldet] = -e;
 #pragma unroll

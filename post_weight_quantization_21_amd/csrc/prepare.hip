@@ -104,36 +104,45 @@ __device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb)
 
 // UL-Cholesky of one diagonal block on one wave64 with no workgroup barriers
 // (the other waves of the workgroup, if any, have left).  On entry lane i holds
-// row i of the block in c (upper part, padded with the identity past nb).  For
-// j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
-// c_ii' -= t_ij t_i'j (i' < j).  The pivot is the step's only serial
+// row i of the block in c (upper part, zero below the diagonal, padded with the
+// identity past nb).  For j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj
+// (i < j);  c_ii' -= t_ij t_i'j (i' < j).  The pivot is the step's only serial
 // dependence.  So step j updates the next kEager columns at once, from column
 // j's entries read out of their lanes (readlane), and writes column j to LDS
 // and reads it back for the remaining columns; those updates run one step
 // later, after the next pivot, so neither the LDS latency nor their issue
 // time sits on the chain of pivots.  (LDS operations of one wave complete in
 // issue order, so the reads see the write without a wait.)
-// On exit c holds row i of T (upper).  A non-positive pivot j sets
-// *info = kb + j + 1 (first one wins).  T goes into the factor's diagonal
+// Every lane runs the same scaling and updates: lane j gets
+// c_jj / sqrt(c_jj) = t_jj, and a lane past j only changes entries below its
+// diagonal, which no later step reads (column j's entries are read from lanes
+// below j only) and which are stored as zero; so no per-lane selects are
+// needed.
+// On exit c holds row i of T (upper).  A non-positive pivot j sets t_jj = 1
+// and *info = kb + j + 1 for the first one in processing order (first one
+// over all blocks wins).  T goes into the factor's diagonal
 // block Tf[kb:kb+nb, kb:kb+nb] (upper part).
 constexpr int kEager = 4;
-__device__ __forceinline__ void factor_block(float (&c)[NB], int lane, int nb, int64_t kb, float *__restrict__ Tf,
-                                             int64_t lda, int32_t *__restrict__ info, float *col) {
-    int32_t first_bad = 0;
+__device__ __forceinline__ void factor_block(float (&c)[NB], int nb, int64_t kb, float *__restrict__ Tf, int64_t lda,
+                                             int32_t *__restrict__ info, float *col) {
+    const int lane = (int)__lane_id();
+    // The masks of the block's loading (lanes and columns against nb) are not
+    // reused here: kept live across the steps, they would take the scalar
+    // registers.
+    asm volatile("" : "+s"(nb));
+    uint64_t bad_mask = 0;  // non-positive pivots
     float tp = 0.0f;        // column j+1 of T (this lane's entry), for the deferred updates
     float4 cv[NB / 4];      // column j+1 of T from LDS
 #pragma unroll
     for (int j = NB - 1; j >= 0; --j) {
         const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));  // pivot, from lane j
         const bool bad = !(p0 > 0.0f);
-        first_bad = (bad && first_bad == 0 && j < nb) ? (int32_t)(kb + j + 1) : first_bad;
-        // hardware reciprocal square root / square root (about 1 ulp): the
-        // factor only has to be accurate; branch-free selects keep the wave on
-        // one path.
-        const float pv = bad ? 1.0f : p0;
-        float t = c[j] * __builtin_amdgcn_rsqf(pv);
-        t = lane == j ? __builtin_amdgcn_sqrtf(pv) : t;
-        t = lane > j ? 0.0f : t;
+        // (bad is the same on every lane; the ballot keeps the mask scalar)
+        bad_mask |= __builtin_amdgcn_ballot_w64(bad) & ((uint64_t)1 << j);
+        asm volatile("" : "+s"(bad_mask));  // formed now: the step's compare mask dies here
+        // hardware reciprocal square root (about 1 ulp): the factor only has
+        // to be accurate
+        const float t = c[j] * __builtin_amdgcn_rsqf(bad ? 1.0f : p0);
         c[j] = t;
 #pragma unroll
         for (int m = 1; m <= kEager; ++m) {
@@ -158,17 +167,28 @@ __device__ __forceinline__ void factor_block(float (&c)[NB], int lane, int nb, i
         tp = t;
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (first_bad != 0 && lane == 0) atomicCAS(info, 0, first_bad);
-    if (lane < nb) {
-        float *dst = Tf + (kb + lane) * lda + kb;
+    // The lane masks of what follows are formed here, not hoisted above the
+    // steps (where they would be kept live in scalar registers).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (bad_mask != 0) {  // uniform, rarely taken: t_jj = 1 and the first bad pivot (highest j below nb)
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            if ((bad_mask >> m) & 1) c[m] = ln == m ? 1.0f : c[m];
+        const uint64_t in_nb = nb >= NB ? ~(uint64_t)0 : (((uint64_t)1 << nb) - 1);
+        const uint64_t b = bad_mask & in_nb;
+        if (b != 0 && ln == 0) atomicCAS(info, 0, (int32_t)(kb + (63 - __builtin_clzll(b)) + 1));
+    }
+    if (ln < nb) {
+        float *dst = Tf + (kb + ln) * lda + kb;
 #pragma unroll
         for (int q = 0; q < NB / 4; ++q) {
-            if (4 * q + 3 < lane) continue;  // wholly below the diagonal
+            if (4 * q + 3 < ln) continue;  // wholly below the diagonal
             float4 v;
-            v.x = (4 * q + 0 >= lane) ? c[4 * q + 0] : 0.0f;
-            v.y = (4 * q + 1 >= lane) ? c[4 * q + 1] : 0.0f;
-            v.z = (4 * q + 2 >= lane) ? c[4 * q + 2] : 0.0f;
-            v.w = (4 * q + 3 >= lane) ? c[4 * q + 3] : 0.0f;
+            v.x = (4 * q + 0 >= ln) ? c[4 * q + 0] : 0.0f;
+            v.y = (4 * q + 1 >= ln) ? c[4 * q + 1] : 0.0f;
+            v.z = (4 * q + 2 >= ln) ? c[4 * q + 2] : 0.0f;
+            v.w = (4 * q + 3 >= ln) ? c[4 * q + 3] : 0.0f;
             if (4 * q + 3 < nb) {
                 *reinterpret_cast<float4 *>(dst + 4 * q) = v;
             } else {
@@ -202,7 +222,7 @@ void panel_kernel(const float *__restrict__ A, float *__restrict__ Tf, int64_t l
         c[4 * q + 3] = v.w;
     }
     mask_block_row(c, lane, nb);
-    factor_block(c, lane, nb, k0, Tf, lda, info, col);
+    factor_block(c, nb, k0, Tf, lda, info, col);
 }
 
 // V = T_bb^-1 of every diagonal block b (one wave each, all blocks at once,
@@ -513,7 +533,7 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
         c[4 * e + 3] = v.w;
     }
     mask_block_row(c, lane, NB);
-    factor_block(c, lane, NB, nb0, Tf, lda, info, &sm.pi[0][0]);  // P_i^T is dead: its first row is scratch
+    factor_block(c, NB, nb0, Tf, lda, info, &sm.pi[0][0]);  // P_i^T is dead: its first row is scratch
 }
 
 // P = panel T_kk^-T for one 64-row block [r0, r0+64) of the leading rows

@@ -34,6 +34,7 @@ namespace gptq {
 struct Grid {
     float s, zoff, qlo, qhi, zadd, zero;
     float ss, rs;  // s' = s 2^k in [1, 2) and RN(1 / s')
+    float zd;      // zero - zadd: code - zero = level - zd (small integers, exact)
     int k;
 };
 
@@ -66,6 +67,7 @@ __device__ __forceinline__ Grid grid_make(float amax, float lo, float hi, int bi
     g.qhi = sym ? qmax_s : maxq;
     g.zadd = sym ? half : 0.0f;
     g.zero = sym ? half : z;
+    g.zd = g.zero - g.zadd;
     grid_scale(g);
     return g;
 }
@@ -80,24 +82,21 @@ __device__ __forceinline__ Grid grid_from_stored(float s, float zero, int bits, 
     g.qhi = sym ? (half - 1.0f) : (float)((1 << bits) - 1);
     g.zadd = sym ? half : 0.0f;
     g.zero = zero;
+    g.zd = zero - g.zadd;
     grid_scale(g);
     return g;
 }
 
-// Stored code (as a float holding a small integer).
-__device__ __forceinline__ float grid_code(float x, const Grid &g) {
+// Grid level clamp(rint(x / s + zoff), qlo, qhi); the stored code is level + zadd.
+__device__ __forceinline__ float grid_level(float x, const Grid &g) {
 #pragma clang fp contract(off)
     const float xs = __builtin_amdgcn_fmed3f(ldexpf(x, g.k), -2097152.0f, 2097152.0f);
     const float q0 = xs * g.rs;
     const float qd = fmaf(fmaf(-q0, g.ss, xs), g.rs, q0);  // RN(x / s)
-    const float q = rintf(qd + g.zoff);
-    return fminf(fmaxf(q, g.qlo), g.qhi) + g.zadd;
+    return __builtin_amdgcn_fmed3f(rintf(qd + g.zoff), g.qlo, g.qhi);
 }
 
-// Dequantized value, rounded to fp32 on its own (never fused into a following add).
-__device__ __forceinline__ float grid_dequant(float code, const Grid &g) {
-#pragma clang fp contract(off)
-    return (code - g.zero) * g.s;
-}
+// Stored code (as a float holding a small integer).
+__device__ __forceinline__ float grid_code(float x, const Grid &g) { return grid_level(x, g) + g.zadd; }
 
 }  // namespace gptq
