@@ -26,23 +26,32 @@ constexpr int NB = 64;  // diagonal block edge
 constexpr int kThreads = 256;
 
 // perm[rank] = column; rank by descending key, ties by lower index (stable).
-// NaN keys sort last, so the ranks always form a permutation.
+// NaN keys sort last, so the ranks always form a permutation.  Each thread
+// ranks one key against all d keys, which pass through LDS in chunks (every
+// lane reads the same key: a broadcast).
 __device__ __forceinline__ double order_key(const double *hdiag, const float *H, int64_t d, int64_t i) {
     const double k = hdiag ? hdiag[i] : (double)H[i * d + i];
     return k == k ? k : -__builtin_inf();
 }
 
+constexpr int kKeyChunk = 2048;
 __global__ __launch_bounds__(kThreads) void order_kernel(const double *__restrict__ hdiag, const float *__restrict__ H,
                                                          int64_t d, int32_t *__restrict__ perm) {
+    __shared__ double keys[kKeyChunk];
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= d) return;
-    const double ki = order_key(hdiag, H, d, i);
+    const double ki = i < d ? order_key(hdiag, H, d, i) : 0.0;
     int64_t rank = 0;
-    for (int64_t j = 0; j < d; ++j) {
-        const double kj = order_key(hdiag, H, d, j);
-        rank += (kj > ki) || (kj == ki && j < i);
+    for (int64_t j0 = 0; j0 < d; j0 += kKeyChunk) {
+        const int n = (int)(d - j0 < kKeyChunk ? d - j0 : kKeyChunk);
+        __syncthreads();  // the previous chunk is consumed
+        for (int jj = threadIdx.x; jj < n; jj += kThreads) keys[jj] = order_key(hdiag, H, d, j0 + jj);
+        __syncthreads();
+        for (int jj = 0; jj < n; ++jj) {
+            const double kj = keys[jj];
+            rank += (kj > ki) || (kj == ki && j0 + jj < i);
+        }
     }
-    perm[rank] = (int32_t)i;
+    if (i < d) perm[rank] = (int32_t)i;
 }
 
 // A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper triangle.

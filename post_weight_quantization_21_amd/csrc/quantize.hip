@@ -80,6 +80,37 @@ __global__ __launch_bounds__(kThreads) void permute_cols_kernel(const float *__r
         W[r * d_in + k] = src[r * d_in + clamp_col(perm[k], d_in)];
 }
 
+// W[r][k] = W[r][perm[k]] in place, one row at a time through LDS (d_in floats,
+// d_in a multiple of 4, W 16-byte aligned).  Rows are read once and written
+// once, coalesced; the gather reads LDS.
+constexpr int64_t kRowPermMax = 16384;  // d_in limit of the in-place path (64 KB of LDS)
+__global__ __launch_bounds__(kThreads) void permute_rows_inplace_kernel(float *__restrict__ W,
+                                                                        const int32_t *__restrict__ perm, int64_t d_out,
+                                                                        int64_t d_in) {
+    extern __shared__ float row[];
+    const int tid = threadIdx.x;
+    for (int64_t r = blockIdx.x; r < d_out; r += gridDim.x) {
+        float *w = W + r * d_in;
+        for (int64_t k = 4 * tid; k < d_in; k += 4 * kThreads)
+            *reinterpret_cast<float4 *>(&row[k]) = *reinterpret_cast<const float4 *>(w + k);
+        __syncthreads();
+        for (int64_t k = 4 * tid; k < d_in; k += 4 * kThreads) {
+            float4 v;
+            v.x = row[clamp_col(perm[k + 0], d_in)];
+            v.y = row[clamp_col(perm[k + 1], d_in)];
+            v.z = row[clamp_col(perm[k + 2], d_in)];
+            v.w = row[clamp_col(perm[k + 3], d_in)];
+            *reinterpret_cast<float4 *>(w + k) = v;
+        }
+        __syncthreads();  // row[] is reused by the next row
+    }
+}
+
+// Whether the act-order permutation of W runs in place (else: copy, then gather).
+bool row_perm_inplace(const float *W, int64_t d_in) {
+    return d_in <= kRowPermMax && d_in % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+}
+
 __global__ __launch_bounds__(kThreads) void gidx_kernel(const int32_t *__restrict__ perm, int64_t d_in, int64_t g,
                                                         int32_t *__restrict__ g_idx) {
     const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -107,8 +138,8 @@ int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
 }
 
 // Workspace of the column pass: E^T of a whole superblock [S][ldet] (one batch
-// when there is a single superblock) and (act-order only) a copy of W for the
-// column gather.
+// when there is a single superblock) and (act-order with rows too long for the
+// in-place permutation only) a copy of W for the column gather.
 struct QuantLayout {
     size_t et_off, wc_off, total;
     int64_t sc;       // superblock width
@@ -121,7 +152,8 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     l.et_rows = l.sc < d_in ? l.sc : c.block_size;
     l.et_off = 0;
     l.wc_off = align_up((size_t)l.et_rows * (size_t)et_ld(d_out) * sizeof(float), 256);
-    l.total = l.wc_off + (c.act_order ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
+    const bool copy = c.act_order && d_in > kRowPermMax;  // aligned W assumed (checked at the boundary)
+    l.total = l.wc_off + (copy ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
     return l;
 }
 
@@ -168,7 +200,13 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     float *Et = reinterpret_cast<float *>(wsb + lay.et_off);
     hipError_t e;
     const int32_t *pp = c.act_order ? perm : nullptr;
-    if (pp) {
+    if (pp && d_in <= kRowPermMax && !row_perm_inplace(W, d_in)) return hipErrorInvalidValue;  // no copy space
+    if (pp && row_perm_inplace(W, d_in)) {
+        const unsigned grid = (unsigned)std::min<int64_t>(d_out, 2048);
+        hipLaunchKernelGGL(permute_rows_inplace_kernel, dim3(grid), dim3(kThreads), (size_t)d_in * sizeof(float), s, W, pp,
+                           d_out, d_in);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (pp) {
         float *Wc = reinterpret_cast<float *>(wsb + lay.wc_off);
         const int64_t n = d_out * d_in, n4 = n / 4;
         hipLaunchKernelGGL(copy_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n4, kThreads), 65536)), dim3(kThreads), 0,

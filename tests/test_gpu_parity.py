@@ -205,6 +205,40 @@ def test_column_pass_with_oracle_factor(oracle_mod, bits, sym, group, block, d_o
     assert np.abs(wq[same] - ref["w_at_q"][same]).max() <= 1e-4 * np.abs(ref["w_at_q"]).max()
 
 
+@pytest.mark.parametrize("d_out,d_in,group", [(4, 16512, 128), (5, 1024, 0)])
+def test_act_order_identity_factor_gives_permuted_rtn(oracle_mod, d_out, d_in, group):
+    """With U = I no error is fed forward, so the pass with a column order is RTN
+    of the permuted columns, bit for bit, and W returns permuted and unchanged.
+    16512 columns take the copy-and-gather permutation of long rows, 1024 (one
+    group per row) the in-place one."""
+    torch = torch_mod()
+    log(f"act-order identity {d_out}x{d_in} g={group}")
+    rng = np.random.default_rng(d_in)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    perm = rng.permutation(d_in).astype(np.int32)
+    ref = oracle_mod.rtn(np.ascontiguousarray(W[:, perm]), 4, True, group)
+    ng = gq.n_groups(d_in, group)
+    cfg = gq.config(4, True, group, 128, 0.01, True)
+    U = torch.eye(d_in, dtype=torch.float32, device="cuda")
+    Wd = cuda(W)
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    ze = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    gidx = torch.empty(d_in, dtype=torch.int32, device="cuda")
+    gq.quantize_layer(Wd, U, cfg, codes, sc, ze, perm=cuda(perm), g_idx=gidx)
+    torch.cuda.synchronize()
+    want = np.empty_like(ref["codes"])
+    want[:, perm] = ref["codes"]
+    assert np.array_equal(host(codes), want)
+    assert np.array_equal(host(sc), ref["scales"])
+    assert np.array_equal(host(ze), ref["zeros"])
+    assert np.array_equal(host(Wd), W[:, perm])
+    g = group if group > 0 else d_in
+    want_g = np.empty(d_in, dtype=np.int32)
+    want_g[perm] = np.arange(d_in) // g
+    assert np.array_equal(host(gidx), want_g)
+
+
 def test_identity_hessian_gives_rtn(oracle_mod):
     """With H = I no error is fed forward: GPTQ on the GPU equals the oracle's RTN bit for bit."""
     torch = torch_mod()
