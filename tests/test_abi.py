@@ -47,7 +47,10 @@ def test_workspace_sizes():
     c = gq.config(4, False, 128, 128)
     assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, c) >= 128 * 4096 * 4
     ca = gq.config(4, True, 128, 128, act_order=True)
-    assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, ca) >= 128 * 4096 * 4 + 4096 * 4096 * 4
+    # rows up to 16384 columns are permuted in place: no copy of W
+    assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, ca) == gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, c)
+    # longer rows are copied, then gathered
+    assert gq.workspace_bytes(gq.OP_QUANTIZE, 8, 16512, 0, ca) >= 128 * 256 * 4 + 8 * 16512 * 4
     assert gq.workspace_bytes(gq.OP_PREPARE, 0, 4096) >= 2 * 4096 * 4096 * 4
     assert gq.workspace_bytes(gq.OP_LOSS, 64, 128) >= 64 * 128 * 4 + 128 * 128 * 4
     # a single tile with few tokens is not split over tokens: no workspace
