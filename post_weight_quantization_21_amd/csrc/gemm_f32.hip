@@ -107,10 +107,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     constexpr int QB = T / 64;  // 32x32 MFMA blocks per wave along each dimension
     constexpr int HW = T / 2;   // wave tile edge
     // With B upper triangular the tiles of the last columns have the longest K:
-    // they are dispatched first (with A upper, the first rows are the longest,
-    // and they already come first).
-    const int tn = g.b_upper ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    const int tm = blockIdx.y, bz = blockIdx.z;
+    // they are dispatched first, column by column over every row of tiles, so
+    // the launch does not end on long tiles (with A upper, the first rows are
+    // the longest, and they already come first).
+    int tm = blockIdx.y, tn = blockIdx.x;
+    if (g.b_upper) {
+        const int id = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;  // dispatch order
+        tn = (int)gridDim.x - 1 - id / (int)gridDim.y;
+        tm = id % (int)gridDim.y;
+    }
+    const int bz = blockIdx.z;
     if (g.upper_only && tm > tn) return;  // strictly below the diagonal: nothing to store
     const int64_t m0 = (int64_t)tm * T, n0 = (int64_t)tn * T;
 
