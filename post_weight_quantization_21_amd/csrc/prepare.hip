@@ -111,127 +111,182 @@ __device__ __forceinline__ void mask_block_row(float (&c)[NB], int lane, int nb)
     }
 }
 
-// UL-Cholesky of one diagonal block on one wave64 with no workgroup barriers
-// (the other waves of the workgroup, if any, have left).  On entry lane i holds
-// row i of the block in c (upper part, zero below the diagonal, padded with the
-// identity past nb).  For j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj
-// (i < j);  c_ii' -= t_ij t_i'j (i' < j).  The pivot is the step's only serial
-// dependence.  So step j updates the next kEager columns at once, from column
-// j's entries read out of their lanes (readlane), and writes column j to LDS
-// and reads it back for the remaining columns; those updates run one step
-// later, after the next pivot, so neither the LDS latency nor their issue
-// time sits on the chain of pivots.  (LDS operations of one wave complete in
-// issue order, so the reads see the write without a wait.)
-// Every lane runs the same scaling and updates: lane j gets
-// c_jj / sqrt(c_jj) = t_jj, and a lane past j only changes entries below its
-// diagonal, which no later step reads (column j's entries are read from lanes
-// below j only) and which are stored as zero; so no per-lane selects are
-// needed.
-// On exit c holds row i of T (upper).  A non-positive pivot j sets t_jj = 1
-// and *info = kb + j + 1 for the first one in processing order (first one
-// over all blocks wins).  T goes into the factor's diagonal
-// block Tf[kb:kb+nb, kb:kb+nb] (upper part).
-constexpr int kEager = 4;
-__device__ __forceinline__ void factor_block(float (&c)[NB], int nb, int64_t kb, float *__restrict__ Tf, int64_t lda,
-                                             int32_t *__restrict__ info, float *col) {
+// UL-Cholesky of one diagonal block on the four waves of a workgroup.  For
+// j = NB-1..0:  t_jj = sqrt(c_jj);  t_ij = c_ij / t_jj (i < j);
+// c_ii' -= t_ij t_i'j (i' < j).  Wave w holds columns 16w .. 16w+15 of every row
+// (lane i = row i) in cw (upper part, zero below the diagonal, the identity past
+// nb).  The columns are factored from the right in four panels of 16:
+//  * the panel's owner wave factors its 16 columns alone: the pivot comes from
+//    its lane by readlane, t = c_j rsq(c_jj) on every lane (lane j gets t_jj;
+//    lanes past j only change entries below their diagonal, which no later step
+//    reads and which are stored as zero); the next pivot's column is updated at
+//    once from a readlane of t, the panel's other columns one step later from
+//    t's copy in LDS (col), so the pivot chain waits for neither; each column of
+//    T also goes to LDS (pt);
+//  * then every wave left of the panel subtracts the panel's rank-16 product
+//    from its own 16 columns, reading its row's panel entries and the panel
+//    rows of its columns (broadcasts) from LDS, four panel columns at a time
+//    into 16 independent sums.
+// A non-positive pivot sets t_jj = 1, and *info = kb + j + 1 for the first one
+// in processing order (the first over all blocks wins).  T goes into the
+// factor's diagonal block Tf[kb:kb+nb, kb:kb+nb] (upper part).
+constexpr int kFCols = NB / 4;  // columns per wave
+struct FactorSmem {
+    float pt[NB][kFCols + 4];  // pt[i][m] = T[i][16 w + m] of the current panel w
+    float col[2][NB];          // the owner's last two columns of T, by row
+    int32_t badj[4];           // per wave: highest bad pivot column below nb, or -1
+};
+static_assert(sizeof(FactorSmem) <= sizeof(float) * NB * (NB + 4), "the factor's LDS reuses one 64 x 68 panel buffer");
+
+// Row `lane` of the block, wave w's columns, masked: zero below the diagonal,
+// the identity past nb.
+__device__ __forceinline__ void mask_block_cols(float (&cw)[kFCols], int lane, int wave, int nb) {
+#pragma unroll
+    for (int m = 0; m < kFCols; ++m) {
+        const int c = kFCols * wave + m;
+        const bool in = lane < nb && c < nb;
+        cw[m] = in ? (c >= lane ? cw[m] : 0.0f) : (c == lane ? 1.0f : 0.0f);
+    }
+}
+
+__device__ __forceinline__ void factor_block(float (&cw)[kFCols], int wave, int nb, int64_t kb, float *__restrict__ Tf,
+                                             int64_t lda, int32_t *__restrict__ info, FactorSmem &fs) {
     const int lane = (int)__lane_id();
+    wave = __builtin_amdgcn_readfirstlane(wave);  // uniform: the panel branches are scalar
     // The masks of the block's loading (lanes and columns against nb) are not
     // reused here: kept live across the steps, they would take the scalar
     // registers.
     asm volatile("" : "+s"(nb));
-    uint64_t bad_mask = 0;  // non-positive pivots
-    float tp = 0.0f;        // column j+1 of T (this lane's entry), for the deferred updates
-    float4 cv[NB / 4];      // column j+1 of T from LDS
+    uint32_t bad_mask = 0;  // bad pivots of this wave's panel (bit m: column 16 wave + m)
 #pragma unroll
-    for (int j = NB - 1; j >= 0; --j) {
-        const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));  // pivot, from lane j
-        const bool bad = !(p0 > 0.0f);
-        // (bad is the same on every lane; the ballot keeps the mask scalar)
-        bad_mask |= __builtin_amdgcn_ballot_w64(bad) & ((uint64_t)1 << j);
-        asm volatile("" : "+s"(bad_mask));  // formed now: the step's compare mask dies here
-        // hardware reciprocal square root (about 1 ulp): the factor only has
-        // to be accurate
-        const float t = c[j] * __builtin_amdgcn_rsqf(bad ? 1.0f : p0);
-        c[j] = t;
+    for (int w = 3; w >= 0; --w) {
+        if (wave == w) {
+            float tp = 0.0f;            // the previous step's column of T (this lane's entry)
+            float4 cv[kFCols / 4] = {};  // ... and its panel rows, read at the end of that step
 #pragma unroll
-        for (int m = 1; m <= kEager; ++m) {
-            if (j - m < 0) break;
-            const float tm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), j - m));
-            c[j - m] = fmaf(-t, tm, c[j - m]);
+            for (int m = kFCols - 1; m >= 0; --m) {
+                const int j = kFCols * w + m;
+                const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw[m]), j));  // pivot
+                const bool bad = !(p0 > 0.0f);
+                // (bad is the same on every lane; the ballot keeps the mask scalar)
+                bad_mask |= __builtin_amdgcn_ballot_w64(bad) ? (1u << m) : 0u;
+                // hardware reciprocal square root (about 1 ulp): the factor
+                // only has to be accurate
+                const float t = cw[m] * __builtin_amdgcn_rsqf(bad ? 1.0f : p0);
+                cw[m] = t;
+                fs.pt[lane][m] = t;
+                // step m+1's update of columns 0 .. m-1 (its column m was updated then)
+                if (m + 1 < kFCols) {
+#pragma unroll
+                    for (int m2 = 0; m2 < m; ++m2) cw[m2] = fmaf(-tp, cv[m2 / 4][m2 % 4], cw[m2]);
+                }
+                // this step's update of the next pivot's column
+                if (m >= 1) {
+                    const float tm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), j - 1));
+                    cw[m - 1] = fmaf(-t, tm, cw[m - 1]);
+                }
+                // this column's panel rows for the next step (LDS operations
+                // of a wave complete in order: the reads see the write)
+                if (m >= 2) {
+                    fs.col[m & 1][lane] = t;
+#pragma unroll
+                    for (int q = 0; q < (m - 1 + 3) / 4; ++q)
+                        cv[q] = *reinterpret_cast<const float4 *>(&fs.col[m & 1][kFCols * w + 4 * q]);
+                }
+                tp = t;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        // step j+1's remaining columns 0 .. j-kEager, in the order of their LDS reads
+        if (w == 0) break;
+        __syncthreads();  // the panel is in LDS
+        if (wave < w) {
+            // c_i,c -= sum_m T[i][16w+m] T[c][16w+m] for this wave's 16 columns c,
+            // panel columns taken in pivot order (right to left)
+            float4 pr[kFCols / 4];  // this row's entries of the panel
 #pragma unroll
-        for (int i2 = 0; i2 <= j - kEager; ++i2) {
-            if (j == NB - 1) break;
-            c[i2] = fmaf(-tp, cv[i2 / 4][i2 % 4], c[i2]);
-        }
-        const int nbulk = j - kEager;  // step j's remaining columns 0 .. nbulk-1
-        if (nbulk > 0) {
-            col[lane] = t;
-            __builtin_amdgcn_wave_barrier();
+            for (int q = 0; q < kFCols / 4; ++q) pr[q] = *reinterpret_cast<const float4 *>(&fs.pt[lane][4 * q]);
 #pragma unroll
-            for (int q = 0; q < (nbulk + 3) / 4; ++q) cv[q] = *reinterpret_cast<const float4 *>(&col[4 * q]);
-            __builtin_amdgcn_wave_barrier();
+            for (int q = kFCols / 4 - 1; q >= 0; --q) {
+                float4 qv[kFCols];  // panel columns 4q..4q+3 of this wave's columns' rows (broadcasts)
+#pragma unroll
+                for (int m2 = 0; m2 < kFCols; ++m2)
+                    qv[m2] = *reinterpret_cast<const float4 *>(&fs.pt[kFCols * wave + m2][4 * q]);
+#pragma unroll
+                for (int m2 = 0; m2 < kFCols; ++m2) cw[m2] = fmaf(-pr[q].w, qv[m2].w, cw[m2]);
+#pragma unroll
+                for (int m2 = 0; m2 < kFCols; ++m2) cw[m2] = fmaf(-pr[q].z, qv[m2].z, cw[m2]);
+#pragma unroll
+                for (int m2 = 0; m2 < kFCols; ++m2) cw[m2] = fmaf(-pr[q].y, qv[m2].y, cw[m2]);
+#pragma unroll
+                for (int m2 = 0; m2 < kFCols; ++m2) cw[m2] = fmaf(-pr[q].x, qv[m2].x, cw[m2]);
+            }
         }
-        tp = t;
-        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // pt is rewritten by the next panel
     }
     // The lane masks of what follows are formed here, not hoisted above the
     // steps (where they would be kept live in scalar registers).
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    if (bad_mask != 0) {  // uniform, rarely taken: t_jj = 1 and the first bad pivot (highest j below nb)
+    const uint32_t in_nb_bits = bad_mask & (kFCols * wave + kFCols <= nb ? 0xFFFFu
+                                            : (kFCols * wave >= nb ? 0u : ((1u << (nb - kFCols * wave)) - 1u)));
+    if (bad_mask != 0) {  // uniform, rarely taken: t_jj = 1
 #pragma unroll
-        for (int m = 0; m < NB; ++m)
-            if ((bad_mask >> m) & 1) c[m] = ln == m ? 1.0f : c[m];
-        const uint64_t in_nb = nb >= NB ? ~(uint64_t)0 : (((uint64_t)1 << nb) - 1);
-        const uint64_t b = bad_mask & in_nb;
-        if (b != 0 && ln == 0) atomicCAS(info, 0, (int32_t)(kb + (63 - __builtin_clzll(b)) + 1));
+        for (int m = 0; m < kFCols; ++m)
+            if ((bad_mask >> m) & 1) cw[m] = ln == kFCols * wave + m ? 1.0f : cw[m];
+    }
+    if (ln == 0) fs.badj[wave] = in_nb_bits ? kFCols * wave + (31 - __builtin_clz(in_nb_bits)) : -1;
+    __syncthreads();
+    if (wave == 0 && ln == 0) {
+        int jb = -1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) jb = fs.badj[v] > jb ? fs.badj[v] : jb;
+        if (jb >= 0) atomicCAS(info, 0, (int32_t)(kb + jb + 1));
     }
     if (ln < nb) {
-        float *dst = Tf + (kb + ln) * lda + kb;
+        float *dst = Tf + (kb + ln) * lda + kb + kFCols * wave;
 #pragma unroll
-        for (int q = 0; q < NB / 4; ++q) {
-            if (4 * q + 3 < ln) continue;  // wholly below the diagonal
+        for (int q = 0; q < kFCols / 4; ++q) {
+            const int c0 = kFCols * wave + 4 * q;
+            if (c0 + 3 < ln) continue;  // wholly below the diagonal
             float4 v;
-            v.x = (4 * q + 0 >= ln) ? c[4 * q + 0] : 0.0f;
-            v.y = (4 * q + 1 >= ln) ? c[4 * q + 1] : 0.0f;
-            v.z = (4 * q + 2 >= ln) ? c[4 * q + 2] : 0.0f;
-            v.w = (4 * q + 3 >= ln) ? c[4 * q + 3] : 0.0f;
-            if (4 * q + 3 < nb) {
+            v.x = (c0 + 0 >= ln) ? cw[4 * q + 0] : 0.0f;
+            v.y = (c0 + 1 >= ln) ? cw[4 * q + 1] : 0.0f;
+            v.z = (c0 + 2 >= ln) ? cw[4 * q + 2] : 0.0f;
+            v.w = (c0 + 3 >= ln) ? cw[4 * q + 3] : 0.0f;
+            if (c0 + 3 < nb) {
                 *reinterpret_cast<float4 *>(dst + 4 * q) = v;
             } else {
                 const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (4 * q + e < nb) dst[4 * q + e] = vv[e];
+                    if (c0 + e < nb) dst[4 * q + e] = vv[e];
             }
         }
     }
 }
 
 // The first (bottom-right) diagonal block A[k0:k0+nb, k0:k0+nb], read from the
-// working matrix and factored by one wave.
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void panel_kernel(const float *__restrict__ A, float *__restrict__ Tf, int64_t lda, int64_t k0, int nb,
-                  int32_t *__restrict__ info) {
-    __shared__ __attribute__((aligned(16))) float col[NB];
-    const int lane = threadIdx.x;
-    // Row `lane` of the block straight into registers (16-byte loads, all in flight at once).
-    float c[NB];
-    const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0;
+// working matrix and factored by four waves.
+__global__ __launch_bounds__(kThreads) void panel_kernel(const float *__restrict__ A, float *__restrict__ Tf, int64_t lda,
+                                                        int64_t k0, int nb, int32_t *__restrict__ info) {
+    __shared__ __attribute__((aligned(16))) FactorSmem fs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Row `lane` of the block, this wave's 16 columns (16-byte loads; chunks
+    // past nb are not read: lda is a multiple of 4, so a chunk that starts
+    // below nb ends inside the row).
+    float cw[kFCols];
+    const float *src = A + (k0 + (lane < nb ? lane : 0)) * lda + k0 + kFCols * wave;
 #pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-        // chunks past nb are not read (lda is a multiple of 4, so a chunk
-        // that starts below nb ends inside the row)
-        const float4 v = 4 * q < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-        c[4 * q + 0] = v.x;
-        c[4 * q + 1] = v.y;
-        c[4 * q + 2] = v.z;
-        c[4 * q + 3] = v.w;
+    for (int q = 0; q < kFCols / 4; ++q) {
+        const int c = kFCols * wave + 4 * q;
+        const float4 v = c < nb ? *reinterpret_cast<const float4 *>(src + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        cw[4 * q + 0] = v.x;
+        cw[4 * q + 1] = v.y;
+        cw[4 * q + 2] = v.z;
+        cw[4 * q + 3] = v.w;
     }
-    mask_block_row(c, lane, nb);
-    factor_block(c, nb, k0, Tf, lda, info, col);
+    mask_block_cols(cw, lane, wave, nb);
+    factor_block(cw, wave, nb, k0, Tf, lda, info, fs);
 }
 
 // V = T_bb^-1 of every diagonal block b (one wave each, all blocks at once,
@@ -531,18 +586,18 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
     }
     if (!last) return;
     __syncthreads();  // the next block is complete in LDS
-    if (wave != 0) return;
-    float c[NB];
+    float cw[kFCols];
 #pragma unroll
-    for (int e = 0; e < NB / 4; ++e) {
-        const float4 v = *reinterpret_cast<const float4 *>(&blk[lane][4 * e]);
-        c[4 * e + 0] = v.x;
-        c[4 * e + 1] = v.y;
-        c[4 * e + 2] = v.z;
-        c[4 * e + 3] = v.w;
+    for (int q = 0; q < kFCols / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(&blk[lane][kFCols * wave + 4 * q]);
+        cw[4 * q + 0] = v.x;
+        cw[4 * q + 1] = v.y;
+        cw[4 * q + 2] = v.z;
+        cw[4 * q + 3] = v.w;
     }
-    mask_block_row(c, lane, NB);
-    factor_block(c, NB, nb0, Tf, lda, info, &sm.pi[0][0]);  // P_i^T is dead: its first row is scratch
+    mask_block_cols(cw, lane, wave, NB);
+    // P_i^T is dead: its space holds the factor's panel
+    factor_block(cw, wave, NB, nb0, Tf, lda, info, *reinterpret_cast<FactorSmem *>(&sm.pi[0][0]));
 }
 
 // P = panel T_kk^-T for one 64-row block [r0, r0+64) of the leading rows
@@ -655,7 +710,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     const int64_t nblk = ceil_div(d, NB);
     {
         const int64_t k0 = (nblk - 1) * NB;
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kWave), 0, s, A, Tf, lda, k0, (int)(d - k0), info);
+        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kThreads), 0, s, A, Tf, lda, k0, (int)(d - k0), info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     for (int64_t kb = nblk - 1; kb >= 1; --kb) {
