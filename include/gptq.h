@@ -127,6 +127,11 @@ GPTQ_API gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void
  *            order) of the factorization of H_d was not positive (then U is
  *            not meaningful).  Read it after synchronizing the stream.
  *   ws       scratch of gptq_workspace_bytes(GPTQ_OP_PREPARE, 0, d_in, 0, cfg).
+ * Part of the inverse's assembly runs on a second stream of the library's own
+ * (one per device, created on first use, default priority), forked from and
+ * joined back to `stream` with events, so the call stays ordered on `stream`.
+ * Calls on one device from several host threads share that stream and are
+ * serialized on it.
  */
 GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg,
                               float *U, int32_t *perm, int32_t *info_dev,

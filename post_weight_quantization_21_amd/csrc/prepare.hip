@@ -19,6 +19,9 @@
 #include "common.h"
 #include "quad.h"
 
+#include <algorithm>
+#include <mutex>
+
 namespace gptq {
 namespace {
 
@@ -289,15 +292,15 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(const float *__restrict
     factor_block(cw, wave, nb, k0, Tf, lda, info, fs);
 }
 
-// V = T_bb^-1 of every diagonal block b (one wave each, all blocks at once,
-// after the factorization): lane c holds column c of V.  For i = NB-1..0:
+// V = T_bb^-1 of the diagonal blocks b = kb0, kb0+NB, ... (one wave each, once
+// their factors exist): lane c holds column c of V.  For i = NB-1..0:
 //   V_ic = -(1/t_ii) sum_{m>i} t_im V_mc (c > i), V_ii = 1/t_ii,
 // reading row i of T from LDS with wave-uniform addresses.  V goes into U's
 // diagonal block (zero below the diagonal).
 __global__ __launch_bounds__(kWave) void invert_blocks_kernel(const float *__restrict__ Tf, float *__restrict__ U,
-                                                              int64_t d, int64_t lda) {
+                                                              int64_t d, int64_t lda, int64_t kb0) {
     __shared__ __attribute__((aligned(16))) float tr[NB][NB + 4];
-    const int64_t kb = (int64_t)blockIdx.x * NB;
+    const int64_t kb = kb0 + (int64_t)blockIdx.x * NB;
     const int nb = (int)(d - kb < NB ? d - kb : NB);
     const int lane = threadIdx.x;
     {
@@ -623,45 +626,138 @@ __global__ __launch_bounds__(kFThreads) void p_kernel(const float *__restrict__ 
     }
 }
 
-// Pairwise merge of inverted diagonal blocks at one level (block size sz):
-//   U12 = -U11 T12 U22   for pairs p_first .. p_first+npairs-1 of (ni x nj) blocks,
-// with T12 read from the factor Tf and the product U11 T12 staged in Tw.
-hipError_t merge_level(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t sz, int64_t p_first,
-                       int64_t npairs, int64_t ni, int64_t nj, hipStream_t st) {
-    const int64_t i0 = 2 * p_first * sz, j0 = i0 + ni;
+// Pairwise merges of inverted blocks: inv([[A, B], [0, C]]) = [[A^-1, -A^-1 B C^-1], [0, C^-1]],
+// i.e. U12 = -U11 T12 U22 for the node [i0, i0 + ni + nj) with children
+// [i0, j0 = i0 + ni) and [j0, j0 + nj).  Two products:
+//   merge_right: Tw[i0:j0, j0:] = T12 U22    (needs the right child and T12)
+//   merge_left:  U[i0:j0, j0:]  = -U11 Tw    (needs the left child as well)
+// so the first can run as soon as the factorization has passed j0.  Batched
+// over `npairs` nodes of one level (`stride` apart along the diagonal).
+hipError_t merge_right(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t i0, int64_t ni, int64_t nj,
+                       int64_t npairs, int64_t stride, hipStream_t st) {
+    const int64_t j0 = i0 + ni;
     GemmDesc g;
     g.batch = (int)npairs;
     g.M = ni;
     g.N = nj;
-    g.K = ni;
-    g.A = U + i0 * d + i0;  // U11 (upper triangular, lower part zero)
-    g.lda = d;
-    g.a_upper = 1;
-    g.B = Tf + i0 * lda + j0;  // T12
-    g.ldb = lda;
+    g.K = nj;
+    g.A = Tf + i0 * lda + j0;  // T12
+    g.lda = lda;
+    g.B = U + j0 * d + j0;  // U22 (upper triangular)
+    g.ldb = d;
+    g.b_upper = 1;
     g.C = Tw + i0 * lda + j0;
     g.ldc = lda;
-    g.strideA = 2 * sz * (d + 1);
-    g.strideB = g.strideC = 2 * sz * (lda + 1);
-    hipError_t e = launch_gemm_f32(g, st);
-    if (e != hipSuccess) return e;
+    g.strideA = g.strideC = stride * (lda + 1);
+    g.strideB = stride * (d + 1);
+    return launch_gemm_f32(g, st);
+}
+
+hipError_t merge_left(float *U, const float *Tw, int64_t d, int64_t lda, int64_t i0, int64_t ni, int64_t nj,
+                      int64_t npairs, int64_t stride, hipStream_t st) {
+    const int64_t j0 = i0 + ni;
     GemmDesc h;
     h.batch = (int)npairs;
     h.M = ni;
     h.N = nj;
-    h.K = nj;
-    h.A = Tw + i0 * lda + j0;
-    h.lda = lda;
-    h.B = U + j0 * d + j0;  // U22 (upper triangular)
-    h.ldb = d;
-    h.b_upper = 1;
+    h.K = ni;
+    h.A = U + i0 * d + i0;  // U11 (upper triangular, lower part zero)
+    h.lda = d;
+    h.a_upper = 1;
+    h.B = Tw + i0 * lda + j0;
+    h.ldb = lda;
     h.C = U + i0 * d + j0;
     h.ldc = d;
     h.alpha = -1.0f;
     h.beta = 0.0f;
-    h.strideA = 2 * sz * (lda + 1);
-    h.strideB = h.strideC = 2 * sz * (d + 1);
+    h.strideA = h.strideC = stride * (d + 1);
+    h.strideB = stride * (lda + 1);
     return launch_gemm_f32(h, st);
+}
+
+// Columns per region of the inverse's assembly: once the factorization has
+// passed a region, its diagonal inverses and the merges inside it run on a
+// second stream, beside the rest of the factorization.
+constexpr int64_t kRegion = 512;
+
+// U over the region [x, min(x + kRegion, d)): the diagonal inverses, then the
+// merges level by level (full nodes batched, the last node possibly partial).
+hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st) {
+    const int64_t end = std::min<int64_t>(x + kRegion, d);
+    hipLaunchKernelGGL(invert_blocks_kernel, dim3((unsigned)ceil_div(end - x, NB)), dim3(kWave), 0, st, Tf, U, d, lda, x);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int64_t sz = NB; sz < end - x; sz *= 2) {
+        const int64_t full = (end - x) / (2 * sz);
+        if (full > 0) {
+            if ((e = merge_right(Tf, U, Tw, d, lda, x, sz, sz, full, 2 * sz, st)) != hipSuccess) return e;
+            if ((e = merge_left(U, Tw, d, lda, x, sz, sz, full, 2 * sz, st)) != hipSuccess) return e;
+        }
+        const int64_t i0 = x + 2 * full * sz;
+        const int64_t ni = std::min<int64_t>(sz, end - i0), nj = end - i0 - ni;
+        if (nj > 0) {
+            if ((e = merge_right(Tf, U, Tw, d, lda, i0, ni, nj, 1, 0, st)) != hipSuccess) return e;
+            if ((e = merge_left(U, Tw, d, lda, i0, ni, nj, 1, 0, st)) != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+// The inverse's work that becomes ready once the factorization has passed
+// column x (a multiple of kRegion; x = 0 at the end): the region at x, then,
+// for the nodes of 2, 4, ... regions, the left product of the node starting
+// at x while x is aligned to it, and the right product of the node whose
+// middle is x (its right half, starting at x, is complete by then).
+hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st) {
+    hipError_t e = assemble_region(Tf, U, Tw, d, lda, x, st);
+    if (e != hipSuccess) return e;
+    for (int64_t n = 2 * kRegion; n / 2 < d; n *= 2) {
+        const int64_t half = n / 2;
+        if (x % n == 0) {
+            if (x + half < d)
+                if ((e = merge_left(U, Tw, d, lda, x, half, std::min<int64_t>(half, d - x - half), 1, 0, st)) != hipSuccess)
+                    return e;
+        } else if (x % n == half) {
+            if ((e = merge_right(Tf, U, Tw, d, lda, x - half, half, std::min<int64_t>(half, d - x), 1, 0, st)) !=
+                hipSuccess)
+                return e;
+            break;
+        } else {
+            break;
+        }
+    }
+    return hipSuccess;
+}
+
+// A second stream per device for the inverse's assembly, with the events that
+// fork it from and join it to the caller's stream (default priority).
+struct SideStream {
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+hipError_t side_stream(SideStream *&out) {
+    static SideStream ss[64];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    SideStream &s = ss[dev];
+    if (!s.st) {
+        if ((e = hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    out = &s;
+    return hipSuccess;
+}
+
+// The side stream continues once the caller's stream has reached this point.
+hipError_t fork_to(const SideStream &ss, hipStream_t s) {
+    hipError_t e = hipEventRecord(ss.fork, s);
+    if (e != hipSuccess) return e;
+    return hipStreamWaitEvent(ss.st, ss.fork, 0);
 }
 
 int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
@@ -713,6 +809,8 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
         hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kThreads), 0, s, A, Tf, lda, k0, (int)(d - k0), info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    SideStream *ss = nullptr;
+    if ((e = side_stream(ss)) != hipSuccess) return e;
     for (int64_t kb = nblk - 1; kb >= 1; --kb) {
         const int64_t k0 = kb * NB;
         const int nb = (int)std::min<int64_t>(NB, d - k0);
@@ -726,25 +824,21 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
             hipLaunchKernelGGL(step_kernel<false>, grid, dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb, nt, info);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    // The inverses of the diagonal blocks of T: U's diagonal blocks.
-    hipLaunchKernelGGL(invert_blocks_kernel, dim3((unsigned)nblk), dim3(kWave), 0, s, Tf, U, d, lda);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // U = T^-1: pairwise merges of the inverted diagonal blocks.
-    for (int64_t sz = NB; sz < d; sz *= 2) {
-        const int64_t npairs_total = ceil_div(d, 2 * sz);
-        int64_t full = d / (2 * sz);
-        if (full > 0) {
-            if ((e = merge_level(Tf, U, Tw, d, lda, sz, 0, full, sz, sz, s)) != hipSuccess) return e;
-        }
-        if (npairs_total > full) {
-            const int64_t i0 = 2 * full * sz;
-            const int64_t ni = std::min<int64_t>(sz, d - i0);
-            const int64_t nj = d - i0 - ni;
-            if (nj > 0)
-                if ((e = merge_level(Tf, U, Tw, d, lda, sz, full, 1, ni, nj, s)) != hipSuccess) return e;
+        // T is complete from column k0 - NB on, and in every column from k0
+        // on: the inverse's work at k0 can start beside the next steps.  (The
+        // right products write Tw only in columns >= k0; the steps still to
+        // come stage P^T there in columns < k0.)
+        if (k0 % kRegion == 0) {
+            if ((e = fork_to(*ss, s)) != hipSuccess) return e;
+            if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st)) != hipSuccess) return e;
         }
     }
+    // The rest of U = T^-1 once T is complete, then the caller's stream waits
+    // for all of it.
+    if ((e = fork_to(*ss, s)) != hipSuccess) return e;
+    if ((e = assemble_at(Tf, U, Tw, d, lda, 0, ss->st)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->join, ss->st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
     return hipSuccess;
 }
 
