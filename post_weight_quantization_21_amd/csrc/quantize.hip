@@ -106,6 +106,37 @@ __global__ __launch_bounds__(kThreads) void permute_rows_inplace_kernel(float *_
     }
 }
 
+// inv[perm[k]] = k.
+__global__ __launch_bounds__(kThreads) void invert_perm_kernel(const int32_t *__restrict__ perm, int64_t d_in,
+                                                               int32_t *__restrict__ inv) {
+    const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (k < d_in) inv[clamp_col(perm[k], d_in)] = (int32_t)k;
+}
+
+// codes[r][c] = cp[r][inv[c]]: codes written in processing order (coalesced
+// during the pass) go back to the original column order, one row at a time
+// through LDS (d_in a multiple of 4); reads and writes of HBM are coalesced.
+constexpr int64_t kCodePermMax = 65536;  // d_in limit (64 KB of LDS)
+__global__ __launch_bounds__(kThreads) void unpermute_codes_kernel(const uint8_t *__restrict__ cp,
+                                                                   const int32_t *__restrict__ inv, int64_t d_out,
+                                                                   int64_t d_in, uint8_t *__restrict__ codes) {
+    extern __shared__ uint32_t rowc[];
+    const uint8_t *rb = reinterpret_cast<const uint8_t *>(rowc);
+    const int tid = threadIdx.x;
+    for (int64_t r = blockIdx.x; r < d_out; r += gridDim.x) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(cp + r * d_in);
+        for (int64_t k = tid; k < d_in / 4; k += kThreads) rowc[k] = src[k];
+        __syncthreads();
+        uint32_t *dst = reinterpret_cast<uint32_t *>(codes + r * d_in);
+        for (int64_t k = tid; k < d_in / 4; k += kThreads) {
+            const int64_t c = 4 * k;
+            dst[k] = (uint32_t)rb[clamp_col(inv[c + 0], d_in)] | ((uint32_t)rb[clamp_col(inv[c + 1], d_in)] << 8) |
+                     ((uint32_t)rb[clamp_col(inv[c + 2], d_in)] << 16) | ((uint32_t)rb[clamp_col(inv[c + 3], d_in)] << 24);
+        }
+        __syncthreads();  // rowc is reused by the next row
+    }
+}
+
 // Whether the act-order permutation of W runs in place (else: copy, then gather).
 bool row_perm_inplace(const float *W, int64_t d_in) {
     return d_in <= kRowPermMax && d_in % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
@@ -138,10 +169,11 @@ int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
 }
 
 // Workspace of the column pass: E^T of a whole superblock [S][ldet] (one batch
-// when there is a single superblock) and (act-order with rows too long for the
-// in-place permutation only) a copy of W for the column gather.
+// when there is a single superblock); with act-order, a copy of W for the
+// column gather (rows too long for the in-place permutation only), and the
+// codes in processing order with the inverse permutation.
 struct QuantLayout {
-    size_t et_off, wc_off, total;
+    size_t et_off, wc_off, cp_off, inv_off, total;
     int64_t sc;       // superblock width
     int64_t et_rows;  // rows of E^T kept
 };
@@ -153,7 +185,11 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     l.et_off = 0;
     l.wc_off = align_up((size_t)l.et_rows * (size_t)et_ld(d_out) * sizeof(float), 256);
     const bool copy = c.act_order && d_in > kRowPermMax;  // aligned W assumed (checked at the boundary)
-    l.total = l.wc_off + (copy ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
+    l.cp_off = l.wc_off + (copy ? align_up((size_t)d_out * (size_t)d_in * sizeof(float), 256) : 0);
+    // act-order: codes in processing order and the inverse permutation
+    const bool cperm = c.act_order && d_in <= kCodePermMax;
+    l.inv_off = l.cp_off + (cperm ? align_up((size_t)d_out * (size_t)d_in, 256) : 0);
+    l.total = l.inv_off + (cperm ? align_up((size_t)d_in * sizeof(int32_t), 256) : 0);
     return l;
 }
 
@@ -224,8 +260,17 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(d_in, kThreads)), dim3(kThreads), 0, s, pp, d_in, g, g_idx);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    // With a column order the pass writes the codes in processing order
+    // (coalesced) and one row-wise pass puts them in the original order.
+    const bool cperm = pp && d_in <= kCodePermMax;
+    uint8_t *cdst = cperm ? reinterpret_cast<uint8_t *>(wsb + lay.cp_off) : codes;
+    int32_t *inv = cperm ? reinterpret_cast<int32_t *>(wsb + lay.inv_off) : nullptr;
+    if (cperm) {
+        hipLaunchKernelGGL(invert_perm_kernel, dim3((unsigned)ceil_div(d_in, kThreads)), dim3(kThreads), 0, s, pp, d_in, inv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t ldet = et_ld(d_out);
-    const int vec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15) == 0);
+    const int vec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(cdst) & 15) == 0);
     const int64_t sc = lay.sc;
     const bool deferred = sc < d_in;  // superblocks leave an update for the columns beyond them
     for (int64_t s0 = 0; s0 < d_in; s0 += sc) {
@@ -250,9 +295,9 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             a.ldu = d_in;
             a.Et = Eb;
             a.ldet = ldet;
-            a.codes = codes;
+            a.codes = cdst;
             a.ldc = d_in;
-            a.perm = pp;
+            a.perm = cperm ? nullptr : pp;
             a.scales = scales;
             a.zeros = zeros;
             a.ng = ng;
@@ -274,6 +319,11 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         // every column beyond the superblock, with the superblock's whole E
         if (deferred && (e = lazy_update(W, d_out, d_in, Et, ldet, U, s0, s1 - s0, s1, d_in - s1, s)) != hipSuccess)
             return e;
+    }
+    if (cperm) {
+        const unsigned grid = (unsigned)std::min<int64_t>(d_out, 2048);
+        hipLaunchKernelGGL(unpermute_codes_kernel, dim3(grid), dim3(kThreads), (size_t)d_in, s, cdst, inv, d_out, d_in, codes);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }
