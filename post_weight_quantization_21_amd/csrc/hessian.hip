@@ -327,21 +327,54 @@ __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(const float *__re
     }
 }
 
-// hdiag[i] += 2 * sum_t X[i][t]^2 in fp64.  One workgroup per channel.
+// hdiag[i] += 2 * sum_t X[i][t]^2 in fp64.  One workgroup per channel; rows
+// are read in 16-byte pieces (X and ldx*sizeof(T) are 16-byte aligned at the
+// boundary), four pieces in flight per thread, the ragged end element-wise.
+template <typename T>
+__device__ __forceinline__ float widen_elem(T v) {
+    if constexpr (sizeof(T) == 2) {
+        return __uint_as_float((uint32_t)v << 16);
+    } else {
+        return v;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void diag_f64_kernel(const T *__restrict__ X, int64_t ldx, int64_t n_tok,
                                                             double *__restrict__ hdiag) {
+    constexpr int kPer = 16 / sizeof(T);  // elements per 16-byte piece
+    constexpr int kUnroll = 4;
     const int64_t i = blockIdx.x;
     const T *row = X + i * ldx;
+    const int64_t npieces = n_tok / kPer;
     double s = 0.0;
-    for (int64_t t = threadIdx.x; t < n_tok; t += kThreads) {
-        float v;
-        if constexpr (sizeof(T) == 2) {
-            v = __uint_as_float((uint32_t)row[t] << 16);
-        } else {
-            v = row[t];
+    int64_t p = threadIdx.x;
+    for (; p + (kUnroll - 1) * kThreads < npieces; p += kUnroll * kThreads) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = *reinterpret_cast<const uint4 *>(row + (p + u * kThreads) * kPer);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const T *e = reinterpret_cast<const T *>(&v[u]);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const double x = (double)widen_elem<T>(e[k]);
+                s = fma(x, x, s);
+            }
         }
-        s += (double)v * (double)v;
+    }
+    for (; p < npieces; p += kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(row + p * kPer);
+        const T *e = reinterpret_cast<const T *>(&v);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const double x = (double)widen_elem<T>(e[k]);
+            s = fma(x, x, s);
+        }
+    }
+    for (int64_t t = npieces * kPer + threadIdx.x; t < n_tok; t += kThreads) {
+        const double x = (double)widen_elem<T>(row[t]);
+        s = fma(x, x, s);
     }
     __shared__ double red[kThreads];
     red[threadIdx.x] = s;

@@ -29,32 +29,38 @@ constexpr int NB = 64;  // diagonal block edge
 constexpr int kThreads = 256;
 
 // perm[rank] = column; rank by descending key, ties by lower index (stable).
-// NaN keys sort last, so the ranks always form a permutation.  Each thread
-// ranks one key against all d keys, which pass through LDS in chunks (every
-// lane reads the same key: a broadcast).
+// NaN keys sort last, so the ranks always form a permutation.
 __device__ __forceinline__ double order_key(const double *hdiag, const float *H, int64_t d, int64_t i) {
     const double k = hdiag ? hdiag[i] : (double)H[i * d + i];
     return k == k ? k : -__builtin_inf();
 }
 
-constexpr int kKeyChunk = 2048;
-__global__ __launch_bounds__(kThreads) void order_kernel(const double *__restrict__ hdiag, const float *__restrict__ H,
-                                                         int64_t d, int32_t *__restrict__ perm) {
-    __shared__ double keys[kKeyChunk];
+// Ranks over slices of kKeySlice keys: workgroup (x, y) ranks keys
+// 256x .. 256x+255 against the keys of slice y (staged in LDS; every lane reads
+// the same key, a broadcast) and adds the partial counts to rank[] (zeroed
+// beforehand); scatter_rank_kernel then writes perm.
+constexpr int kKeySlice = 1024;
+__global__ __launch_bounds__(kThreads) void rank_kernel(const double *__restrict__ hdiag, const float *__restrict__ H,
+                                                        int64_t d, int32_t *__restrict__ rank) {
+    __shared__ double keys[kKeySlice];
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.y * kKeySlice;
+    const int n = (int)(d - j0 < kKeySlice ? d - j0 : kKeySlice);
+    for (int jj = threadIdx.x; jj < n; jj += kThreads) keys[jj] = order_key(hdiag, H, d, j0 + jj);
     const double ki = i < d ? order_key(hdiag, H, d, i) : 0.0;
-    int64_t rank = 0;
-    for (int64_t j0 = 0; j0 < d; j0 += kKeyChunk) {
-        const int n = (int)(d - j0 < kKeyChunk ? d - j0 : kKeyChunk);
-        __syncthreads();  // the previous chunk is consumed
-        for (int jj = threadIdx.x; jj < n; jj += kThreads) keys[jj] = order_key(hdiag, H, d, j0 + jj);
-        __syncthreads();
-        for (int jj = 0; jj < n; ++jj) {
-            const double kj = keys[jj];
-            rank += (kj > ki) || (kj == ki && j0 + jj < i);
-        }
+    __syncthreads();
+    int32_t r = 0;
+    for (int jj = 0; jj < n; ++jj) {
+        const double kj = keys[jj];
+        r += (kj > ki) || (kj == ki && j0 + jj < i);
     }
-    if (i < d) perm[rank] = (int32_t)i;
+    if (i < d && r > 0) atomicAdd(&rank[i], r);
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_rank_kernel(const int32_t *__restrict__ rank, int64_t d,
+                                                                int32_t *__restrict__ perm) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < d) perm[rank[i]] = (int32_t)i;
 }
 
 // A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper triangle.
@@ -783,7 +789,14 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, s, info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (act_order) {
-        hipLaunchKernelGGL(order_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, hdiag, H, d, perm);
+        // the ranks are counted in the working matrix's first d entries (free until the gather below)
+        int32_t *rank = reinterpret_cast<int32_t *>(A);
+        hipLaunchKernelGGL(fill_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, A, d, 0.0f);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(d, kThreads), (unsigned)ceil_div(d, kKeySlice)), dim3(kThreads),
+                           0, s, hdiag, H, d, rank);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(scatter_rank_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, rank, d, perm);
     } else if (perm) {
         hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, perm, d);
     }
