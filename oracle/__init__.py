@@ -20,7 +20,10 @@ Steps, in the pages' order:
    is the literal elimination sequence H_F^-1 of page "PTQ 权重量化：从 GPTQ 到
    AWQ" (GPTQ section) and pins U in the tests.
 5. ``gptq``: the greedy column pass with error feedback (C, ``gptq_oracle.c``),
-   unblocked by default, or with lazy batches of B columns.
+   unblocked by default, or with lazy batches of B columns; group grids fitted
+   as the pass reaches them (dynamic), from the original W before the pass
+   (static), or one grid for the whole matrix (tensor) -- page "LLM 量化方法原理
+   与实现详解", §2.3 granularity.
 6. ``layer_loss``: ||W X - W_hat X||_F^2 = 1/2 sum_r D_r H D_r^T with D = W_hat - W
    and the undamped H (page "LLM 量化方法原理与实现详解", §4.1 objective).
 
@@ -49,6 +52,8 @@ def _lib():
         lib.oracle_rtn.restype = i32
         lib.oracle_gptq_pass.argtypes = [i64, i64, vp, i64, vp, i32, i32, i64, i64, vp, vp, vp, vp, vp]
         lib.oracle_gptq_pass.restype = i32
+        lib.oracle_gptq_pass_fixed.argtypes = [i64, i64, vp, i64, vp, i32, i32, vp, i64, vp, vp, i64, vp, vp, vp]
+        lib.oracle_gptq_pass_fixed.restype = i32
         lib.oracle_hessian_entries.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp]
         lib.oracle_hessian_entries.restype = i32
         _LIB = lib
@@ -165,17 +170,55 @@ def gptq_pass(W: np.ndarray, U: np.ndarray, bits: int, sym: bool, group: int, bl
     return dict(codes=codes, scales=scales, zeros=zeros, w_at_q=w_at_q, err=err)
 
 
+def gptq_pass_fixed(W: np.ndarray, U: np.ndarray, bits: int, sym: bool, col_grid, gscales, gzeros,
+                    block: int = 0):
+    """Column pass on grids fixed beforehand: processing column j uses grid col_grid[j] of its row."""
+    W64 = np.ascontiguousarray(W, dtype=np.float64)
+    U64 = np.ascontiguousarray(U, dtype=np.float64)
+    n, d = W64.shape
+    cg = np.ascontiguousarray(col_grid, dtype=np.int64)
+    gs = np.ascontiguousarray(gscales, dtype=np.float32)
+    gz = np.ascontiguousarray(gzeros, dtype=np.float32)
+    if cg.shape != (d,) or gs.shape != gz.shape or gs.shape[0] != n:
+        raise ValueError("gptq_pass_fixed: shape mismatch")
+    codes = np.zeros((n, d), dtype=np.uint8)
+    w_at_q = np.zeros((n, d), dtype=np.float64)
+    err = np.zeros((n, d), dtype=np.float64)
+    st = _lib().oracle_gptq_pass_fixed(n, d, _p(W64), d, _p(U64), bits, int(bool(sym)), _p(cg), gs.shape[1],
+                                       _p(gs), _p(gz), block, _p(codes), _p(w_at_q), _p(err))
+    if st != 0:
+        raise ValueError(f"oracle_gptq_pass_fixed failed ({st})")
+    return dict(codes=codes, w_at_q=w_at_q, err=err)
+
+
+def tensor_grid(W: np.ndarray, bits: int, sym: bool):
+    """The one grid of a whole matrix: the per-row grid of W flattened into a single row."""
+    r = rtn(np.reshape(np.asarray(W, dtype=np.float32), (1, -1)), bits, sym, 0)
+    return float(r["scales"][0, 0]), float(r["zeros"][0, 0])
+
+
 def gptq(W: np.ndarray, H: np.ndarray, bits: int, sym: bool, group: int, damp_rel: float,
-         act_order: bool = False, block: int = 0, rows=None, hdiag=None):
+         act_order: bool = False, block: int = 0, rows=None, hdiag=None, grid: str = "dynamic"):
     """Whole-layer GPTQ.  Codes are returned in the original column order.
 
     ``rows`` (optional) selects the output rows to quantize: rows are
-    independent given U, so a sample of rows gives exact per-row results.
-    ``hdiag`` (optional) is the fp64 diag(H) used as the ordering key.
+    independent given U (and given the grids, which are fitted on the whole
+    matrix first when ``grid`` is "tensor"), so a sample of rows gives exact
+    per-row results.  ``hdiag`` (optional) is the fp64 diag(H) used as the
+    ordering key.  ``grid``: "dynamic" fits each group when the pass reaches
+    it (groups in processing order); "static" fits every group of the
+    original W before the pass (groups in original column order, so
+    g_idx[c] = c // group under act-order too); "tensor" fits one grid on the
+    whole original W (group must be 0; scales/zeros [rows][1] all equal).
     """
     W = np.asarray(W)
     d = W.shape[1]
     g = group if group > 0 else d
+    if grid not in ("dynamic", "static", "tensor"):
+        raise ValueError(f"unknown grid {grid!r}")
+    if grid == "tensor" and group != 0:
+        raise ValueError("a per-tensor grid has no groups (group must be 0)")
+    ts = tensor_grid(W, bits, sym) if grid == "tensor" else None
     if rows is not None:
         W = W[np.asarray(rows)]
     perm = np.arange(d, dtype=np.int32)
@@ -185,19 +228,45 @@ def gptq(W: np.ndarray, H: np.ndarray, bits: int, sym: bool, group: int, damp_re
         Hp = H[np.ix_(perm, perm)]
     Hd = damp(Hp, damp_rel)
     U = inv_chol_upper(Hd)
-    out = gptq_pass(W[:, perm], U, bits, sym, group, block)
+    g_idx = np.empty(d, dtype=np.int32)
+    if grid == "dynamic":
+        out = gptq_pass(W[:, perm], U, bits, sym, group, block)
+        g_idx[perm] = np.arange(d, dtype=np.int32) // g
+    else:
+        n = W.shape[0]
+        if grid == "static":
+            r = rtn(W, bits, sym, group)
+            gs, gz = r["scales"], r["zeros"]
+            col_grid = perm.astype(np.int64) // g
+        else:
+            gs = np.full((n, 1), ts[0], dtype=np.float32)
+            gz = np.full((n, 1), ts[1], dtype=np.float32)
+            col_grid = np.zeros(d, dtype=np.int64)
+        out = gptq_pass_fixed(W[:, perm], U, bits, sym, col_grid, gs, gz, block)
+        out.update(scales=gs, zeros=gz)
+        g_idx[:] = np.arange(d, dtype=np.int32) // g
     codes = np.empty_like(out["codes"])
     codes[:, perm] = out["codes"]
-    g_idx = np.empty(d, dtype=np.int32)
-    g_idx[perm] = np.arange(d, dtype=np.int32) // g
     out.update(codes_perm=out["codes"], codes=codes, g_idx=g_idx, perm=perm, U=U, Hd=Hd)
     return out
 
 
-def rtn(W: np.ndarray, bits: int, sym: bool, group: int):
-    """Round-to-nearest baseline with the same grids as the column pass."""
+def rtn(W: np.ndarray, bits: int, sym: bool, group: int, grid: str = "dynamic"):
+    """Round-to-nearest baseline with the same grids as the column pass.
+
+    RTN fits every grid on the original W, so "static" is "dynamic" here;
+    "tensor" rounds on the one grid of the whole matrix (scales [d_out][1]).
+    """
     W32 = np.ascontiguousarray(W, dtype=np.float32)
     n, d = W32.shape
+    if grid == "tensor":
+        if group != 0:
+            raise ValueError("a per-tensor grid has no groups (group must be 0)")
+        r = rtn(np.reshape(W32, (1, n * d)), bits, sym, 0)
+        return dict(codes=np.reshape(r["codes"], (n, d)), scales=np.full((n, 1), r["scales"][0, 0], dtype=np.float32),
+                    zeros=np.full((n, 1), r["zeros"][0, 0], dtype=np.float32))
+    if grid not in ("dynamic", "static"):
+        raise ValueError(f"unknown grid {grid!r}")
     g = group if group > 0 else d
     codes = np.zeros((n, d), dtype=np.uint8)
     scales = np.zeros((n, d // g), dtype=np.float32)

@@ -30,6 +30,8 @@
  *  - rint rounds half to even (the pages' code uses torch.round);
  *  - a group's scale is fitted when its first column is reached, from the
  *    weights as they are at that moment (after earlier error feedback);
+ *    the static variant fits every group from the original weights before
+ *    the pass, and the per-tensor variant one grid from the whole matrix;
  *  - update sign: remaining weights -= (w - w_hat) / U[j][j] * U[j][k], where
  *    U is the upper Cholesky factor of the damped inverse Hessian
  *    (U^T U = H^-1), i.e. the scaled row of H_F^-1 on the remaining set F.
@@ -202,6 +204,65 @@ int oracle_gptq_pass(int64_t n_rows, int64_t d, const double *W, int64_t ldw, co
                 }
             }
             c0 = c1;
+        }
+        free(w);
+        free(e);
+    }
+    return status;
+}
+
+/*
+ * Column pass on grids fixed before it starts (page "LLM 量化方法原理与实现详解",
+ * §2.3 granularity: static groups, whose scales come from the original
+ * weights, and a single grid for the whole tensor).  The updates are those of
+ * oracle_gptq_pass; only the grid of each column differs: processing column j
+ * of row r is quantized on grid col_grid[j] of that row, i.e. on
+ * (gscales[r][col_grid[j]], gzeros[r][col_grid[j]]), and no grid is refitted
+ * during the pass.  Lazy batches (block > 0) are plain runs of `block`
+ * columns: with no refit, no batch has to be cut short.
+ *   col_grid [d]              grid index of each processing column, in [0, ngrid)
+ *   gscales, gzeros [n_rows][ngrid]
+ * Outputs as in oracle_gptq_pass (codes, w_at_q, err; the latter two may be NULL).
+ */
+int oracle_gptq_pass_fixed(int64_t n_rows, int64_t d, const double *W, int64_t ldw, const double *U,
+                           int bits, int sym, const int64_t *col_grid, int64_t ngrid, const float *gscales,
+                           const float *gzeros, int64_t block, uint8_t *codes, double *w_at_q, double *err)
+{
+    if (bits < 2 || bits > 8 || block < 0 || ngrid < 1) return -1;
+    for (int64_t j = 0; j < d; ++j)
+        if (col_grid[j] < 0 || col_grid[j] >= ngrid) return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        double *w = (double *)malloc(sizeof(double) * (size_t)d);
+        double *e = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!w || !e) {
+            status = -2;
+            free(w);
+            free(e);
+            continue;
+        }
+        memcpy(w, W + r * ldw, sizeof(double) * (size_t)d);
+        int64_t step = block > 0 ? block : d;
+        for (int64_t c0 = 0; c0 < d; c0 += step) {
+            int64_t c1 = c0 + step < d ? c0 + step : d;
+            for (int64_t j = c0; j < c1; ++j) {
+                float s = gscales[r * ngrid + col_grid[j]];
+                float z = gzeros[r * ngrid + col_grid[j]];
+                float code = code_of((float)w[j], s, z, bits, sym);
+                double wh = (double)dequant(code, s, z);
+                double ej = (w[j] - wh) / U[j * d + j];
+                codes[r * d + j] = (uint8_t)code;
+                if (w_at_q) w_at_q[r * d + j] = w[j];
+                e[j] = ej;
+                if (err) err[r * d + j] = ej;
+                for (int64_t k = j + 1; k < c1; ++k) w[k] -= ej * U[j * d + k];
+            }
+            for (int64_t k = c1; k < d; ++k) {
+                double acc = 0.0;
+                for (int64_t j = c0; j < c1; ++j) acc += e[j] * U[j * d + k];
+                w[k] -= acc;
+            }
         }
         free(w);
         free(e);
