@@ -76,6 +76,21 @@ typedef enum {
     GPTQ_OP_LOSS = 3
 } gptq_op;
 
+/*
+ * When the grids are fitted (page "LLM 量化方法原理与实现详解", §2.3 names the
+ * granularities; when they are fitted is a choice of the quantizer):
+ *   GPTQ_GRID_DYNAMIC  each group's grid when the pass reaches the group's
+ *                      first column, from the weights as they are then;
+ *                      groups follow the processing order.
+ *   GPTQ_GRID_STATIC   every group's grid from the ORIGINAL weights, before
+ *                      the pass; groups keep the original column order (under
+ *                      act-order too), each column uses its own group's grid.
+ *   GPTQ_GRID_TENSOR   one grid for the whole matrix, fitted on the original
+ *                      weights; group_size must be 0; scales and zeros keep the
+ *                      [d_out][1] layout, every row holding the same values.
+ */
+typedef enum { GPTQ_GRID_DYNAMIC = 0, GPTQ_GRID_STATIC = 1, GPTQ_GRID_TENSOR = 2 } gptq_grid;
+
 typedef struct {
     int32_t bits;       /* 2..8 */
     int32_t symmetric;  /* 1: symmetric grid, 0: asymmetric grid (see above) */
@@ -83,6 +98,7 @@ typedef struct {
     int32_t block_size; /* lazy batch width B: 32, 64 or 128 */
     float damp_rel;     /* lambda = damp_rel * mean(diag H), >= 0 */
     int32_t act_order;  /* 1: process columns by descending diag(H) */
+    int32_t grid;       /* gptq_grid: when the grids are fitted */
 } gptq_config;
 
 /*
@@ -142,21 +158,25 @@ GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int6
  * (page "PTQ 权重量化：从 GPTQ 到 AWQ", GPTQ section: update formula and the
  * 128-column lazy batch; page "量化经典" §二 steps 3-4).  For each column j in
  * processing order, for every row: fit the group grid when j starts a group
- * (from the current weights), quantize w_j, e = (w_j - w_hat_j) / U[j][j],
- * and w_k -= e * U[j][k] for the later columns -- inside the current batch at
- * once, for columns beyond it when the batch of block_size columns ends.
+ * (from the current weights; with cfg->grid STATIC or TENSOR all grids are
+ * fitted on the original W before the pass instead), quantize w_j,
+ * e = (w_j - w_hat_j) / U[j][j], and w_k -= e * U[j][k] for the later
+ * columns -- inside the current batch at once, for columns beyond it when the
+ * batch of block_size columns ends.
  *
  *   W       [d_out][d_in] fp32, in/out (working storage).  On entry the
  *           layer in ORIGINAL column order.  On return W[r][k] holds, for
  *           processing position k, the weight's value when it was quantized.
  *   U, perm from gptq_prepare_hinv (perm may be NULL when !cfg->act_order).
  *   codes   [d_out][d_in] u8 out, ORIGINAL column order.
- *   scales, zeros [d_out][n_groups] fp32 out, groups in processing order.
+ *   scales, zeros [d_out][n_groups] fp32 out, groups in processing order
+ *           (DYNAMIC) or in original column order (STATIC); [d_out][1] (TENSOR).
  *   g_idx   [d_in] int32 out or NULL: group of each ORIGINAL column.
  *   ws      scratch of gptq_workspace_bytes(GPTQ_OP_QUANTIZE, d_out, d_in, 0, cfg).
  * GPTQ_ERR_UNSUPPORTED when block_size is not 32/64/128, or when group_size
  * is neither 0, nor a divisor of block_size in {32, 64, 128}, nor a multiple
- * of block_size.
+ * of block_size (group_size 0 counts as d_in).  GPTQ_ERR_INVALID_ARG for an
+ * unknown grid, or TENSOR with group_size != 0.
  */
 GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
                                 const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros,
@@ -166,7 +186,9 @@ GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, 
  * Round-to-nearest baseline (page "PTQ 权重量化：从 GPTQ 到 AWQ", section on
  * RTN's limits: every weight rounded on its own): same grids as above fitted
  * on the original W, no error feedback, natural column order.  Uses bits,
- * symmetric and group_size of cfg.
+ * symmetric, group_size and grid of cfg (DYNAMIC and STATIC are the same
+ * here; TENSOR rounds on the one grid of the whole matrix, scales and zeros
+ * [d_out][1]).
  */
 GPTQ_API gptq_status gptq_rtn_quantize(const float *W, int64_t d_out, int64_t d_in, const gptq_config *cfg,
                               uint8_t *codes, float *scales, float *zeros, hipStream_t stream);

@@ -30,6 +30,10 @@ gptq_status check_cfg(const gptq_config *c, int64_t d_in, const char *fn) {
     if (c->group_size < 0 || (c->group_size > 0 && d_in % c->group_size != 0))
         return fail(GPTQ_ERR_INVALID_ARG, "%s: group_size=%d does not divide d_in=%lld", fn, c->group_size, (long long)d_in);
     if (!(c->damp_rel >= 0.0f)) return fail(GPTQ_ERR_INVALID_ARG, "%s: damp_rel must be >= 0", fn);
+    if (c->grid != GPTQ_GRID_DYNAMIC && c->grid != GPTQ_GRID_STATIC && c->grid != GPTQ_GRID_TENSOR)
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown grid %d", fn, c->grid);
+    if (c->grid == GPTQ_GRID_TENSOR && c->group_size != 0)
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: a per-tensor grid needs group_size 0", fn);
     return GPTQ_OK;
 }
 

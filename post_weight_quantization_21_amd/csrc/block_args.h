@@ -15,7 +15,10 @@ struct BlockArgs {
     int64_t ldet;
     uint8_t *codes;  // [d_out][ldc], original column order
     int64_t ldc;
-    const int32_t *perm;  // processing position -> original column, or NULL
+    const int32_t *perm;  // processing position -> original column (code destination), or NULL
+    // grids fitted before the pass, per column: processing position -> original
+    // column, whose group's stored grid is used (the grid-per-column kernels only)
+    const int32_t *gperm;
     float *scales, *zeros;
     int64_t ng, g;
     int bits, sym, vec;
@@ -23,9 +26,20 @@ struct BlockArgs {
 
 constexpr int kBlockThreads = 256;
 
-hipError_t launch_block_32(const BlockArgs &a, int gt, hipStream_t s);
-hipError_t launch_block_64(const BlockArgs &a, int gt, hipStream_t s);
-hipError_t launch_block_128(const BlockArgs &a, int gt, hipStream_t s);
+// How the batch kernel gets its grids:
+//   kFitGrids    fitted from the current weights at each group start (GT > 0),
+//                or read from scales/zeros at the batch start (GT == 0: the
+//                group spans whole batches and was fitted before the batch);
+//   kStoredGrids read from scales/zeros (fitted before the pass) at each
+//                group start (GT > 0) or at the batch start (GT == 0);
+//   kColumnGrids read from scales/zeros for every column, group gperm[c] / g
+//                (groups in original column order while columns are processed
+//                in another order).
+enum GridSource { kFitGrids = 0, kStoredGrids = 1, kColumnGrids = 2 };
+
+hipError_t launch_block_32(const BlockArgs &a, int gt, int src, hipStream_t s);
+hipError_t launch_block_64(const BlockArgs &a, int gt, int src, hipStream_t s);
+hipError_t launch_block_128(const BlockArgs &a, int gt, int src, hipStream_t s);
 
 // Column indices read from a permutation are clamped into [0, n) so that a
 // malformed permutation can only give wrong results, never a wild access.

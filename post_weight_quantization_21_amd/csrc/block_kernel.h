@@ -5,8 +5,8 @@
 // Four lanes per output row.  The row's BT weights of the batch stay in
 // registers (BT/4 per lane) for the whole batch; the BT x BT block of U sits
 // in LDS.  For each column j:
-// fit the group grid when j starts a group (GT > 0: from the current
-// weights; GT == 0: the grid was fitted before the batch), quantize, form
+// take the column's grid (SRC, see GridSource: fitted from the current
+// weights at a group start, or read from the grids fitted before), quantize, form
 // e = (w_j - w_hat_j) / U[j][j], update w_k -= e U[j][k] for the batch's later
 // columns, and store -e into E^T for the trailing matrix-core update.  The
 // unrolled column loop is branch-free: the LDS copy of U is zero on and below
@@ -28,8 +28,9 @@ constexpr int kRowLanes = 4;  // lanes per output row
 // broadcasts the weight to its quad (DPP), all four lanes quantize it (same
 // result), and each lane pushes the error onto its own later columns.
 // NT threads per workgroup (NT / 4 rows).
-template <int BT, int GT, int NT>
+template <int BT, int GT, int NT, int SRC>
 __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
+    static_assert(SRC != kColumnGrids || GT == 0, "per-column grids take no group tile");
     constexpr int CPL = BT / kRowLanes;
     constexpr int kRows = NT / kRowLanes;
     // The B x B block of U, strictly upper part (zero on and below the
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     __shared__ __attribute__((aligned(16))) float ut[BT][NP][kRowLanes][4];
     __shared__ float inv_d[BT];
     __shared__ int32_t pcol[BT];
+    __shared__ int32_t gcol[SRC == kColumnGrids ? BT : 1];  // group of each column (per-column grids)
     const int tid = threadIdx.x;
     const int nc = a.ncols;
     const int q = tid & (kRowLanes - 1);
@@ -64,6 +66,25 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             const int64_t k = a.c0 + (c < nc ? c : 0);
             const uint32_t v = (uint32_t)clamp_col(pp[k], a.ldc);
             pc[u] = (int32_t)((v & mp) | ((uint32_t)(a.c0 + c) & ~mp));
+        }
+    }
+    int32_t gc[SRC == kColumnGrids ? kPc : 1];
+    if constexpr (SRC == kColumnGrids) {
+#pragma unroll
+        for (int u = 0; u < kPc; ++u) {
+            const int c = tid + u * NT;
+            gc[u] = (int32_t)(clamp_col(a.gperm[a.c0 + (c < nc ? c : nc - 1)], a.ldc) / a.g);
+        }
+    }
+    const int64_t rr = active ? r : a.d_out - 1;  // a row whose grids exist
+    constexpr int NG = GT > 0 ? BT / GT : 1;
+    float fs[NG], fz[NG];  // grids of the batch's groups, fitted before the pass
+    if constexpr (SRC == kStoredGrids && GT > 0) {
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            const int64_t gi = (a.c0 + (gg * GT < nc ? gg * GT : 0)) / a.g;
+            fs[gg] = a.scales[rr * a.ng + gi];
+            fz[gg] = a.zeros[rr * a.ng + gi];
         }
     }
     float w[CPL];
@@ -142,17 +163,33 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     for (int u = 0; u < kPc; ++u) {
         const int c = tid + u * NT;
         if (c < BT) pcol[c] = pc[u];  // every entry 0..BT-1 is written
+        if constexpr (SRC == kColumnGrids)
+            if (c < BT) gcol[c] = gc[u];
     }
     __syncthreads();
 
     Grid gr = grid_make(0.0f, 0.0f, 0.0f, a.bits, a.sym);
-    if constexpr (GT == 0) {
+    if constexpr (GT == 0 && SRC != kColumnGrids) {
         if (active) {
             const int64_t gi = a.c0 / a.g;
             gr = grid_from_stored(a.scales[r * a.ng + gi], a.zeros[r * a.ng + gi], a.bits, a.sym);
         }
     }
-    constexpr int NG = GT > 0 ? BT / GT : 1;
+    // Per-column grids: the stored scale and zero of column j's group are read
+    // kPf columns ahead into a ring of kPf + 1 slots.
+    constexpr int kPf = 2;
+    float cs[kPf + 1], cz[kPf + 1];
+    const float *srow = a.scales + rr * a.ng;
+    const float *zrow = a.zeros + rr * a.ng;
+    auto load_grid = [&](int j, int slot) {
+        const int gi = gcol[j];
+        cs[slot] = srow[gi];
+        cz[slot] = zrow[gi];
+    };
+    if constexpr (SRC == kColumnGrids) {
+#pragma unroll
+        for (int j = 0; j < kPf; ++j) load_grid(j, j);
+    }
     float g_s[NG], g_z[NG];
     uint32_t cw[(CPL + 3) / 4];
 #pragma unroll
@@ -175,9 +212,15 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         const int oq = j & (kRowLanes - 1), ot = j / kRowLanes;
         const int cur = j & 1;
         if (j + 1 < BT) load_row(j + 1, urow[cur ^ 1], idn[cur ^ 1]);
-        // the reads stay here, a column ahead of their use
+        if constexpr (SRC == kColumnGrids)
+            if (j + kPf < BT) load_grid(j + kPf, (j + kPf) % (kPf + 1));
+        // the reads stay here, ahead of their use
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (GT > 0) {
+        if constexpr (SRC == kColumnGrids) {
+            gr = grid_from_stored(cs[j % (kPf + 1)], cz[j % (kPf + 1)], a.bits, a.sym);
+        } else if constexpr (SRC == kStoredGrids && GT > 0) {
+            if (j % GT == 0) gr = grid_from_stored(fs[j / GT], fz[j / GT], a.bits, a.sym);
+        } else if constexpr (GT > 0) {
             if (j % GT == 0) {
                 float amax = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
@@ -216,7 +259,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     }
 
     if (!active) return;
-    if constexpr (GT > 0) {
+    if constexpr (SRC == kFitGrids && GT > 0) {
         if (q == 0) {
 #pragma unroll
             for (int g = 0; g < NG; ++g)
@@ -239,41 +282,47 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     }
 }
 
+template <int BT, int GT, int NT>
+hipError_t launch_block_gt(const BlockArgs &a, int src, unsigned grid, hipStream_t s) {
+    if (src == kStoredGrids)
+        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kStoredGrids>), dim3(grid), dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kFitGrids>), dim3(grid), dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int BT, int NT>
-hipError_t launch_block_nt(const BlockArgs &a, int gt, hipStream_t s) {
+hipError_t launch_block_nt(const BlockArgs &a, int gt, int src, hipStream_t s) {
     const unsigned grid = (unsigned)ceil_div(a.d_out, NT / kRowLanes);
+    if (src == kColumnGrids) {
+        if (!a.gperm || gt != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kColumnGrids>), dim3(grid), dim3(NT), 0, s, a);
+        return hipGetLastError();
+    }
     switch (gt) {
-    case 0:
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT>), dim3(grid), dim3(NT), 0, s, a);
-        break;
+    case 0:  // the grid is read at the batch start either way
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kFitGrids>), dim3(grid), dim3(NT), 0, s, a);
+        return hipGetLastError();
     case 32:
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 32, NT>), dim3(grid), dim3(NT), 0, s, a);
-        break;
+        return launch_block_gt<BT, 32, NT>(a, src, grid, s);
     case 64:
-        if constexpr (BT >= 64) {
-            hipLaunchKernelGGL((gptq_block_kernel<BT, 64, NT>), dim3(grid), dim3(NT), 0, s, a);
-            break;
-        }
+        if constexpr (BT >= 64) return launch_block_gt<BT, 64, NT>(a, src, grid, s);
         return hipErrorInvalidValue;
     case 128:
-        if constexpr (BT >= 128) {
-            hipLaunchKernelGGL((gptq_block_kernel<BT, 128, NT>), dim3(grid), dim3(NT), 0, s, a);
-            break;
-        }
+        if constexpr (BT >= 128) return launch_block_gt<BT, 128, NT>(a, src, grid, s);
         return hipErrorInvalidValue;
     default:
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 // Four-wave workgroups (64 rows).  One-wave workgroups (16 rows), which
 // spread a small layer over more CUs, measured slower: each row's column chain,
 // not the CU count, sets the time.
 template <int BT>
-hipError_t launch_block_bt(const BlockArgs &a, int gt, hipStream_t s) {
+hipError_t launch_block_bt(const BlockArgs &a, int gt, int src, hipStream_t s) {
     if (!a.Et || !a.W || !a.U || !a.codes) return hipErrorInvalidValue;
-    return launch_block_nt<BT, kBlockThreads>(a, gt, s);
+    return launch_block_nt<BT, kBlockThreads>(a, gt, src, s);
 }
 
 }  // namespace gptq

@@ -26,39 +26,137 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One wave per (row, group): fit the group's grid from W (current values);
-// optionally write the codes (round-to-nearest).  Groups g_first .. g_first+g_count-1.
+// One wave per (row, group): fit the group's grid from W (current values),
+// or (fit == 0) take the grid stored in scales/zeros; optionally write the
+// codes (round-to-nearest).  Groups g_first .. g_first+g_count-1.
 __global__ __launch_bounds__(kThreads) void rtn_kernel(const float *__restrict__ W, int64_t ldw, int64_t d_out,
                                                        int64_t g, int64_t ng, int64_t g_first, int64_t g_count,
-                                                       int bits, int sym, uint8_t *__restrict__ codes, int64_t ldc,
-                                                       float *__restrict__ scales, float *__restrict__ zeros) {
+                                                       int bits, int sym, int fit, uint8_t *__restrict__ codes,
+                                                       int64_t ldc, float *__restrict__ scales, float *__restrict__ zeros) {
     const int64_t wid = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kWave;
     const int lane = threadIdx.x % kWave;
     if (wid >= d_out * g_count) return;
     const int64_t r = wid / g_count, gi = g_first + wid % g_count;
     const float *src = W + r * ldw + gi * g;
-    float lo = 0.0f, hi = 0.0f, amax = 0.0f;
-    for (int64_t k = lane; k < g; k += kWave) {
-        const float v = src[k];
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-        amax = fmaxf(amax, fabsf(v));
-    }
+    Grid gr;
+    if (fit) {
+        float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+        for (int64_t k = lane; k < g; k += kWave) {
+            const float v = src[k];
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+            amax = fmaxf(amax, fabsf(v));
+        }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, off));
-        hi = fmaxf(hi, __shfl_xor(hi, off));
-        amax = fmaxf(amax, __shfl_xor(amax, off));
-    }
-    const Grid gr = grid_make(amax, lo, hi, bits, sym);
-    if (lane == 0) {
-        scales[r * ng + gi] = gr.s;
-        zeros[r * ng + gi] = gr.zero;
+        for (int off = 32; off > 0; off >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+            amax = fmaxf(amax, __shfl_xor(amax, off));
+        }
+        gr = grid_make(amax, lo, hi, bits, sym);
+        if (lane == 0) {
+            scales[r * ng + gi] = gr.s;
+            zeros[r * ng + gi] = gr.zero;
+        }
+    } else {
+        gr = grid_from_stored(scales[r * ng + gi], zeros[r * ng + gi], bits, sym);
     }
     if (codes) {
         uint8_t *dst = codes + r * ldc + gi * g;
         for (int64_t k = lane; k < g; k += kWave) dst[k] = (uint8_t)grid_code(src[k], gr);
     }
+}
+
+// The one grid of a whole matrix (page "LLM 量化方法原理与实现详解", §2.3:
+// one scale per tensor), in two kernels that need no scratch: the outputs
+// scales and zeros ([d_out][1]) first hold partial ranges.  Block b reduces its
+// grid-stride share of W to hi = max(max x, 0) and nlo = max(-min x, 0)
+// (exact, so the order does not matter) into scales[b] and zeros[b].
+__global__ __launch_bounds__(kThreads) void tensor_range_kernel(const float *__restrict__ W, int64_t n, int vec,
+                                                                float *__restrict__ hi_out, float *__restrict__ nlo_out) {
+    __shared__ float red[2][kThreads / kWave];
+    float hi = 0.0f, nlo = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i0 = 0;
+    if (vec) {
+        const int64_t n4 = n / 4;
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+            const float4 v = reinterpret_cast<const float4 *>(W)[i];
+            hi = fmaxf(hi, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+            nlo = fmaxf(nlo, fmaxf(fmaxf(-v.x, -v.y), fmaxf(-v.z, -v.w)));
+        }
+        i0 = n4 * 4;
+    }
+    for (int64_t i = i0 + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+        hi = fmaxf(hi, W[i]);
+        nlo = fmaxf(nlo, -W[i]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        hi = fmaxf(hi, __shfl_xor(hi, off));
+        nlo = fmaxf(nlo, __shfl_xor(nlo, off));
+    }
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        red[0][wave] = hi;
+        red[1][wave] = nlo;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kThreads / kWave; ++w) {
+            hi = fmaxf(hi, red[0][w]);
+            nlo = fmaxf(nlo, red[1][w]);
+        }
+        hi_out[blockIdx.x] = hi;
+        nlo_out[blockIdx.x] = nlo;
+    }
+}
+
+// One block: the tensor's grid from the nparts partial ranges, then written
+// to every row of scales and zeros (after all partials have been read).
+__global__ __launch_bounds__(kThreads) void tensor_grid_kernel(float *__restrict__ scales, float *__restrict__ zeros,
+                                                               int64_t d_out, int nparts, int bits, int sym) {
+    __shared__ float red[2][kThreads / kWave];
+    float hi = 0.0f, nlo = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += kThreads) {
+        hi = fmaxf(hi, scales[i]);
+        nlo = fmaxf(nlo, zeros[i]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        hi = fmaxf(hi, __shfl_xor(hi, off));
+        nlo = fmaxf(nlo, __shfl_xor(nlo, off));
+    }
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        red[0][wave] = hi;
+        red[1][wave] = nlo;
+    }
+    __syncthreads();
+    hi = red[0][0];
+    nlo = red[1][0];
+    for (int w = 1; w < kThreads / kWave; ++w) {
+        hi = fmaxf(hi, red[0][w]);
+        nlo = fmaxf(nlo, red[1][w]);
+    }
+    // max|x| = max(hi, nlo); lo = min(min x, 0) = -nlo
+    const Grid gr = grid_make(fmaxf(hi, nlo), -nlo, hi, bits, sym);
+    for (int64_t r = threadIdx.x; r < d_out; r += kThreads) {
+        scales[r] = gr.s;
+        zeros[r] = gr.zero;
+    }
+}
+
+hipError_t tensor_grid(const float *W, int64_t d_out, int64_t d_in, const gptq_config &c, float *scales, float *zeros,
+                       hipStream_t s) {
+    const int nparts = (int)std::min<int64_t>(d_out, 1024);
+    const int vec = (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+    hipLaunchKernelGGL(tensor_range_kernel, dim3((unsigned)nparts), dim3(kThreads), 0, s, W, d_out * d_in, vec, scales, zeros);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tensor_grid_kernel, dim3(1), dim3(kThreads), 0, s, scales, zeros, d_out, nparts, c.bits,
+                       c.symmetric ? 1 : 0);
+    return hipGetLastError();
 }
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(const float4 *__restrict__ src, float4 *__restrict__ dst, int64_t n4) {
@@ -237,6 +335,18 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     hipError_t e;
     const int32_t *pp = c.act_order ? perm : nullptr;
     if (pp && d_in <= kRowPermMax && !row_perm_inplace(W, d_in)) return hipErrorInvalidValue;  // no copy space
+    // Grids fitted on the original W, before any column moves.
+    const bool fixed = c.grid != GPTQ_GRID_DYNAMIC;
+    if (c.grid == GPTQ_GRID_STATIC) {
+        hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(d_out * ng * kWave, kThreads)), dim3(kThreads), 0, s, W,
+                           d_in, d_out, g, ng, (int64_t)0, ng, c.bits, c.symmetric, 1, (uint8_t *)nullptr, d_in, scales,
+                           zeros);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (c.grid == GPTQ_GRID_TENSOR) {
+        if ((e = tensor_grid(W, d_out, d_in, c, scales, zeros, s)) != hipSuccess) return e;
+    }
+    // Static groups under a column order: every column looks up its own group's grid.
+    const int src = !fixed ? kFitGrids : (pp && c.grid == GPTQ_GRID_STATIC) ? kColumnGrids : kStoredGrids;
     if (pp && row_perm_inplace(W, d_in)) {
         const unsigned grid = (unsigned)std::min<int64_t>(d_out, 2048);
         hipLaunchKernelGGL(permute_rows_inplace_kernel, dim3(grid), dim3(kThreads), (size_t)d_in * sizeof(float), s, W, pp,
@@ -257,7 +367,8 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (g_idx) {
-        hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(d_in, kThreads)), dim3(kThreads), 0, s, pp, d_in, g, g_idx);
+        hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(d_in, kThreads)), dim3(kThreads), 0, s,
+                           fixed ? nullptr : pp, d_in, g, g_idx);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // With a column order the pass writes the codes in processing order
@@ -277,11 +388,11 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
         const int64_t s1 = std::min<int64_t>(s0 + sc, d_in);
         for (int64_t c0 = s0; c0 < s1; c0 += B) {
             const int nc = (int)std::min<int64_t>(B, s1 - c0);
-            if (gt == 0 && c0 % g == 0) {
+            if (!fixed && gt == 0 && c0 % g == 0) {
                 const int64_t waves = d_out;
                 hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W,
-                                   d_in, d_out, g, ng, c0 / g, (int64_t)1, c.bits, c.symmetric, (uint8_t *)nullptr, d_in,
-                                   scales, zeros);
+                                   d_in, d_out, g, ng, c0 / g, (int64_t)1, c.bits, c.symmetric, 1, (uint8_t *)nullptr,
+                                   d_in, scales, zeros);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             float *Eb = Et + (deferred ? (c0 - s0) * ldet : 0);  // this batch's rows of E^T
@@ -298,6 +409,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             a.codes = cdst;
             a.ldc = d_in;
             a.perm = cperm ? nullptr : pp;
+            a.gperm = pp;
             a.scales = scales;
             a.zeros = zeros;
             a.ng = ng;
@@ -305,12 +417,13 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             a.bits = c.bits;
             a.sym = c.symmetric ? 1 : 0;
             a.vec = vec;
+            const int bgt = src == kColumnGrids ? 0 : gt;
             if (B == 32)
-                e = launch_block_32(a, gt, s);
+                e = launch_block_32(a, bgt, src, s);
             else if (B == 64)
-                e = launch_block_64(a, gt, s);
+                e = launch_block_64(a, bgt, src, s);
             else
-                e = launch_block_128(a, gt, s);
+                e = launch_block_128(a, bgt, src, s);
             if (e != hipSuccess) return e;
             // the rest of the superblock
             const int64_t c1 = c0 + nc;
@@ -333,8 +446,13 @@ hipError_t run_rtn(const float *W, int64_t d_out, int64_t d_in, const gptq_confi
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
     const int64_t ng = d_in / g;
     const int64_t waves = d_out * ng;
+    const int fit = c.grid != GPTQ_GRID_TENSOR;
+    if (!fit) {
+        const hipError_t e = tensor_grid(W, d_out, d_in, c, scales, zeros, s);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W, d_in, d_out, g,
-                       ng, (int64_t)0, ng, c.bits, c.symmetric, codes, d_in, scales, zeros);
+                       ng, (int64_t)0, ng, c.bits, c.symmetric, fit, codes, d_in, scales, zeros);
     return hipGetLastError();
 }
 

@@ -2,5 +2,5 @@
 #include "block_kernel.h"
 
 namespace gptq {
-hipError_t launch_block_128(const BlockArgs &a, int gt, hipStream_t s) { return launch_block_bt<128>(a, gt, s); }
+hipError_t launch_block_128(const BlockArgs &a, int gt, int src, hipStream_t s) { return launch_block_bt<128>(a, gt, src, s); }
 }  // namespace gptq
