@@ -19,6 +19,7 @@ struct BlockArgs {
     // grids fitted before the pass, per column: processing position -> original
     // column, whose group's stored grid is used (the grid-per-column kernels only)
     const int32_t *gperm;
+    const float4 *gtab;  // [d_out][ng] packed grids (grid_pack) for the per-column lookup
     float *scales, *zeros;
     int64_t ng, g;
     int bits, sym, vec;
@@ -32,9 +33,9 @@ constexpr int kBlockThreads = 256;
 //                group spans whole batches and was fitted before the batch);
 //   kStoredGrids read from scales/zeros (fitted before the pass) at each
 //                group start (GT > 0) or at the batch start (GT == 0);
-//   kColumnGrids read from scales/zeros for every column, group gperm[c] / g
-//                (groups in original column order while columns are processed
-//                in another order).
+//   kColumnGrids read from gtab for every column, group gperm[c] / g (groups
+//                in original column order while columns are processed in
+//                another order).
 enum GridSource { kFitGrids = 0, kStoredGrids = 1, kColumnGrids = 2 };
 
 hipError_t launch_block_32(const BlockArgs &a, int gt, int src, hipStream_t s);

@@ -175,22 +175,18 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             gr = grid_from_stored(a.scales[r * a.ng + gi], a.zeros[r * a.ng + gi], a.bits, a.sym);
         }
     }
-    // Per-column grids: the stored scale and zero of column j's group are read
-    // kPf columns ahead into a ring of kPf + 1 slots.
+    // Per-column grids: the packed grid of column j's group is read kPf
+    // columns ahead into a ring of kPf + 1 slots (unpacking costs one ldexp).
     constexpr int kPf = 2;
-    float cs[kPf + 1], cz[kPf + 1];
-    const float *srow = a.scales + rr * a.ng;
-    const float *zrow = a.zeros + rr * a.ng;
-    auto load_grid = [&](int j, int slot) {
-        const int gi = gcol[j];
-        cs[slot] = srow[gi];
-        cz[slot] = zrow[gi];
-    };
+    float4 ct[kPf + 1];
+    const float4 *trow = a.gtab + rr * a.ng;
+    auto load_grid = [&](int j, int slot) { ct[slot] = trow[gcol[j]]; };
     if constexpr (SRC == kColumnGrids) {
 #pragma unroll
         for (int j = 0; j < kPf; ++j) load_grid(j, j);
     }
-    float g_s[NG], g_z[NG];
+    // grids fitted in this batch, kept in LDS (not registers) until the end
+    __shared__ float fit_sz[SRC == kFitGrids && GT > 0 ? kRows : 1][NG][2];
     uint32_t cw[(CPL + 3) / 4];
 #pragma unroll
     for (int t = 0; t < (CPL + 3) / 4; ++t) cw[t] = 0u;
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         // the reads stay here, ahead of their use
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SRC == kColumnGrids) {
-            gr = grid_from_stored(cs[j % (kPf + 1)], cz[j % (kPf + 1)], a.bits, a.sym);
+            gr = grid_unpack(ct[j % (kPf + 1)], a.bits, a.sym);
         } else if constexpr (SRC == kStoredGrids && GT > 0) {
             if (j % GT == 0) gr = grid_from_stored(fs[j / GT], fz[j / GT], a.bits, a.sym);
         } else if constexpr (GT > 0) {
@@ -236,8 +232,8 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                 lo = fminf(lo, quad_xor2(lo));
                 hi = fmaxf(hi, quad_xor2(hi));
                 gr = grid_make(amax, lo, hi, a.bits, a.sym);
-                g_s[j / GT] = gr.s;
-                g_z[j / GT] = gr.zero;
+                fit_sz[tid >> 2][j / GT][0] = gr.s;
+                fit_sz[tid >> 2][j / GT][1] = gr.zero;
             }
         }
         const float wj = quad_bcast(w[ot], oq);
@@ -265,8 +261,8 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             for (int g = 0; g < NG; ++g)
                 if (g * GT < nc) {
                     const int64_t gi = (a.c0 + g * GT) / a.g;
-                    a.scales[r * a.ng + gi] = g_s[g];
-                    a.zeros[r * a.ng + gi] = g_z[g];
+                    a.scales[r * a.ng + gi] = fit_sz[tid >> 2][g][0];
+                    a.zeros[r * a.ng + gi] = fit_sz[tid >> 2][g][1];
                 }
         }
     }
@@ -295,7 +291,7 @@ template <int BT, int NT>
 hipError_t launch_block_nt(const BlockArgs &a, int gt, int src, hipStream_t s) {
     const unsigned grid = (unsigned)ceil_div(a.d_out, NT / kRowLanes);
     if (src == kColumnGrids) {
-        if (!a.gperm || gt != 0) return hipErrorInvalidValue;
+        if (!a.gperm || !a.gtab || gt != 0) return hipErrorInvalidValue;
         hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kColumnGrids>), dim3(grid), dim3(NT), 0, s, a);
         return hipGetLastError();
     }

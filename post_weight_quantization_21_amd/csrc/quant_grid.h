@@ -60,7 +60,12 @@ __device__ __forceinline__ Grid grid_make(float amax, float lo, float hi, int bi
     float sa = (hi - lo) / maxq;
     const bool za = (sa == 0.0f);
     sa = za ? 1.0f : sa;
-    float z = za ? 0.0f : fminf(fmaxf(rintf(-lo / sa), 0.0f), maxq);
+    // The zero point is formed unconditionally and made opaque before the
+    // select: otherwise the division goes under a branch, and the compiler
+    // then sinks the pending weight updates of later columns past it.
+    float zq = fminf(fmaxf(rintf(-lo / sa), 0.0f), maxq);
+    asm volatile("" : "+v"(zq));
+    const float z = za ? 0.0f : zq;
     g.s = sym ? ss : sa;
     g.zoff = sym ? 0.0f : z;
     g.qlo = sym ? -qmax_s : 0.0f;
@@ -84,6 +89,27 @@ __device__ __forceinline__ Grid grid_from_stored(float s, float zero, int bits, 
     g.zero = zero;
     g.zd = zero - g.zadd;
     grid_scale(g);
+    return g;
+}
+
+// Compact form {s, zoff, RN(1/s'), k} of a grid, for lookups per column: s' =
+// s 2^k is rebuilt exactly by ldexp, and zd equals zoff (symmetric: both 0;
+// asymmetric: zadd = 0, so zd = zero = zoff).
+__device__ __forceinline__ float4 grid_pack(const Grid &g) { return make_float4(g.s, g.zoff, g.rs, __int_as_float(g.k)); }
+
+__device__ __forceinline__ Grid grid_unpack(float4 t, int bits, int sym) {
+    Grid g;
+    const float half = (float)(1 << (bits - 1));
+    g.s = t.x;
+    g.zoff = t.y;
+    g.zd = t.y;
+    g.rs = t.z;
+    g.k = __float_as_int(t.w);
+    g.ss = ldexpf(t.x, g.k);
+    g.qlo = sym ? -(half - 1.0f) : 0.0f;
+    g.qhi = sym ? (half - 1.0f) : (float)((1 << bits) - 1);
+    g.zadd = sym ? half : 0.0f;
+    g.zero = sym ? half : t.y;
     return g;
 }
 

@@ -67,6 +67,61 @@ __global__ __launch_bounds__(kThreads) void rtn_kernel(const float *__restrict__
     }
 }
 
+// Static groups: every group's grid from the original W, before the pass.  One
+// wave per row.  For g dividing 256 the row is read in coalesced 16-byte pieces
+// (g / 4 lanes per group, reduced by shuffles); otherwise one group at a time
+// over the whole wave.  Writes scales and zeros ([d_out][ng], original group
+// order) and, when tab is given, the packed grids for lookups per column.
+__global__ __launch_bounds__(kThreads) void fit_static_kernel(const float *__restrict__ W, int64_t d_out, int64_t d_in,
+                                                              int64_t g, int64_t ng, int bits, int sym,
+                                                              float *__restrict__ scales, float *__restrict__ zeros,
+                                                              float4 *__restrict__ tab) {
+    const int64_t r = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kWave;  // uniform per wave
+    const int lane = threadIdx.x % kWave;
+    if (r >= d_out) return;
+    const float *row = W + r * d_in;
+    auto put = [&](int64_t gi, float amax, float lo, float hi) {
+        const Grid gr = grid_make(amax, lo, hi, bits, sym);
+        scales[r * ng + gi] = gr.s;
+        zeros[r * ng + gi] = gr.zero;
+        if (tab) tab[r * ng + gi] = grid_pack(gr);
+    };
+    if (g % 4 == 0 && (4 * kWave) % g == 0) {  // rows are 16-byte aligned (W is, and 4 | g | d_in)
+        const int lpg = (int)(g / 4);  // lanes per group
+        for (int64_t k0 = 0; k0 < d_in; k0 += 4 * kWave) {
+            const int64_t k = k0 + 4 * lane;
+            const float4 v = k < d_in ? *reinterpret_cast<const float4 *>(row + k) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            float hi = fmaxf(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)), 0.0f);
+            float lo = fminf(fminf(fminf(v.x, v.y), fminf(v.z, v.w)), 0.0f);
+            float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+            for (int off = 1; off < lpg; off <<= 1) {
+                hi = fmaxf(hi, __shfl_xor(hi, off));
+                lo = fminf(lo, __shfl_xor(lo, off));
+                amax = fmaxf(amax, __shfl_xor(amax, off));
+            }
+            if (lane % lpg == 0 && k < d_in) put(k / g, amax, lo, hi);
+        }
+    } else {
+        for (int64_t gi = 0; gi < ng; ++gi) {
+            const float *src = row + gi * g;
+            float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+            for (int64_t k = lane; k < g; k += kWave) {
+                const float v = src[k];
+                lo = fminf(lo, v);
+                hi = fmaxf(hi, v);
+                amax = fmaxf(amax, fabsf(v));
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                lo = fminf(lo, __shfl_xor(lo, off));
+                hi = fmaxf(hi, __shfl_xor(hi, off));
+                amax = fmaxf(amax, __shfl_xor(amax, off));
+            }
+            if (lane == 0) put(gi, amax, lo, hi);
+        }
+    }
+}
+
 // The one grid of a whole matrix (page "LLM 量化方法原理与实现详解", §2.3:
 // one scale per tensor), in two kernels that need no scratch: the outputs
 // scales and zeros ([d_out][1]) first hold partial ranges.  Block b reduces its
@@ -256,22 +311,26 @@ int64_t et_ld(int64_t d_out) { return ceil_div(d_out, kBlockThreads) * kBlockThr
 
 constexpr int64_t kSuperCols = 1024;  // columns per superblock of the two-level lazy update
 
-// Superblock width: a multiple of the batch and, when a group spans several
-// batches, of the group (a group's grid is fitted from columns that must all
-// be up to date).  At least d_in means one superblock: no deferred update.
+// Superblock width: a multiple of the batch and, when a grid fitted during
+// the pass spans several batches, of its group (the grid is fitted from
+// columns that must all be up to date).  Grids fitted before the pass, and the
+// one grid of a row (fitted at column 0, before any update), set no such
+// bound.  At least d_in means one superblock: no deferred update.
 int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
-    const int64_t unit = gt > 0 ? c.block_size : g;  // g is a multiple of B when gt == 0
+    const bool refit = c.grid == GPTQ_GRID_DYNAMIC && gt == 0 && g < d_in;  // g is a multiple of B here
+    const int64_t unit = refit ? g : c.block_size;
     const int64_t sc = unit >= kSuperCols ? unit : (kSuperCols / unit) * unit;
     return sc;
 }
 
 // Workspace of the column pass: E^T of a whole superblock [S][ldet] (one batch
 // when there is a single superblock); with act-order, a copy of W for the
-// column gather (rows too long for the in-place permutation only), and the
-// codes in processing order with the inverse permutation.
+// column gather (rows too long for the in-place permutation only), the codes
+// in processing order with the inverse permutation, and, for static groups,
+// the packed grids [d_out][ng] of the lookup per column.
 struct QuantLayout {
-    size_t et_off, wc_off, cp_off, inv_off, total;
+    size_t et_off, wc_off, cp_off, inv_off, tab_off, total;
     int64_t sc;       // superblock width
     int64_t et_rows;  // rows of E^T kept
 };
@@ -287,7 +346,11 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     // act-order: codes in processing order and the inverse permutation
     const bool cperm = c.act_order && d_in <= kCodePermMax;
     l.inv_off = l.cp_off + (cperm ? align_up((size_t)d_out * (size_t)d_in, 256) : 0);
-    l.total = l.inv_off + (cperm ? align_up((size_t)d_in * sizeof(int32_t), 256) : 0);
+    l.tab_off = l.inv_off + (cperm ? align_up((size_t)d_in * sizeof(int32_t), 256) : 0);
+    // static groups under act-order: packed grids for the lookup per column
+    const bool tab = c.act_order && c.grid == GPTQ_GRID_STATIC;
+    const int64_t ng = d_in / (c.group_size > 0 ? c.group_size : d_in);
+    l.total = l.tab_off + (tab ? align_up((size_t)d_out * (size_t)ng * 16, 256) : 0);
     return l;
 }
 
@@ -337,10 +400,10 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     if (pp && d_in <= kRowPermMax && !row_perm_inplace(W, d_in)) return hipErrorInvalidValue;  // no copy space
     // Grids fitted on the original W, before any column moves.
     const bool fixed = c.grid != GPTQ_GRID_DYNAMIC;
+    float4 *gtab = (pp && c.grid == GPTQ_GRID_STATIC) ? reinterpret_cast<float4 *>(wsb + lay.tab_off) : nullptr;
     if (c.grid == GPTQ_GRID_STATIC) {
-        hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(d_out * ng * kWave, kThreads)), dim3(kThreads), 0, s, W,
-                           d_in, d_out, g, ng, (int64_t)0, ng, c.bits, c.symmetric, 1, (uint8_t *)nullptr, d_in, scales,
-                           zeros);
+        hipLaunchKernelGGL(fit_static_kernel, dim3((unsigned)ceil_div(d_out * kWave, kThreads)), dim3(kThreads), 0, s, W,
+                           d_out, d_in, g, ng, c.bits, c.symmetric, scales, zeros, gtab);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (c.grid == GPTQ_GRID_TENSOR) {
         if ((e = tensor_grid(W, d_out, d_in, c, scales, zeros, s)) != hipSuccess) return e;
@@ -410,6 +473,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             a.ldc = d_in;
             a.perm = cperm ? nullptr : pp;
             a.gperm = pp;
+            a.gtab = gtab;
             a.scales = scales;
             a.zeros = zeros;
             a.ng = ng;

@@ -169,7 +169,7 @@ PASS_CASES = [
     (4, True, 256, 128, 48, 2560),    # groups spanning two batches
     (3, True, 32, 32, 40, 1152),      # 32-column batches, a partial last superblock
     (4, False, 1024, 128, 32, 2048),  # one group per superblock
-    (4, False, 0, 128, 32, 1536),     # per-row grid: one superblock of 1536
+    (4, False, 0, 128, 32, 1536),     # per-row grid: fitted at column 0, superblocks of 1024 + 512
 ]
 
 
