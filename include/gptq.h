@@ -99,6 +99,14 @@ typedef struct {
     float damp_rel;     /* lambda = damp_rel * mean(diag H), >= 0 */
     int32_t act_order;  /* 1: process columns by descending diag(H) */
     int32_t grid;       /* gptq_grid: when the grids are fitted */
+    int32_t super_cols; /* columns per superblock of the two-level lazy update
+                           (0: 1024).  Batches of one superblock update only the
+                           rest of it; the superblock's stacked errors update
+                           every later column when it ends.  Rounded down to a
+                           multiple of block_size (and of group_size when a
+                           dynamic group spans batches), at least one of them;
+                           >= d_in gives the one-level update.  The results
+                           are the same sums in another fp32 order. */
 } gptq_config;
 
 /*

@@ -37,7 +37,7 @@ class Config(ctypes.Structure):
     """Mirror of ``gptq_config``."""
     _fields_ = [("bits", ctypes.c_int32), ("symmetric", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("damp_rel", ctypes.c_float), ("act_order", ctypes.c_int32),
-                ("grid", ctypes.c_int32)]
+                ("grid", ctypes.c_int32), ("super_cols", ctypes.c_int32)]
 
 
 # gptq_grid: when the quantization grids are fitted
@@ -45,9 +45,9 @@ GRIDS = {"dynamic": 0, "static": 1, "tensor": 2}
 
 
 def config(bits: int = 4, symmetric: bool = False, group_size: int = 128, block_size: int = 128,
-           damp_rel: float = 0.01, act_order: bool = False, grid: str = "dynamic") -> Config:
+           damp_rel: float = 0.01, act_order: bool = False, grid: str = "dynamic", super_cols: int = 0) -> Config:
     return Config(int(bits), int(bool(symmetric)), int(group_size), int(block_size), float(damp_rel),
-                  int(bool(act_order)), GRIDS[grid])
+                  int(bool(act_order)), GRIDS[grid], int(super_cols))
 
 
 _lib = None

@@ -32,6 +32,7 @@ gptq_status check_cfg(const gptq_config *c, int64_t d_in, const char *fn) {
     if (!(c->damp_rel >= 0.0f)) return fail(GPTQ_ERR_INVALID_ARG, "%s: damp_rel must be >= 0", fn);
     if (c->grid != GPTQ_GRID_DYNAMIC && c->grid != GPTQ_GRID_STATIC && c->grid != GPTQ_GRID_TENSOR)
         return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown grid %d", fn, c->grid);
+    if (c->super_cols < 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: super_cols must be >= 0", fn);
     if (c->grid == GPTQ_GRID_TENSOR && c->group_size != 0)
         return fail(GPTQ_ERR_INVALID_ARG, "%s: a per-tensor grid needs group_size 0", fn);
     return GPTQ_OK;
@@ -67,6 +68,7 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
     case GPTQ_OP_QUANTIZE: {
         if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: quantize needs cfg");
         if (cfg->block_size <= 0) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: block_size must be > 0");
+        if (cfg->super_cols < 0) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: super_cols must be >= 0");
         *out = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
         return GPTQ_OK;
     }

@@ -309,7 +309,7 @@ int group_tile(const gptq_config &c, int64_t d_in) {
 // E^T rows are padded to whole workgroups so the batch kernel stores without a row test.
 int64_t et_ld(int64_t d_out) { return ceil_div(d_out, kBlockThreads) * kBlockThreads; }
 
-constexpr int64_t kSuperCols = 1024;  // columns per superblock of the two-level lazy update
+constexpr int64_t kSuperCols = 1024;  // default columns per superblock of the two-level lazy update
 
 // Superblock width: a multiple of the batch and, when a grid fitted during
 // the pass spans several batches, of its group (the grid is fitted from
@@ -320,7 +320,8 @@ int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
     const bool refit = c.grid == GPTQ_GRID_DYNAMIC && gt == 0 && g < d_in;  // g is a multiple of B here
     const int64_t unit = refit ? g : c.block_size;
-    const int64_t sc = unit >= kSuperCols ? unit : (kSuperCols / unit) * unit;
+    const int64_t want = c.super_cols > 0 ? c.super_cols : kSuperCols;
+    const int64_t sc = unit >= want ? unit : (want / unit) * unit;
     return sc;
 }
 

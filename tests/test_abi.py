@@ -53,6 +53,15 @@ def test_workspace_sizes():
     assert base + 4096 * 4096 <= gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, ca) < base + 4096 * 4096 * 2
     # longer rows are copied, then gathered
     assert gq.workspace_bytes(gq.OP_QUANTIZE, 8, 16512, 0, ca) >= 128 * 256 * 4 + 8 * 16512 * 4
+    # E^T holds one superblock: the tunable width sets its rows (at least one batch)
+    w128 = gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, gq.config(4, False, 128, 128, super_cols=128))
+    w2048 = gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, gq.config(4, False, 128, 128, super_cols=2048))
+    assert 128 * 4096 * 4 <= w128 < 2 * 128 * 4096 * 4 and w2048 >= 2048 * 4096 * 4
+    assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, gq.config(4, False, 128, 128, super_cols=100)) == w128
+    # static groups under act-order keep the packed grids (16 bytes per row and group)
+    cs = gq.config(4, True, 128, 128, act_order=True, grid="static")
+    assert gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, cs) >= \
+        gq.workspace_bytes(gq.OP_QUANTIZE, 4096, 4096, 0, ca) + 4096 * 32 * 16
     assert gq.workspace_bytes(gq.OP_PREPARE, 0, 4096) >= 2 * 4096 * 4096 * 4
     assert gq.workspace_bytes(gq.OP_LOSS, 64, 128) >= 64 * 128 * 4 + 128 * 128 * 4
     # a single tile with few tokens is not split over tokens: no workspace
@@ -83,6 +92,12 @@ def test_argument_errors_are_synchronous():
     assert _call_quantize(gq.config(), ptr=0x10004) == gq.ERR_INVALID_ARG  # misaligned
     assert _call_quantize(gq.config(), ws_bytes=16) == gq.ERR_WORKSPACE
     assert _call_quantize(gq.config(act_order=True)) == gq.ERR_INVALID_ARG  # act_order without perm
+    assert _call_quantize(gq.config(group_size=32, grid="tensor")) == gq.ERR_INVALID_ARG  # one grid, no groups
+    assert b"group_size 0" in lib.gptq_last_error()
+    bad_grid = gq.config()
+    bad_grid.grid = 7
+    assert _call_quantize(bad_grid) == gq.ERR_INVALID_ARG
+    assert _call_quantize(gq.config(super_cols=-128)) == gq.ERR_INVALID_ARG
     cfg = gq.config()
     p = ctypes.c_void_p(0x10000)
     assert lib.gptq_prepare_hinv(p, None, 0, ctypes.byref(cfg), p, p, p, p, 1 << 30, None) == gq.ERR_INVALID_ARG

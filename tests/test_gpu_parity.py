@@ -205,6 +205,34 @@ def test_column_pass_with_oracle_factor(oracle_mod, bits, sym, group, block, d_o
     assert np.abs(wq[same] - ref["w_at_q"][same]).max() <= 1e-4 * np.abs(ref["w_at_q"]).max()
 
 
+@pytest.mark.parametrize("super_cols", [128, 512, 0, 2048, 4096])
+def test_superblock_width_is_a_tunable(oracle_mod, super_cols):
+    """The two-level lazy update at several superblock widths (128: every batch updates all later
+    columns at once; 4096 >= d_in: one level) gives the oracle's result within the parity bars."""
+    torch = torch_mod()
+    d_out, d_in, group, block = 96, 2304, 128, 128
+    log(f"superblock {super_cols} {d_out}x{d_in}")
+    H = _spd_h(oracle_mod, d_in, 4, "q_proj_7b")
+    U32 = oracle_mod.inv_chol_upper(oracle_mod.damp(H, 0.01)).astype(np.float32)
+    rng = np.random.default_rng(super_cols + 1)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    ref = oracle_mod.gptq_pass(W, U32.astype(np.float64), 4, False, group)
+    cfg = gq.config(4, False, group, block, 0.01, False, super_cols=super_cols)
+    ng = d_in // group
+    Wd = cuda(W)
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    ze = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    gq.quantize_layer(Wd, cuda(U32), cfg, codes, sc, ze)
+    torch.cuda.synchronize()
+    gout = dict(codes=host(codes), scales=host(sc), zeros=host(ze))
+    st = compare_layer(gout, dict(codes=ref["codes"], scales=ref["scales"], zeros=ref["zeros"], perm=np.arange(d_in)),
+                       group, d_in)
+    log(f"  {st}")
+    assert st["match"] >= 0.999
+    assert st["scale_rel_clean"] <= 1e-5 and st["zero_rel_clean"] == 0.0
+
+
 @pytest.mark.parametrize("d_out,d_in,group", [(4, 16512, 128), (5, 1024, 0)])
 def test_act_order_identity_factor_gives_permuted_rtn(oracle_mod, d_out, d_in, group):
     """With U = I no error is fed forward, so the pass with a column order is RTN
