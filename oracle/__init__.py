@@ -26,6 +26,8 @@ Steps, in the pages' order:
    与实现详解", §2.3 granularity.
 6. ``layer_loss``: ||W X - W_hat X||_F^2 = 1/2 sum_r D_r H D_r^T with D = W_hat - W
    and the undamped H (page "LLM 量化方法原理与实现详解", §4.1 objective).
+7. ``pack_codes`` / ``w4a16_matmul``: the codes as little-endian bit streams and
+   the product of 16-bit activations with the dequantized 4-bit weights.
 
 Every function is pinned by ``tests/test_oracle_*.py`` (closed forms, special
 cases, invariants, brute force and the pages' worked example).
@@ -288,6 +290,59 @@ def dequant(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int
     s = scales[:, gi]
     z = zeros[:, gi]
     return ((codes.astype(np.float32) - z) * s).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# after the pass: packed codes and the W4A16 product that consumes them
+# ----------------------------------------------------------------------------
+def pack_codes(codes: np.ndarray, bits: int, perm=None) -> np.ndarray:
+    """Rows of codes as little-endian bit streams in 32-bit words.
+
+    Column k of the packed row (k-th code of the stream) is codes[o][perm[k]]
+    (codes[o][k] without perm) at bits [bits*k, bits*k + bits); the stream is
+    padded with zero bits to whole words.  The pages print no storage format
+    for low-bit weights (page "量化经典：LLM.int8 / GPTQ / AWQ", GPTQ section:
+    3/4-bit weights plus scales); this is the plainest dense one.
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    if perm is not None:
+        c = c[:, np.asarray(perm)]
+    n, d = c.shape
+    if np.any(c >> bits):
+        raise ValueError("a code does not fit in the bit width")
+    words = (d * bits + 31) // 32
+    bitplane = ((c[:, :, None] >> np.arange(bits, dtype=np.uint8)) & 1).reshape(n, d * bits)
+    stream = np.zeros((n, words * 32), dtype=np.uint8)
+    stream[:, :d * bits] = bitplane
+    return np.packbits(stream, axis=1, bitorder="little").view("<u4").reshape(n, words)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, d_in: int) -> np.ndarray:
+    """Inverse of pack_codes (in packed column order)."""
+    p = np.ascontiguousarray(packed, dtype="<u4")
+    n = p.shape[0]
+    stream = np.unpackbits(p.view(np.uint8), axis=1, bitorder="little")[:, :d_in * bits].reshape(n, d_in, bits)
+    return (stream.astype(np.uint32) << np.arange(bits, dtype=np.uint32)).sum(axis=2).astype(np.uint8)
+
+
+def w4a16_matmul(X: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int,
+                 kperm=None) -> np.ndarray:
+    """Y = X' W_hat^T in fp64 with 4-bit packed weights.
+
+    X [M][d_in] (fp16 values); X' = X[:, kperm] (X without kperm): column k of
+    X' meets packed column k.  W_hat[o][k] = (code - zero) * scale of group
+    k // group (groups contiguous in packed order), taken exactly
+    (page "LLM 量化方法原理与实现详解", §2.2 dequantization; weight-only
+    4-bit with 16-bit activations: page "量化经典", GPTQ section).
+    """
+    X64 = np.asarray(X, dtype=np.float64)
+    d = X64.shape[1]
+    g = group if group > 0 else d
+    q = unpack_codes(packed, 4, d).astype(np.float64)
+    gi = np.arange(d) // g
+    What = (q - np.asarray(zeros, dtype=np.float64)[:, gi]) * np.asarray(scales, dtype=np.float64)[:, gi]
+    Xp = X64 if kperm is None else X64[:, np.asarray(kperm)]
+    return Xp @ What.T
 
 
 def layer_loss(W: np.ndarray, What: np.ndarray, H: np.ndarray) -> float:
