@@ -67,13 +67,14 @@ typedef enum {
     GPTQ_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } gptq_status;
 
-typedef enum { GPTQ_DT_F32 = 0, GPTQ_DT_BF16 = 1 } gptq_dtype;
+typedef enum { GPTQ_DT_F32 = 0, GPTQ_DT_BF16 = 1, GPTQ_DT_F16 = 2 } gptq_dtype;
 
 typedef enum {
     GPTQ_OP_HESSIAN = 0,
     GPTQ_OP_PREPARE = 1,
     GPTQ_OP_QUANTIZE = 2,
-    GPTQ_OP_LOSS = 3
+    GPTQ_OP_LOSS = 3,
+    GPTQ_OP_W4A16 = 4 /* n_tok = M, the rows of X */
 } gptq_op;
 
 /*
@@ -218,6 +219,45 @@ GPTQ_API gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const
                             const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in,
                             int32_t group_size, double *loss_dev, void *ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/*
+ * Packed codes (after the pass; page "量化经典：LLM.int8 / GPTQ / AWQ", GPTQ
+ * section: 3/4-bit weights plus scales -- the pages print no storage format).
+ * Each row becomes one little-endian bit stream: packed column k is
+ * codes[o][perm ? perm[k] : k] at bits [bits*k, bits*k + bits) of the row's
+ * stream, in 32-bit words (word w = stream bits 32w .. 32w+31), the tail
+ * padded with zero bits.
+ *   codes   [d_out][d_in] u8, ORIGINAL column order; codes are masked to bits.
+ *   perm    [d_in] int32 or NULL: the order the groups run in.  Pass the
+ *           act-order permutation when the grids are DYNAMIC (groups in
+ *           processing order), NULL for STATIC, TENSOR or natural order.
+ *   packed  [d_out][ceil(d_in*bits/32)] u32 out.
+ * bits: 2..8.  Integer work: bit-exact.
+ */
+GPTQ_API gptq_status gptq_pack_codes(const uint8_t *codes, int64_t d_out, int64_t d_in, int32_t bits,
+                                     const int32_t *perm, uint32_t *packed, hipStream_t stream);
+
+/*
+ * W4A16 product (page "LLM 量化方法原理与实现详解", §6.2: 4-bit weights, 16-bit
+ * activations; §2.2: dequantized weight (q - z) s):
+ *   Y[m][o] = sum_k X[m][kperm ? kperm[k] : k] * (q[o][k] - z[o][k/g]) * s[o][k/g]
+ * with q[o][k] packed column k of row o (4-bit, from gptq_pack_codes) and g =
+ * group_size (0: d_in).  Groups are contiguous in packed order.
+ *   X       fp16 [M][ldx] activations, one row per token (x_dtype must be
+ *           GPTQ_DT_F16); 16-byte aligned, ldx a multiple of 8.
+ *   kperm   [d_in] int32 or NULL: the perm the codes were packed with.
+ *   packed  [d_out][d_in/8] u32; scales, zeros [d_out][d_in/g] fp32, zeros
+ *           integers in 0..15 (as the quantizer stores them).
+ *   Y       fp32 [M][ldy] out.
+ *   ws      scratch of gptq_workspace_bytes(GPTQ_OP_W4A16, d_out, d_in, M, NULL).
+ * Products are exact (integer weights times fp16 on fp16 matrix cores); sums
+ * are fp32, added over K splits in a fixed order (deterministic).  g must be
+ * a multiple of 32 (else GPTQ_ERR_UNSUPPORTED); packed 16-byte aligned.
+ */
+GPTQ_API gptq_status gptq_w4a16_gemm(const void *X, gptq_dtype x_dtype, int64_t M, int64_t d_in, int64_t ldx,
+                                     const int32_t *kperm, const uint32_t *packed, const float *scales,
+                                     const float *zeros, int32_t group_size, int64_t d_out, float *Y, int64_t ldy,
+                                     void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Scratch bytes needed by `op` for these sizes (cfg may be NULL for
  * GPTQ_OP_HESSIAN and GPTQ_OP_LOSS).  `out` is a host pointer. */

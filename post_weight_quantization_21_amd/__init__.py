@@ -18,12 +18,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgptq.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-DT_F32, DT_BF16 = 0, 1
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS = 0, 1, 2, 3
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16 = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_rtn_quantize",
     "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
+    "gptq_pack_codes", "gptq_w4a16_gemm",
 )
 
 
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_rtn_quantize": [vp, i64, i64, cfgp, vp, vp, vp, vp],
         "gptq_layer_loss": [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, vp],
         "gptq_workspace_bytes": [ctypes.c_int, i64, i64, i64, cfgp, ctypes.POINTER(sz)],
+        "gptq_pack_codes": [vp, i64, i64, i32, vp, vp, vp],
+        "gptq_w4a16_gemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i64, vp, i64, vp, sz, vp],
         "gptq_status_string": [ctypes.c_int],
         "gptq_last_error": [],
     }
@@ -179,6 +182,42 @@ def layer_loss(W, codes, scales, zeros, H, group_size: int, g_idx=None, out=None
                                           d_out, d_in, int(group_size), _ptr(out), _ptr(ws), ws.numel(),
                                           _stream(stream)))
     return out
+
+
+def packed_words(d_in: int, bits: int) -> int:
+    """32-bit words per packed row."""
+    return (d_in * bits + 31) // 32
+
+
+def pack_codes(codes, bits: int, packed=None, perm=None, stream=None):
+    """Codes [d_out][d_in] u8 -> rows of little-endian bit streams (u32 [d_out][words])."""
+    import torch
+    _need_cuda(codes, packed, perm)
+    d_out, d_in = codes.shape
+    if packed is None:
+        packed = torch.empty(d_out, packed_words(d_in, bits), dtype=torch.int32, device=codes.device)
+    _check(load_library().gptq_pack_codes(_ptr(codes), d_out, d_in, int(bits), _ptr(perm), _ptr(packed),
+                                          _stream(stream)))
+    return packed
+
+
+def w4a16_gemm(X, packed, scales, zeros, group_size: int, d_out: int, kperm=None, Y=None, ws=None, stream=None):
+    """Y = X' W_hat^T with fp16 X [M][d_in] and 4-bit packed weights; Y fp32 [M][d_out]."""
+    import torch
+    _need_cuda(X, packed, scales, zeros, kperm, Y)
+    if X.dtype != torch.float16:
+        raise TypeError("X must be float16")
+    M, d_in = X.shape
+    if X.stride(1) != 1:
+        raise ValueError("X rows must be contiguous")
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_W4A16, d_out, d_in, M), X.device)
+    _check(load_library().gptq_w4a16_gemm(_ptr(X), DT_F16, M, d_in, X.stride(0), _ptr(kperm), _ptr(packed),
+                                          _ptr(scales), _ptr(zeros), int(group_size), d_out, _ptr(Y), Y.stride(0),
+                                          _ptr(ws), ws.numel(), _stream(stream)))
+    return Y
 
 
 @dataclass

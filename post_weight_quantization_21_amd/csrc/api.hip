@@ -1,4 +1,5 @@
 // C ABI entry points: argument checks, workspace sizing, dispatch.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -74,6 +75,9 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
     }
     case GPTQ_OP_LOSS:
         *out = gptq::loss_ws_bytes(d_out, d_in);
+        return GPTQ_OK;
+    case GPTQ_OP_W4A16:  // the largest plan over the supported group sizes
+        *out = std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 32), gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 64));
         return GPTQ_OK;
     }
     return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: unknown op %d", op);
@@ -155,6 +159,37 @@ gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const float *s
     const size_t need = gptq::loss_ws_bytes(d_out, d_in);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_loss(W, codes, scales, zeros, g_idx, H, d_out, d_in, group_size, loss_dev, ws, stream), fn);
+}
+
+gptq_status gptq_pack_codes(const uint8_t *codes, int64_t d_out, int64_t d_in, int32_t bits, const int32_t *perm,
+                            uint32_t *packed, hipStream_t stream) {
+    const char *fn = "gptq_pack_codes";
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    if (bits < 2 || bits > 8) return fail(GPTQ_ERR_INVALID_ARG, "%s: bits=%d outside 2..8", fn, bits);
+    if (!codes || !packed) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(packed, 4) || (perm && !aligned(perm, 4))) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return hip_status(gptq::run_pack(codes, d_out, d_in, bits, perm, packed, stream), fn);
+}
+
+gptq_status gptq_w4a16_gemm(const void *X, gptq_dtype x_dtype, int64_t M, int64_t d_in, int64_t ldx,
+                            const int32_t *kperm, const uint32_t *packed, const float *scales, const float *zeros,
+                            int32_t group_size, int64_t d_out, float *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    const char *fn = "gptq_w4a16_gemm";
+    if (M <= 0 || d_in <= 0 || d_out <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    if (x_dtype != GPTQ_DT_F16) return fail(GPTQ_ERR_UNSUPPORTED, "%s: activations must be fp16", fn);
+    if (group_size < 0 || (group_size > 0 && d_in % group_size != 0))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: group_size does not divide d_in", fn);
+    const int64_t g = group_size > 0 ? group_size : d_in;
+    if (g % 32 != 0) return fail(GPTQ_ERR_UNSUPPORTED, "%s: group_size (or d_in when 0) must be a multiple of 32", fn);
+    if (!X || !packed || !scales || !zeros || !Y) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (ldx < d_in || ldy < d_out) return fail(GPTQ_ERR_INVALID_ARG, "%s: ldx < d_in or ldy < d_out", fn);
+    if (!aligned(X) || ldx % 8 != 0 || !aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(Y, 4) ||
+        (kperm && !aligned(kperm, 4)))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: X must be 16-byte aligned with ldx a multiple of 8; other pointers 4-byte aligned", fn);
+    const size_t need = gptq::w4a16_ws_bytes(M, d_in, d_out, g);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_w4a16(X, M, d_in, ldx, kperm, packed, scales, zeros, g, d_out, Y, ldy, ws, stream), fn);
 }
 
 }  // extern "C"

@@ -88,6 +88,16 @@ hipError_t run_loss(const float *W, const uint8_t *codes, const float *scales, c
                     const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in, int32_t group_size,
                     double *loss, void *ws, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Packed codes and the W4A16 product (w4a16.hip)
+// ---------------------------------------------------------------------------
+hipError_t run_pack(const uint8_t *codes, int64_t d_out, int64_t d_in, int bits, const int32_t *perm,
+                    uint32_t *packed, hipStream_t s);
+size_t w4a16_ws_bytes(int64_t M, int64_t d_in, int64_t d_out, int64_t g);
+hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const int32_t *kperm,
+                     const uint32_t *packed, const float *scales, const float *zeros, int64_t g, int64_t d_out,
+                     float *Y, int64_t ldy, void *ws, hipStream_t s);
+
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
