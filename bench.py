@@ -72,6 +72,77 @@ def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
                        f"{rows} of {d_out} rows (x{d_out / rows:g}); measured {t_h:.2f}+{t_p:.2f}+{t_q:.2f} s")}
 
 
+def bench_w4a16(args) -> int:
+    """The product of M fp16 tokens with the 4-bit packed up_proj_70b layer (28672 x 8192, groups of 128).
+
+    Codes, scales and zeros are seeded synthetic values of the quantizer's
+    ranges.  Reported: microseconds per product, the weight stream against HBM
+    bandwidth, a dense fp16 product of the dequantized weights for context, and
+    the oracle on a sample of rows.
+    """
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_21_amd as gq
+
+    gq.load_library()
+    dev = torch.device("cuda:0")
+    M, d_out, d_in, g = args.w4a16, 28672, 8192, 128
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 16, size=(d_out, d_in), dtype=np.uint8)
+    scales = rng.uniform(1e-3, 2e-2, size=(d_out, d_in // g)).astype(np.float32)
+    zeros = rng.integers(0, 16, size=(d_out, d_in // g)).astype(np.float32)
+    X = rng.standard_normal((M, d_in)).astype(np.float16)
+    cd, sd, zd, xd = (torch.from_numpy(a).to(dev) for a in (codes, scales, zeros, X))
+    packed = gq.pack_codes(cd, 4)
+    Y = torch.empty(M, d_out, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(gq.workspace_bytes(gq.OP_W4A16, d_out, d_in, M), 1), dtype=torch.uint8, device=dev)
+    run = lambda: gq.w4a16_gemm(xd, packed, sd, zd, g, d_out, Y=Y, ws=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    Wd = ((cd.float() - zd.repeat_interleave(g, 1)) * sd.repeat_interleave(g, 1)).half()
+    del cd
+    for _ in range(2):
+        torch.matmul(xd, Wd.t())
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        torch.matmul(xd, Wd.t())
+    b.record()
+    torch.cuda.synchronize()
+    us_dense = a.elapsed_time(b) * 1e3 / args.steps
+    nbytes = d_out * d_in // 2 + 2 * 4 * d_out * (d_in // g) + 2 * M * d_in + 4 * M * d_out  # weights, grids, X, Y
+    achieved = nbytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 2048
+        pk = oracle.pack_codes(codes[:rows], 4)
+        t0 = time.perf_counter()
+        oracle.w4a16_matmul(X, pk, scales[:rows], zeros[:rows], g)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt * 1e6 * d_out / rows, 1), "unit": "us", "cores": torch.get_num_threads(),
+               "kind": "oracle", "sample": f"{rows} of {d_out} weight rows (unpack, dequantize, fp64 matmul), scaled x{d_out // rows}"}
+    out = {"metric": "w4a16_product_us", "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic", "config": {"workload": "w4a16_up_proj_70b", "tokens": M, "d_out": d_out, "d_in": d_in,
+                                           "group": g},
+           "dense_fp16_us": round(us_dense, 2),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(achieved / 8000.0, 4), "traffic": None},
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,11 +150,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="q_proj_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w4a16", type=int, default=0, metavar="M",
+                    help="instead: time the W4A16 product of M tokens with the packed 28672x8192 layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this benchmark runs GPTQ on one GPU only "
               f"(sharding the layer: an all-reduce of H over token slices, then the column pass split by output rows, is not built).", file=sys.stderr)
         return 2
+
+    if args.w4a16 > 0:
+        return bench_w4a16(args)
 
     import torch
 

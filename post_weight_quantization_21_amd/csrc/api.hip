@@ -76,8 +76,9 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
     case GPTQ_OP_LOSS:
         *out = gptq::loss_ws_bytes(d_out, d_in);
         return GPTQ_OK;
-    case GPTQ_OP_W4A16:  // the largest plan over the supported group sizes
-        *out = std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 32), gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 64));
+    case GPTQ_OP_W4A16:  // the largest plan over the group sizes (the plan depends on g only through 32, 64, 128 | g)
+        *out = std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 32),
+                        std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 64), gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 128)));
         return GPTQ_OK;
     }
     return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: unknown op %d", op);

@@ -54,44 +54,81 @@ __global__ __launch_bounds__(kThreads) void pack_codes_kernel(const uint8_t *__r
     }
 }
 
-// Xp[m][k] = X[m][kperm[k]] (fp16), rows of ldxp elements.
+// The activations in the operand order: Xp[m][8 c + j] = X[m][kp(8 c + il(j))]
+// with il = (0, 4, 1, 5, 2, 6, 3, 7) (the order dequant8 yields the codes of a
+// word in) and kp = kperm, or the identity.  d_in is a multiple of 8.
 __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t *__restrict__ X, int64_t ldx, int64_t M,
                                                                int64_t d_in, const int32_t *__restrict__ kperm,
                                                                uint16_t *__restrict__ Xp, int64_t ldxp) {
     const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (k >= d_in) return;
-    int64_t c = kperm[k];
+    const int j = (int)(k & 7);
+    const int64_t src = (k & ~(int64_t)7) + ((j & 1) ? 4 + (j >> 1) : (j >> 1));
+    int64_t c = kperm ? kperm[src] : src;
     c = c < 0 ? 0 : (c >= d_in ? d_in - 1 : c);
     for (int64_t m = blockIdx.y; m < M; m += gridDim.y) Xp[m * ldxp + k] = X[m * ldx + c];
 }
 
-// Eight 4-bit codes (code i at bits 4i) as fp16 (code - z).  bias = 1024 + z in both halves.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 bias) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+// Eight 4-bit codes (code i at bits 4i) as fp16 (code - z), exactly, in the
+// order 0, 4, 1, 5, 2, 6, 3, 7 (the activations are stored in the same order
+// within each 8-column chunk).  Masking a code into mantissa bits 0-3 or 4-7
+// of an fp16 with exponent 10 gives 1024 + q or 1024 + 16 q:
+//   codes 0, 4:  (w      & 0x000F000F) | 0x6400 6400 -> 1024 + q, minus (1024 + z)
+//   codes 1, 5:  (w      & 0x00F000F0) | 0x6400 6400 -> 1024 + 16 q, times 1/16 minus (64 + z)
+//   codes 2, 6 and 3, 7: the same on w >> 8.
+// Each result is a small integer, so the packed fp16 add and fma are exact.
+struct Bias {
+    f16x2 b1;   // 1024 + z
+    f16x2 b16;  // 64 + z
+};
+__device__ __forceinline__ Bias bias_of(float z) {
+    Bias b;
+    b.b1[0] = b.b1[1] = (_Float16)(1024.0f + z);
+    b.b16[0] = b.b16[1] = (_Float16)(64.0f + z);
+    return b;
+}
+// The exponent pattern is passed in a register (`magic`): a VOP3 instruction on
+// this architecture takes no literal, so a register operand is what lets each
+// mask-and-insert be one v_and_or_b32.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, const Bias &b, uint32_t magic) {
+    const uint32_t w8 = w >> 8;
+    f16x2 sixteenth;
+    sixteenth[0] = sixteenth[1] = (_Float16)0.0625f;
+    const f16x2 h0 = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | magic) - b.b1;
+    const f16x2 h1 = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | magic) * sixteenth - b.b16;
+    const f16x2 h2 = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | magic) - b.b1;
+    const f16x2 h3 = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | magic) * sixteenth - b.b16;
     f16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // bytes: lo.byte i, 0, hi.byte i, 0 (selector 12 gives a zero byte)
-        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + i) << 16) | (uint32_t)i;
-        const uint32_t d = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-        const f16x2 h = __builtin_bit_cast(f16x2, d) - bias;
-        r[2 * i] = h[0];
-        r[2 * i + 1] = h[1];
-    }
+    r[0] = h0[0];  // code 0
+    r[1] = h0[1];  // code 4
+    r[2] = h1[0];  // code 1
+    r[3] = h1[1];  // code 5
+    r[4] = h2[0];  // code 2
+    r[5] = h2[1];  // code 6
+    r[6] = h3[0];  // code 3
+    r[7] = h3[1];  // code 7
     return r;
 }
 
 // One workgroup: 128 output features x 32 TM tokens over K range
 // [kb, kb + kspan).  Wave w owns features 32 w .. 32 w + 31; lane l supplies
 // feature l % 32 of the weight operand and token l % 32 of each activation
-// block.  K advances in macro steps of 16 U columns (U MFMAs): lane half h
-// takes packed words U h .. U h + U - 1 of the step (one 4U-byte load) and the
+// block.  K advances in steps of 16 U columns (U MFMAs): lane half h takes
+// packed words U h .. U h + U - 1 of the step (one 4U-byte load) and the
 // matching 8 U activations (one contiguous 16U-byte load), and MFMA u uses
 // word U h + u -- A and B agree on every K index, which is all the product
-// needs.  Operands are read PD macro steps ahead into a ring of PD + 1 slots.
+// needs.  Two steps form a body, which never crosses a group (32 U divides
+// g); each body's sum is scaled into the accumulators at its end (the same
+// as once per group, up to fp32 rounding).  The main loop is branch-free:
+// operands are read three steps ahead into a ring of four slots (two bodies
+// per iteration), and each body's scale and zero a body ahead.
+// (Used for more than 32 tokens; fewer take the few-token kernels below.)
 template <int U>
 struct WordsT;
+template <>
+struct WordsT<1> {
+    typedef uint32_t T;
+};
 template <>
 struct WordsT<2> {
     typedef uint2 T;
@@ -100,18 +137,20 @@ template <>
 struct WordsT<4> {
     typedef uint4 T;
 };
+__device__ __forceinline__ uint32_t word_at(const uint32_t &w, int) { return w; }
 __device__ __forceinline__ uint32_t word_at(const uint2 &w, int u) { return u == 0 ? w.x : w.y; }
 __device__ __forceinline__ uint32_t word_at(const uint4 &w, int u) { return u == 0 ? w.x : (u == 1 ? w.y : (u == 2 ? w.z : w.w)); }
 
-template <int TM, int U, int PD>
+template <int TM, int U>
 __global__ __launch_bounds__(kThreads) void w4a16_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                          int64_t d_in, const uint32_t *__restrict__ packed, int64_t ldp,
                                                          const float *__restrict__ scales,
                                                          const float *__restrict__ zeros, int64_t g, int64_t ng,
                                                          int64_t d_out, int64_t kspan, float *__restrict__ out,
                                                          int64_t ldo, int64_t split_stride) {
-    constexpr int KS = 16 * U;  // K columns per macro step
-    constexpr int NS = PD + 1;  // ring slots
+    constexpr int KS = 16 * U;  // K columns per step
+    constexpr int BL = 2 * KS;  // K columns per body
+    constexpr int NS = 4;       // ring slots: operands are read NS - 1 steps ahead
     typedef typename WordsT<U>::T Words;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int half = lane >> 5;
@@ -121,12 +160,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const _Float16 *__restr
     const int64_t kb = (int64_t)blockIdx.z * kspan;
     const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
     if (kb >= ke) return;  // uniform over the workgroup
+    const int64_t nsteps = (ke - kb) / KS, nbody = nsteps / 2;
     const uint32_t *brow = packed + oc * ldp + U * half;  // + k / 8
     const _Float16 *arow[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
         const int64_t m = m0 + 32 * t + (lane & 31);
-        arow[t] = X + (m < M ? m : M - 1) * ldx + 8 * U * half;  // + k
+        const int64_t mc = m < M ? m : M - 1;
+        arow[t] = X + mc * ldx + 8 * U * half;  // + k
     }
     floatx16 acc[TM], accg[TM];
 #pragma unroll
@@ -134,60 +175,75 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const _Float16 *__restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = accg[t][r] = 0.0f;
 
-    int64_t grp = kb / g;
-    int64_t gend = std::min<int64_t>((grp + 1) * g, ke);
     const float *srow = scales + oc * ng, *zrow = zeros + oc * ng;
-    float s = srow[grp];
-    f16x2 bias;
-    bias[0] = bias[1] = (_Float16)(1024.0f + zrow[grp]);
-    // the next group's scale and zero are read a group ahead
-    const int64_t gn0 = grp + 1 < ng ? grp + 1 : grp;
-    float s_n = srow[gn0], z_n = zrow[gn0];
+    auto body_group = [&](int64_t b) {  // clamped: reads past the end are harmless
+        const int64_t bb = b < nbody ? b : nbody - 1;
+        return (kb + bb * BL) / g;
+    };
+    // scale and zero of the even and the odd body of an iteration
+    float se = srow[body_group(0)], ze = zrow[body_group(0)];
+    float so = srow[body_group(1)], zo = zrow[body_group(1)];
 
     Words bw[NS];
     f16x8 a[NS][TM][U];
-    auto load = [&](int slot, int64_t k) {  // k < ke
+    auto load = [&](int slot, int64_t step) {
+        const int64_t k = kb + (step < nsteps ? step : nsteps - 1) * KS;
         bw[slot] = *reinterpret_cast<const Words *>(brow + k / 8);
 #pragma unroll
         for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int u = 0; u < U; ++u) a[slot][t][u] = *reinterpret_cast<const f16x8 *>(arow[t] + k + 8 * u);
     };
+    uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
+    asm volatile("" : "+v"(magic));
+    auto mma = [&](int slot, const Bias &bias) {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) load(p, std::min<int64_t>(kb + p * KS, ke - KS));
-
-    for (int64_t k0 = kb; k0 < ke; k0 += NS * KS) {
+        for (int u = 0; u < U; ++u) {
+            const f16x8 b = dequant8(word_at(bw[slot], u), bias, magic);
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            const int64_t k = k0 + st * KS;
-            if (k < ke) {  // uniform
-                // read PD steps ahead (the last steps re-read the final step: always in bounds)
-                load((st + PD) % NS, std::min<int64_t>(k + PD * KS, ke - KS));
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const f16x8 b = dequant8(word_at(bw[st], u), bias);
-#pragma unroll
-                    for (int t = 0; t < TM; ++t)
-                        accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[st][t][u], b, accg[t], 0, 0, 0);
-                }
-                if (k + KS >= gend) {  // the group (or this split's part of it) ends: fold in its scale
-#pragma unroll
-                    for (int t = 0; t < TM; ++t)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            acc[t][r] = fmaf(s, accg[t][r], acc[t][r]);
-                            accg[t][r] = 0.0f;
-                        }
-                    ++grp;
-                    gend = std::min<int64_t>(gend + g, ke);
-                    s = s_n;
-                    bias[0] = bias[1] = (_Float16)(1024.0f + z_n);
-                    const int64_t gn = grp + 1 < ng ? grp + 1 : ng - 1;
-                    s_n = srow[gn];
-                    z_n = zrow[gn];
-                }
-            }
+            for (int t = 0; t < TM; ++t) accg[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[slot][t][u], b, accg[t], 0, 0, 0);
         }
+    };
+    auto fold = [&](float sc) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc[t][r] = fmaf(sc, accg[t][r], acc[t][r]);
+                accg[t][r] = 0.0f;
+            }
+    };
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) load(p, p);
+
+    int64_t step = 0;
+    for (int64_t b = 0; b + 2 <= nbody; b += 2, step += 4) {
+        {  // even body: steps 0, 1
+            const Bias bias = bias_of(ze);
+            load(3, step + 3);
+            mma(0, bias);
+            load(0, step + 4);
+            mma(1, bias);
+            fold(se);
+            se = srow[body_group(b + 2)];
+            ze = zrow[body_group(b + 2)];
+        }
+        {  // odd body: steps 2, 3
+            const Bias bias = bias_of(zo);
+            load(1, step + 5);
+            mma(2, bias);
+            load(2, step + 6);
+            mma(3, bias);
+            fold(so);
+            so = srow[body_group(b + 3)];
+            zo = zrow[body_group(b + 3)];
+        }
+    }
+    if (nbody & 1) {  // the last body (slots 0 and 1 hold its operands)
+        const Bias bias = bias_of(ze);
+        mma(0, bias);
+        mma(1, bias);
+        fold(se);
     }
     if (o >= d_out) return;
     float *dst = out + (int64_t)blockIdx.z * split_stride + o;
@@ -198,6 +254,284 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const _Float16 *__restr
             const int64_t m = m0 + 32 * t + mfma32_row(r, lane);
             if (m < M) dst[m * ldo] = acc[t][r];
         }
+}
+
+// Staging of the few-token kernels: the workgroup's rows of X over [kb, ke)
+// into xs (rows ldxs halves apart), and the scales and zeros of its 128
+// features over groups g0 .. g0 + ngs - 1 into sz ([group][feature][scale,
+// zero]).  Every load is issued before the first store (batches of 8 pieces of
+// X; one feature's contiguous run of scales or of zeros per thread), so the
+// staging costs about one memory latency.  ngs <= kMaxGroups.
+constexpr int kMaxGroups = 32;
+__device__ __forceinline__ void stage_few(const _Float16 *__restrict__ X, int64_t ldx, int64_t M, int64_t kb,
+                                          int64_t ke, _Float16 *xs, int64_t ldxs, const float *__restrict__ scales,
+                                          const float *__restrict__ zeros, int64_t ng, int64_t n0, int64_t d_out,
+                                          int64_t g0, int64_t ngs, float *sz) {
+    const int tid = threadIdx.x;
+    {
+        const int f = tid >> 1;  // feature of the tile; tid & 1: scales or zeros
+        const int64_t of = n0 + f < d_out ? n0 + f : d_out - 1;
+        const float *src = ((tid & 1) ? zeros : scales) + of * ng + g0;
+        float v[kMaxGroups];
+#pragma unroll
+        for (int j = 0; j < kMaxGroups; ++j)
+            if (j < ngs) v[j] = src[j];
+#pragma unroll
+        for (int j = 0; j < kMaxGroups; ++j)
+            if (j < ngs) sz[(j * kTileN + f) * 2 + (tid & 1)] = v[j];
+    }
+    const int64_t chunks = (ke - kb) / 8;  // 16-byte pieces per row
+    const int64_t n = M * chunks;
+    for (int64_t i0 = 0; i0 < n; i0 += 8 * kThreads) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = i0 + u * kThreads + tid;
+            const int64_t ic = i < n ? i : n - 1;
+            v[u] = *reinterpret_cast<const uint4 *>(X + (ic / chunks) * ldx + kb + 8 * (ic % chunks));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = i0 + u * kThreads + tid;
+            if (i < n) *reinterpret_cast<uint4 *>(xs + (i / chunks) * ldxs + 8 * (i % chunks)) = v[u];
+        }
+    }
+}
+
+// Few tokens (M <= 32): the product is a stream of packed weights.  The
+// workgroup first stages in LDS its rows of X over [kb, ke) and the scales and
+// zeros of its 128 features over the groups the range touches; the loop then
+// issues one global load per step (the lane's packed words), kNB - 1 steps
+// ahead through a ring of kNB slots, reads the activation operand from LDS
+// one step ahead, and folds each two-step body with its group's scale.
+// Bodies past the end of the range (the last chunk of kNB steps may overrun
+// it) read clamped addresses and fold with scale 0, so the loop has no
+// branches.  Lane layout and K order are those of w4a16_kernel.
+constexpr int kNB = 8;  // packed-word ring slots (steps of look-ahead + 1)
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void w4a16_few_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
+                                                             int64_t d_in, const uint32_t *__restrict__ packed,
+                                                             int64_t ldp, const float *__restrict__ scales,
+                                                             const float *__restrict__ zeros, int64_t g, int64_t ng,
+                                                             int64_t d_out, int64_t kspan, float *__restrict__ out,
+                                                             int64_t ldo, int64_t split_stride) {
+    constexpr int KS = 16 * U;  // K columns per step
+    constexpr int BL = 2 * KS;  // K columns per body
+    typedef typename WordsT<U>::T Words;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int half = lane >> 5;
+    const int64_t n0 = (int64_t)blockIdx.x * kTileN;
+    const int fl = wave * 32 + (lane & 31);  // feature within the tile
+    const int64_t o = n0 + fl;
+    const int64_t oc = o < d_out ? o : d_out - 1;
+    const int64_t kb = (int64_t)blockIdx.z * kspan;
+    const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
+    if (kb >= ke) return;  // uniform over the workgroup
+    const int64_t nsteps = (ke - kb) / KS, nbody = nsteps / 2;
+    const int64_t g0 = kb / g, ngs = (ke - 1) / g - g0 + 1;  // groups the range touches
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int64_t ldxs = kspan + 8;  // halves; the pad staggers the banks
+    _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
+    float2 *szs = reinterpret_cast<float2 *>(smem + align_up((size_t)M * (size_t)ldxs * 2, 16));  // [group][feature]
+    stage_few(X, ldx, M, kb, ke, xs, ldxs, scales, zeros, ng, n0, d_out, g0, ngs, reinterpret_cast<float *>(szs));
+    __syncthreads();
+
+    const uint32_t *brow = packed + oc * ldp + U * half + kb / 8;  // + 2 U step
+    const int64_t mc = (lane & 31) < M ? (lane & 31) : M - 1;
+    const _Float16 *arow = xs + mc * ldxs + 8 * U * half;  // + KS step
+    floatx16 acc, accg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = accg[r] = 0.0f;
+    uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
+    asm volatile("" : "+v"(magic));
+
+    Words bw[kNB];
+    f16x8 a[2][U];
+    auto load_b = [&](int slot, int64_t st) { bw[slot] = *reinterpret_cast<const Words *>(brow + 2 * U * (st < nsteps ? st : nsteps - 1)); };
+    auto load_a = [&](int slot, int64_t st) {
+        const int64_t sc = st < nsteps ? st : nsteps - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[slot][u] = *reinterpret_cast<const f16x8 *>(arow + KS * sc + 8 * u);
+    };
+    auto body_sz = [&](int64_t b) {  // scale (0 past the end) and zero of body b
+        const int64_t bc = b < nbody ? b : nbody - 1;
+        float2 v = szs[((kb + bc * BL) / g - g0) * kTileN + fl];
+        if (b >= nbody) v.x = 0.0f;
+        return v;
+    };
+#pragma unroll
+    for (int p = 0; p < kNB - 1; ++p) load_b(p, p);
+    load_a(0, 0);
+
+    for (int64_t base = 0; base < nsteps; base += kNB) {
+#pragma unroll
+        for (int st = 0; st < kNB; st += 2) {  // one body: steps base + st, base + st + 1
+            const float2 sz = body_sz((base + st) / 2);
+            const Bias bias = bias_of(sz.y);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int s = st + h;
+                load_b((s + kNB - 1) % kNB, base + s + kNB - 1);
+                load_a((s + 1) & 1, base + s + 1);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const f16x8 b = dequant8(word_at(bw[s], u), bias, magic);
+                    accg = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s & 1][u], b, accg, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc[r] = fmaf(sz.x, accg[r], acc[r]);
+                accg[r] = 0.0f;
+            }
+        }
+    }
+    if (o >= d_out) return;
+    float *dst = out + (int64_t)blockIdx.z * split_stride + o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = mfma32_row(r, lane);
+        if (m < M) dst[m * ldo] = acc[r];
+    }
+}
+
+// Few tokens with groups of a multiple of 128: the weight stream in 64-byte
+// pieces.  K advances in chunks of 256 columns (32 packed words of a row).
+// Lane half h loads words 16 h .. 16 h + 15 of the chunk (64 contiguous bytes;
+// rows read this way stream near full bandwidth, where 16-byte pieces of many
+// rows do not), i.e. half 0 holds the chunk's first group-aligned 128 columns
+// (A) and half 1 its second (B).  v_permlane32_swap then trades the upper
+// halves of A for the lower halves of B between the two lane halves, so that
+// each half holds 8 words of A and 8 of B: half h takes words 8 h .. 8 h + 7
+// of each, and MFMA i of a 128-column body uses word 8 h + i (columns
+// 64 h + 8 i .. + 7), both halves in one group.  The next chunk's words and its
+// two bodies' scales and zeros are read while the current chunk is used; the
+// activation operand comes from LDS, staged once (IL: straight from X, put in
+// the operand order on the way).  Bodies past the end fold with scale 0.
+template <bool IL>
+__global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
+                                                               int64_t d_in, const uint32_t *__restrict__ packed,
+                                                               int64_t ldp, const float *__restrict__ scales,
+                                                               const float *__restrict__ zeros, int64_t g, int64_t ng,
+                                                               int64_t d_out, int64_t kspan, float *__restrict__ out,
+                                                               int64_t ldo, int64_t split_stride) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int half = lane >> 5;
+    const int64_t o = (int64_t)blockIdx.x * kTileN + wave * 32 + (lane & 31);
+    const int64_t oc = o < d_out ? o : d_out - 1;
+    const int64_t kb = (int64_t)blockIdx.z * kspan;
+    const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
+    if (kb >= ke) return;  // uniform over the workgroup
+    const int64_t nbody = (ke - kb) / 128, nchunks = (nbody + 1) / 2;
+
+    // this lane's 64 bytes of chunk c: words 32 c + 16 h .. + 15 past kb, clamped into [kb, ke)
+    const uint32_t *brow = packed + oc * ldp + kb / 8;
+    const int64_t wlast = (ke - kb) / 8 - 16;  // last 16-word piece that stays inside the range
+    const float *srow = scales + oc * ng, *zrow = zeros + oc * ng;
+    uint4 q[2][4];
+    float2 sz[2][2];  // [slot][body of the chunk]: scale (0 past the end), zero
+    auto load = [&](int slot, int64_t c) {
+        const int64_t cc = c < nchunks ? c : nchunks - 1;
+        const int64_t w = std::min<int64_t>(32 * cc + 16 * half, wlast);
+        const uint4 *p = reinterpret_cast<const uint4 *>(brow + w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[slot][j] = p[j];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t b = 2 * c + h, bc = b < nbody ? b : nbody - 1;
+            const int64_t gi = (kb + 128 * bc) / g;
+            sz[slot][h] = make_float2(srow[gi], zrow[gi]);
+        }
+    };
+    load(0, 0);  // the first chunk is in flight during the staging
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int64_t ldxs = kspan + 8;  // halves; the pad staggers the banks
+    _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
+    {  // rows of X over [kb, ke) into LDS, every load issued before the first store
+        const int64_t chunks = (ke - kb) / 8;  // 16-byte pieces per row
+        const int64_t n = M * chunks;
+        for (int64_t i0 = 0; i0 < n; i0 += 8 * kThreads) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + u * kThreads + threadIdx.x;
+                const int64_t ic = i < n ? i : n - 1;
+                v[u] = *reinterpret_cast<const uint4 *>(X + (ic / chunks) * ldx + kb + 8 * (ic % chunks));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + u * kThreads + threadIdx.x;
+                uint4 w = v[u];
+                if constexpr (IL) {  // halves 0..7 -> 0, 4, 1, 5, 2, 6, 3, 7
+                    w = make_uint4(__builtin_amdgcn_perm(v[u].z, v[u].x, 0x05040100u), __builtin_amdgcn_perm(v[u].z, v[u].x, 0x07060302u),
+                                   __builtin_amdgcn_perm(v[u].w, v[u].y, 0x05040100u), __builtin_amdgcn_perm(v[u].w, v[u].y, 0x07060302u));
+                }
+                if (i < n) *reinterpret_cast<uint4 *>(xs + (i / chunks) * ldxs + 8 * (i % chunks)) = w;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int64_t mc = (lane & 31) < M ? (lane & 31) : M - 1;
+    const _Float16 *arow = xs + mc * ldxs + 64 * half;  // + 128 body + 8 i
+    floatx16 acc, accg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = accg[r] = 0.0f;
+    uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
+    asm volatile("" : "+v"(magic));
+
+    auto swap = [&](uint4 &x, uint4 &y) {  // x's upper lane half <-> y's lower lane half
+        uint32_t xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const auto r = __builtin_amdgcn_permlane32_swap(xv[j], yv[j], false, false);
+            xv[j] = r[0];
+            yv[j] = r[1];
+        }
+        x = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+        y = make_uint4(yv[0], yv[1], yv[2], yv[3]);
+    };
+    auto body = [&](const uint4 &w0, const uint4 &w1, int64_t b, float2 v) {  // 128 columns, words w0 (i < 4), w1
+        const int64_t bc = b < nbody ? b : nbody - 1;
+        const float s = b < nbody ? v.x : 0.0f;
+        const Bias bias = bias_of(v.y);
+        const _Float16 *ap = arow + 128 * bc;
+        f16x8 a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f16x8 *>(ap + 8 * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 &wv = i < 4 ? w0 : w1;
+            const f16x8 bq = dequant8(word_at(wv, i & 3), bias, magic);
+            accg = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bq, accg, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc[r] = fmaf(s, accg[r], acc[r]);
+            accg[r] = 0.0f;
+        }
+    };
+    for (int64_t c = 0; c < nchunks; c += 2) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            load(sl ^ 1, c + sl + 1);
+            uint4(&w)[4] = q[sl];
+            swap(w[0], w[2]);
+            swap(w[1], w[3]);
+            body(w[0], w[1], 2 * (c + sl), sz[sl][0]);
+            body(w[2], w[3], 2 * (c + sl) + 1, sz[sl][1]);
+        }
+    }
+    if (o >= d_out) return;
+    float *dst = out + (int64_t)blockIdx.z * split_stride + o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = mfma32_row(r, lane);
+        if (m < M) dst[m * ldo] = acc[r];
+    }
 }
 
 // Y[m][o] = sum over splits of P[split][m][o], splits in order.
@@ -213,8 +547,13 @@ __global__ __launch_bounds__(kThreads) void split_sum_kernel(const float *__rest
 
 int64_t xp_ld(int64_t d_in) { return (d_in + 7) / 8 * 8; }
 
+constexpr size_t kXlBytes = 32768;  // LDS budget for the activations of one workgroup
+
 struct GemmPlan {
     int tm, u;
+    bool xl;           // few tokens (M <= 32): activations through LDS
+    bool chunk;        // few tokens, groups of a multiple of 128: w4a16_chunk_kernel
+    size_t lds_bytes;  // dynamic LDS per workgroup (few-token kernels)
     int64_t n_tiles, m_tiles, splits, kspan;
     size_t xp_bytes, part_bytes;
 };
@@ -222,15 +561,34 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     GemmPlan p;
     p.tm = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
-    p.u = g % 64 == 0 ? 4 : 2;  // a macro step stays inside one group
+    p.u = g % 128 == 0 ? 4 : (g % 64 == 0 ? 2 : 1);  // a body (32 U columns) stays inside one group
     p.n_tiles = ceil_div(d_out, kTileN);
     p.m_tiles = ceil_div(M, 32 * p.tm);
     // about four workgroups per CU; a split keeps at least 256 K values
     const int64_t tiles = p.n_tiles * p.m_tiles;
     int64_t sp = tiles >= 1024 ? 1 : ceil_div(1024, tiles);
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
-    p.kspan = ceil_div(ceil_div(d_in, sp), 16 * p.u) * 16 * p.u;
+    p.xl = M <= 32;
+    p.chunk = p.xl && p.u == 4;
+    if (p.chunk) {  // the activations of a whole split in 32 KB of LDS; no more splits than that needs
+        const int64_t kmax = std::max<int64_t>(128, (int64_t)(kXlBytes / (2 * M)) - 8);
+        sp = ceil_div(d_in, kmax);
+    } else if (p.xl) {  // at most 32 KB of activations and 32 groups of scales per workgroup: more splits if needed
+        const int64_t kmax = std::max<int64_t>(32 * p.u, std::min<int64_t>((int64_t)(kXlBytes / (2 * M)) - 8, 30 * g));
+        sp = std::max<int64_t>(sp, ceil_div(d_in, kmax));
+    }
+    p.kspan = ceil_div(ceil_div(d_in, sp), 32 * p.u) * 32 * p.u;  // whole bodies
+    if (p.chunk)
+        while ((size_t)M * (size_t)(p.kspan + 8) * 2 > kXlBytes && p.kspan > 128) p.kspan -= 128;
+    else if (p.xl)
+        while (((size_t)M * (size_t)(p.kspan + 8) * 2 > kXlBytes || p.kspan > 30 * g) && p.kspan > 32 * p.u)
+            p.kspan -= 32 * p.u;
     p.splits = ceil_div(d_in, p.kspan);
+    // activations, then float2 (scale, zero) for 128 features x the groups a range touches
+    // (a range touches at most kspan / g + 2 <= kMaxGroups groups)
+    p.lds_bytes = p.chunk ? (size_t)M * (size_t)(p.kspan + 8) * 2
+                : p.xl  ? align_up((size_t)M * (size_t)(p.kspan + 8) * 2, 16) + (size_t)(p.kspan / g + 2) * kTileN * 8
+                        : 0;
     p.xp_bytes = align_up((size_t)M * (size_t)xp_ld(d_in) * 2, 256);
     p.part_bytes = p.splits > 1 ? align_up((size_t)p.splits * (size_t)M * (size_t)d_out * 4, 256) : 0;
     return p;
@@ -259,7 +617,7 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
     const _Float16 *Xk = static_cast<const _Float16 *>(X);
     int64_t ldk = ldx;
     hipError_t e;
-    if (kperm) {  // columns of X into the packed order, once
+    if (kperm || !p.chunk) {  // columns of X into the operand order (and the packed order), once
         uint16_t *Xp = reinterpret_cast<uint16_t *>(wsb);
         const dim3 grid((unsigned)ceil_div(d_in, kThreads), (unsigned)std::min<int64_t>(M, 65535));
         hipLaunchKernelGGL(gather_cols_kernel, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(X), ldx, M, d_in,
@@ -274,24 +632,31 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
     const int64_t ldo = p.splits > 1 ? d_out : ldy;
     const int64_t stride = p.splits > 1 ? M * d_out : 0;
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.m_tiles, (unsigned)p.splits);
-#define W4A16_LAUNCH(TM, U, PD)                                                                                 \
-    hipLaunchKernelGGL((w4a16_kernel<TM, U, PD>), grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales, \
+#define W4A16_LAUNCH(TM, U)                                                                                     \
+    hipLaunchKernelGGL((w4a16_kernel<TM, U>), grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales, \
                        zeros, g, ng, d_out, p.kspan, out, ldo, stride)
+#define W4A16_TM(U)                                                                                              \
+    if (p.chunk && !kperm)                                                                                       \
+        hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
+                           ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \
+    else if (p.chunk)                                                                                            \
+        hipLaunchKernelGGL(w4a16_chunk_kernel<false>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
+                           ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \
+    else if (p.xl)                                                                                               \
+        hipLaunchKernelGGL((w4a16_few_kernel<U>), grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, ldp, \
+                           scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                            \
+    else if (p.tm == 2)                                                                                          \
+        W4A16_LAUNCH(2, U);                                                                                      \
+    else                                                                                                         \
+        W4A16_LAUNCH(4, U);
     if (p.u == 4) {
-        if (p.tm == 1)
-            W4A16_LAUNCH(1, 4, 2);
-        else if (p.tm == 2)
-            W4A16_LAUNCH(2, 4, 1);
-        else
-            W4A16_LAUNCH(4, 4, 1);
+        W4A16_TM(4)
+    } else if (p.u == 2) {
+        W4A16_TM(2)
     } else {
-        if (p.tm == 1)
-            W4A16_LAUNCH(1, 2, 2);
-        else if (p.tm == 2)
-            W4A16_LAUNCH(2, 2, 1);
-        else
-            W4A16_LAUNCH(4, 2, 1);
+        W4A16_TM(1)
     }
+#undef W4A16_TM
 #undef W4A16_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.splits > 1) {

@@ -67,6 +67,9 @@ def _layer(rng, d_out, d_in, group):
     (40, 128, 768, 0, False),       # one group per row; two token blocks
     (200, 160, 1024, 128, True),    # four token blocks, ragged
     (7, 96, 8192, 128, False),      # long K: split over K
+    (2, 130, 384, 128, True),       # half a 256-column chunk at the end; column gather
+    (5, 64, 640, 128, False),       # odd number of 128-column bodies
+    (32, 200, 1024, 256, False),    # groups spanning two bodies
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
