@@ -74,7 +74,8 @@ typedef enum {
     GPTQ_OP_PREPARE = 1,
     GPTQ_OP_QUANTIZE = 2,
     GPTQ_OP_LOSS = 3,
-    GPTQ_OP_W4A16 = 4 /* n_tok = M, the rows of X */
+    GPTQ_OP_W4A16 = 4, /* n_tok = M, the rows of X */
+    GPTQ_OP_HESSIAN_TOKENS = 5
 } gptq_op;
 
 /*
@@ -129,6 +130,26 @@ typedef struct {
 GPTQ_API gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void *X, gptq_dtype x_dtype,
                                     int64_t d_in, int64_t n_tok, int64_t ldx,
                                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step 1 from token-major activations, as a layer's inputs arrive during
+ * calibration (page "量化经典：LLM.int8 / GPTQ / AWQ", §二 step 1; page "LLM
+ * 量化方法原理与实现详解", §4.1: H = 2 X X^T over all calibration tokens).
+ * Same result as gptq_hessian_accumulate on the transposed activations.
+ *
+ *   H      [d_in][d_in] fp32 in/out, upper triangle: H[i][j] += 2 sum_t X[t][i] X[t][j].
+ *   hdiag  [d_in] fp64 in/out or NULL, as in gptq_hessian_accumulate.
+ *   X      [n_tok][ldx] one row per token, d_in channels used per row; bf16
+ *          (raw 16-bit patterns) or fp32; 4-byte aligned, ldx >= d_in.
+ *   ws     scratch of gptq_workspace_bytes(GPTQ_OP_HESSIAN_TOKENS, 0, d_in, n_tok, NULL):
+ *          a channel-major panel of at most 65536 tokens plus the SYRK's own scratch.
+ * Tokens are taken in blocks of 65536, each transposed into the panel and
+ * accumulated in turn; repeated calls accumulate further chunks.  The sums
+ * equal those of gptq_hessian_accumulate called once per such block.
+ */
+GPTQ_API gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *X, gptq_dtype x_dtype,
+                                                    int64_t d_in, int64_t n_tok, int64_t ldx, void *ws,
+                                                    size_t ws_bytes, hipStream_t stream);
 
 /*
  * Steps 2-3 -- column order, damping and the inverse-Hessian factor.

@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_PKG, "libgptq.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16 = 0, 1, 2, 3, 4
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16, OP_HESSIAN_TOKENS = 0, 1, 2, 3, 4, 5
 
 EXPORTED = (
     "gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_rtn_quantize",
     "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
-    "gptq_pack_codes", "gptq_w4a16_gemm",
+    "gptq_pack_codes", "gptq_w4a16_gemm", "gptq_hessian_accumulate_tokens",
 )
 
 
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_layer_loss": [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, vp],
         "gptq_workspace_bytes": [ctypes.c_int, i64, i64, i64, cfgp, ctypes.POINTER(sz)],
         "gptq_pack_codes": [vp, i64, i64, i32, vp, vp, vp],
+        "gptq_hessian_accumulate_tokens": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
         "gptq_w4a16_gemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i64, vp, i64, vp, sz, vp],
         "gptq_status_string": [ctypes.c_int],
         "gptq_last_error": [],
@@ -135,6 +136,25 @@ def hessian_accumulate(H, X, hdiag=None, ws=None, stream=None) -> None:
         ws = _workspace(workspace_bytes(OP_HESSIAN, 0, d, n), X.device)
     _check(load_library().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), _ptr(X), dt, d, n, X.stride(0), _ptr(ws),
                                                   ws.numel(), _stream(stream)))
+
+
+def hessian_accumulate_tokens(H, X, hdiag=None, ws=None, stream=None) -> None:
+    """H (fp32 [d,d], upper) += 2 X^T X for token-major X: bf16 or fp32 [n_tok][d], one row per token."""
+    import torch
+    _need_cuda(H, hdiag)
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit stride along channels")
+    if X.dtype == torch.bfloat16:
+        dt = DT_BF16
+    elif X.dtype == torch.float32:
+        dt = DT_F32
+    else:
+        raise ValueError("X must be bfloat16 or float32")
+    n, d = X.shape
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_HESSIAN_TOKENS, 0, d, n), X.device)
+    _check(load_library().gptq_hessian_accumulate_tokens(_ptr(H), _ptr(hdiag), _ptr(X), dt, d, n, X.stride(0),
+                                                         _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def prepare_hinv(H, cfg: Config, U, perm=None, info=None, hdiag=None, ws=None, stream=None):

@@ -76,6 +76,10 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
     case GPTQ_OP_LOSS:
         *out = gptq::loss_ws_bytes(d_out, d_in);
         return GPTQ_OK;
+    case GPTQ_OP_HESSIAN_TOKENS:
+        *out = gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
+        if (n_tok > 0) *out = std::max(*out, gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_F32));
+        return GPTQ_OK;
     case GPTQ_OP_W4A16:  // the largest plan over the group sizes (the plan depends on g only through 32, 64, 128 | g)
         *out = std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 32),
                         std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 64), gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 128)));
@@ -99,6 +103,22 @@ gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void *X, gptq
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, ws, stream), fn);
+}
+
+gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *X, gptq_dtype x_dtype, int64_t d_in,
+                                           int64_t n_tok, int64_t ldx, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_hessian_accumulate_tokens";
+    if (d_in <= 0 || n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: d_in must be > 0 and n_tok >= 0", fn);
+    if (x_dtype != GPTQ_DT_F32 && x_dtype != GPTQ_DT_BF16) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    if (ldx < d_in) return fail(GPTQ_ERR_INVALID_ARG, "%s: ldx < d_in", fn);
+    if (!H || (n_tok > 0 && !X)) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(H) || (X && !aligned(X, 4)) || (hdiag && !aligned(hdiag, 8)))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (n_tok == 0) return GPTQ_OK;
+    const size_t need = gptq::hessian_tokens_ws_bytes(d_in, n_tok, x_dtype);
+    if (!ws || ws_bytes < need)
+        return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_hessian_tokens(H, hdiag, X, x_dtype, d_in, n_tok, ldx, ws, stream), fn);
 }
 
 gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg, float *U,

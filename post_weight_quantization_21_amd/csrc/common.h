@@ -62,6 +62,11 @@ size_t hessian_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt);
 hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, int64_t d_in, int64_t n_tok,
                        int64_t ldx, void *ws, hipStream_t s);
 
+// token-major activations (hessian_tokens.hip)
+size_t hessian_tokens_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt);
+hipError_t run_hessian_tokens(float *H, double *hdiag, const void *X, gptq_dtype dt, int64_t d_in, int64_t n_tok,
+                              int64_t ldx, void *ws, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Prepare (prepare.hip)
 // ---------------------------------------------------------------------------
