@@ -28,6 +28,9 @@ Steps, in the pages' order:
    and the undamped H (page "LLM 量化方法原理与实现详解", §4.1 objective).
 7. ``pack_codes`` / ``w4a16_matmul``: the codes as little-endian bit streams and
    the product of 16-bit activations with the dequantized 4-bit weights.
+8. ``awq_search`` / ``smooth_scales`` / ``scale_layer``: the per-channel scaling
+   pre-passes (page "LLM 量化方法原理与实现详解", §4.2 AWQ and §4.3 SmoothQuant)
+   and the equivalent problem (W diag(s), diag(s)^-1 H diag(s)^-1) GPTQ then solves.
 
 Every function is pinned by ``tests/test_oracle_*.py`` (closed forms, special
 cases, invariants, brute force and the pages' worked example).
@@ -290,6 +293,66 @@ def dequant(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int
     s = scales[:, gi]
     z = zeros[:, gi]
     return ((codes.astype(np.float32) - z) * s).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# before the pass: per-channel scaling (AWQ search, SmoothQuant migration)
+# ----------------------------------------------------------------------------
+def channel_stats(X: np.ndarray):
+    """Per input channel over the tokens: (max |x|, mean |x|), X [d_in][n_tok] (bf16 bits or fp32)."""
+    A = np.abs(widen(X))
+    return A.max(axis=1), A.mean(axis=1)
+
+
+def weight_stats(W: np.ndarray):
+    """Per input column over the output rows: (max |w|, mean |w|)."""
+    A = np.abs(np.asarray(W, dtype=np.float64))
+    return A.max(axis=0), A.mean(axis=0)
+
+
+def awq_scales(act_mean, w_mean, alpha: float) -> np.ndarray:
+    """s_j = (mean|X_j| / mean|W_j|)^alpha in fp32 (page "LLM 量化方法原理与实现详解", §4.2, the
+    printed AWQ sketch), kept at least 1e-5; a column whose weights are all zero gets s = 1."""
+    a = np.asarray(act_mean, dtype=np.float32)
+    w = np.asarray(w_mean, dtype=np.float32)
+    r = np.where(w > 0, a / np.where(w > 0, w, np.float32(1)), np.float32(1)).astype(np.float32)
+    s = np.power(r, np.float32(alpha), dtype=np.float32)
+    return np.maximum(s, np.float32(1e-5)).astype(np.float32)
+
+
+def smooth_scales(act_max, w_max, alpha: float = 0.5) -> np.ndarray:
+    """s_j = max|X_j|^alpha / max|W_j|^(1 - alpha), kept at least 1e-5 (§4.3, SmoothQuant sketch), fp32."""
+    a = np.asarray(act_max, dtype=np.float32)
+    w = np.asarray(w_max, dtype=np.float32)
+    num = np.power(a, np.float32(alpha), dtype=np.float32)
+    den = np.power(w, np.float32(1.0 - alpha), dtype=np.float32)
+    s = np.where(den > 0, num / np.where(den > 0, den, np.float32(1)), np.float32(1)).astype(np.float32)
+    return np.maximum(s, np.float32(1e-5)).astype(np.float32)
+
+
+def scale_layer(W: np.ndarray, H: np.ndarray, s):
+    """The equivalent problem after X' = X diag(s)^-1, W' = W diag(s): W' in fp32 (the scaled weights
+    are what gets quantized), H' = diag(s)^-1 H diag(s)^-1 = 2 X' X'^T in fp64."""
+    s32 = np.asarray(s, dtype=np.float32)
+    Ws = (np.asarray(W, dtype=np.float32) * s32[None, :]).astype(np.float32)
+    inv = 1.0 / s32.astype(np.float64)
+    return Ws, np.asarray(H, dtype=np.float64) * np.outer(inv, inv)
+
+
+def awq_search(W: np.ndarray, H: np.ndarray, act_mean, bits: int, sym: bool, group: int, n_grid: int = 20):
+    """AWQ's scale search (§4.2): for alpha = i / n_grid, i < n_grid, quantize W diag(s) to the nearest
+    grid point and measure ||(Q(W diag(s)) diag(s)^-1 - W) X||^2 through H; the smallest loss wins
+    (the first on ties).  Returns (alphas, losses, best index, s of the best)."""
+    _, w_mean = weight_stats(W)
+    alphas = [i / n_grid for i in range(n_grid)]
+    losses = []
+    for a in alphas:
+        s = awq_scales(act_mean, w_mean, a)
+        Ws, Hs = scale_layer(W, H, s)
+        r = rtn(Ws, bits, sym, group)
+        losses.append(layer_loss(Ws, dequant(r["codes"], r["scales"], r["zeros"], group), Hs))
+    best = int(np.argmin(losses))
+    return alphas, np.array(losses), best, awq_scales(act_mean, w_mean, alphas[best])
 
 
 # ----------------------------------------------------------------------------
