@@ -143,6 +143,54 @@ def bench_w4a16(args) -> int:
     return 0
 
 
+def bench_awq(args) -> int:
+    """AWQ's scale search on the workload's layer: per-channel |x| statistics (outside the timed
+    region, like H), then 20 alphas of scale, RTN and loss through the scaled H."""
+    import torch
+
+    import datagen
+    import post_weight_quantization_21_amd as gq
+
+    gq.load_library()
+    dev = torch.device("cuda:0")
+    lay = datagen.make_layer(args.workload)
+    d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
+    cfg = gq.config(lay["bits"], lay["sym"], lay["group"], lay["block"], lay["damp"], False)
+    Xd = torch.from_numpy(lay["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+    _, asum = gq.channel_stats(Xd)
+    H = torch.zeros(d_in, d_in, dtype=torch.float32, device=dev)
+    gq.hessian_accumulate(H, Xd)
+    del Xd
+    Wd = torch.from_numpy(lay["W"]).to(dev)
+    n_grid = 20
+    ws = torch.empty(gq.workspace_bytes(gq.OP_AWQ, d_out, d_in, 0, cfg), dtype=torch.uint8, device=dev)
+    run = lambda: gq.awq_search(Wd, H, asum, n, cfg, n_grid, ws=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        s, losses, best = run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    loss_flops = n_grid * 2.0 * d_out * d_in * d_in  # the loss's (W' - Q(W')) H' products, per search
+    tf = loss_flops / (ms * 1e-3) / 1e12
+    lv = losses.cpu().numpy()
+    out = {"metric": "awq_search_ms", "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic", "config": {"workload": args.workload + "_awq", "d_out": d_out, "d_in": d_in,
+                                           "n_grid": n_grid, "bits": lay["bits"], "group_size": lay["group"]},
+           "best_alpha": int(best.cpu()[0]) / n_grid, "loss_rtn": float(lv[0]), "loss_best": float(lv.min()),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 157.3, "unit": "TFLOP/s",
+                        "frac": round(tf / 157.3, 4), "traffic": None,
+                        "note": "loss flops over the whole search time (scaling and RTN included): a lower bound"},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +200,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a16", type=int, default=0, metavar="M",
                     help="instead: time the W4A16 product of M tokens with the packed 28672x8192 layer")
+    ap.add_argument("--awq", action="store_true",
+                    help="instead: time the AWQ scale search (20 alphas) on the workload's layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this benchmark runs GPTQ on one GPU only "
@@ -160,6 +210,8 @@ def main() -> int:
 
     if args.w4a16 > 0:
         return bench_w4a16(args)
+    if args.awq:
+        return bench_awq(args)
 
     import torch
 

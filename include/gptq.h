@@ -75,7 +75,9 @@ typedef enum {
     GPTQ_OP_QUANTIZE = 2,
     GPTQ_OP_LOSS = 3,
     GPTQ_OP_W4A16 = 4, /* n_tok = M, the rows of X */
-    GPTQ_OP_HESSIAN_TOKENS = 5
+    GPTQ_OP_HESSIAN_TOKENS = 5,
+    GPTQ_OP_SMOOTH = 6, /* gptq_smooth_scales */
+    GPTQ_OP_AWQ = 7     /* gptq_awq_search (cfg: bits, symmetric, group_size) */
 } gptq_op;
 
 /*
@@ -240,6 +242,42 @@ GPTQ_API gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const
                             const int32_t *g_idx, const float *H, int64_t d_out, int64_t d_in,
                             int32_t group_size, double *loss_dev, void *ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/*
+ * Per-channel scaling before the pass (page "LLM 量化方法原理与实现详解", §4.2
+ * AWQ and §4.3 SmoothQuant).  Both pick s[d_in] > 0 and hand GPTQ (or RTN)
+ * the equivalent problem W' = W diag(s), H' = diag(s)^-1 H diag(s)^-1; at
+ * inference the activations are divided by s (folded into the previous op).
+ *
+ * gptq_channel_stats: per input channel of X [d_in][ldx] (bf16 bit patterns
+ *   or fp32, n_tok tokens): absmax[c] = max(absmax[c], max_t |x|) (fp32) and
+ *   abssum[c] += sum_t |x| (fp64), both device arrays, accumulating over
+ *   calls (start them at 0).
+ * gptq_smooth_scales: s_j = max(act_absmax_j^alpha / max_r |W[r][j]|^(1-alpha), 1e-5)
+ *   (s_j = 1 when the denominator is 0), 0 <= alpha <= 1.
+ *   ws: gptq_workspace_bytes(GPTQ_OP_SMOOTH, d_out, d_in, 0, NULL).
+ * gptq_awq_search: for alpha = i / n_grid, i = 0 .. n_grid - 1, the scales
+ *   s_j = max((a_j / w_j)^alpha, 1e-5) with a_j = act_abssum_j / n_tok and
+ *   w_j = mean_r |W[r][j]| (s_j = 1 when w_j = 0); W' is rounded to the
+ *   nearest grid point (bits, symmetric, group_size of cfg, grids fitted on W')
+ *   and losses[i] = ||Q(W') diag(s)^-1 X - W X||^2, measured through H'
+ *   (H: the undamped upper triangle).  best = the first smallest loss; s gets
+ *   its scales.  All outputs are device pointers; nothing synchronizes.
+ *   1 <= n_grid <= 64.  ws: gptq_workspace_bytes(GPTQ_OP_AWQ, d_out, d_in, 0, cfg).
+ * gptq_scale_layer: in place, W <- W diag(s) (may be NULL), H <- diag(s)^-1 H
+ *   diag(s)^-1 on the upper triangle (may be NULL), hdiag <- hdiag / s^2 (may
+ *   be NULL).
+ */
+GPTQ_API gptq_status gptq_channel_stats(const void *X, gptq_dtype x_dtype, int64_t d_in, int64_t n_tok, int64_t ldx,
+                                        float *absmax, double *abssum, hipStream_t stream);
+GPTQ_API gptq_status gptq_smooth_scales(const float *act_absmax, const float *W, int64_t d_out, int64_t d_in,
+                                        float alpha, float *s, void *ws, size_t ws_bytes, hipStream_t stream);
+GPTQ_API gptq_status gptq_awq_search(const float *W, int64_t d_out, int64_t d_in, const float *H,
+                                     const double *act_abssum, int64_t n_tok, const gptq_config *cfg, int32_t n_grid,
+                                     float *s, double *losses, int32_t *best, void *ws, size_t ws_bytes,
+                                     hipStream_t stream);
+GPTQ_API gptq_status gptq_scale_layer(float *W, int64_t d_out, int64_t d_in, float *H, double *hdiag, const float *s,
+                                      hipStream_t stream);
 
 /*
  * Packed codes (after the pass; page "量化经典：LLM.int8 / GPTQ / AWQ", GPTQ

@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libgptq.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16, OP_HESSIAN_TOKENS = 0, 1, 2, 3, 4, 5
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16, OP_HESSIAN_TOKENS, OP_SMOOTH, OP_AWQ = 0, 1, 2, 3, 4, 5, 6, 7
 
 EXPORTED = (
     "gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_rtn_quantize",
     "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
     "gptq_pack_codes", "gptq_w4a16_gemm", "gptq_hessian_accumulate_tokens",
+    "gptq_channel_stats", "gptq_smooth_scales", "gptq_awq_search", "gptq_scale_layer",
 )
 
 
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_layer_loss": [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, vp],
         "gptq_workspace_bytes": [ctypes.c_int, i64, i64, i64, cfgp, ctypes.POINTER(sz)],
         "gptq_pack_codes": [vp, i64, i64, i32, vp, vp, vp],
+        "gptq_channel_stats": [vp, i32, i64, i64, i64, vp, vp, vp],
+        "gptq_smooth_scales": [vp, vp, i64, i64, ctypes.c_float, vp, vp, sz, vp],
+        "gptq_awq_search": [vp, i64, i64, vp, vp, i64, cfgp, i32, vp, vp, vp, vp, sz, vp],
+        "gptq_scale_layer": [vp, i64, i64, vp, vp, vp, vp],
         "gptq_hessian_accumulate_tokens": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
         "gptq_w4a16_gemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i64, vp, i64, vp, sz, vp],
         "gptq_status_string": [ctypes.c_int],
@@ -202,6 +207,63 @@ def layer_loss(W, codes, scales, zeros, H, group_size: int, g_idx=None, out=None
                                           d_out, d_in, int(group_size), _ptr(out), _ptr(ws), ws.numel(),
                                           _stream(stream)))
     return out
+
+
+def channel_stats(X, absmax=None, abssum=None, stream=None):
+    """Per input channel of X ([d][n], bf16 or fp32): (max |x| fp32, sum |x| fp64), accumulated."""
+    import torch
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit stride along tokens")
+    dt = DT_BF16 if X.dtype == torch.bfloat16 else DT_F32
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("X must be bfloat16 or float32")
+    d, n = X.shape
+    if absmax is None:
+        absmax = torch.zeros(d, dtype=torch.float32, device=X.device)
+    if abssum is None:
+        abssum = torch.zeros(d, dtype=torch.float64, device=X.device)
+    _need_cuda(absmax, abssum)
+    _check(load_library().gptq_channel_stats(_ptr(X), dt, d, n, X.stride(0), _ptr(absmax), _ptr(abssum),
+                                             _stream(stream)))
+    return absmax, abssum
+
+
+def smooth_scales(act_absmax, W, alpha: float = 0.5, s=None, ws=None, stream=None):
+    """SmoothQuant scales s_j = max|X_j|^alpha / max|W_j|^(1 - alpha)."""
+    import torch
+    _need_cuda(act_absmax, W, s)
+    d_out, d_in = W.shape
+    if s is None:
+        s = torch.empty(d_in, dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_SMOOTH, d_out, d_in), W.device)
+    _check(load_library().gptq_smooth_scales(_ptr(act_absmax), _ptr(W), d_out, d_in, float(alpha), _ptr(s), _ptr(ws),
+                                             ws.numel(), _stream(stream)))
+    return s
+
+
+def awq_search(W, H, act_abssum, n_tok: int, cfg: Config, n_grid: int = 20, ws=None, stream=None):
+    """AWQ's grid search; returns device tensors (s [d_in], losses [n_grid] fp64, best [1] int32)."""
+    import torch
+    _need_cuda(W, H, act_abssum)
+    d_out, d_in = W.shape
+    s = torch.empty(d_in, dtype=torch.float32, device=W.device)
+    losses = torch.empty(n_grid, dtype=torch.float64, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_AWQ, d_out, d_in, 0, cfg), W.device)
+    _check(load_library().gptq_awq_search(_ptr(W), d_out, d_in, _ptr(H), _ptr(act_abssum), int(n_tok), ctypes.byref(cfg),
+                                          int(n_grid), _ptr(s), _ptr(losses), _ptr(best), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
+    return s, losses, best
+
+
+def scale_layer(s, W=None, H=None, hdiag=None, stream=None) -> None:
+    """In place: W <- W diag(s), H <- diag(s)^-1 H diag(s)^-1 (upper), hdiag <- hdiag / s^2."""
+    _need_cuda(s, W, H, hdiag)
+    d_in = s.shape[0]
+    d_out = W.shape[0] if W is not None else 0
+    _check(load_library().gptq_scale_layer(_ptr(W), d_out, d_in, _ptr(H), _ptr(hdiag), _ptr(s), _stream(stream)))
 
 
 def packed_words(d_in: int, bits: int) -> int:

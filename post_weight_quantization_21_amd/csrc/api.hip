@@ -80,6 +80,16 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
         *out = gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
         if (n_tok > 0) *out = std::max(*out, gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_F32));
         return GPTQ_OK;
+    case GPTQ_OP_SMOOTH:
+        *out = gptq::smooth_ws_bytes(d_out, d_in);
+        return GPTQ_OK;
+    case GPTQ_OP_AWQ: {
+        if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: the AWQ search needs cfg");
+        gptq_status st = check_cfg(cfg, d_in, "gptq_workspace_bytes");
+        if (st != GPTQ_OK) return st;
+        *out = gptq::awq_ws_bytes(d_out, d_in, *cfg);
+        return GPTQ_OK;
+    }
     case GPTQ_OP_W4A16:  // the largest plan over the group sizes (the plan depends on g only through 32, 64, 128 | g)
         *out = std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 32),
                         std::max(gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 64), gptq::w4a16_ws_bytes(n_tok, d_in, d_out, 128)));
@@ -180,6 +190,54 @@ gptq_status gptq_layer_loss(const float *W, const uint8_t *codes, const float *s
     const size_t need = gptq::loss_ws_bytes(d_out, d_in);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_loss(W, codes, scales, zeros, g_idx, H, d_out, d_in, group_size, loss_dev, ws, stream), fn);
+}
+
+gptq_status gptq_channel_stats(const void *X, gptq_dtype x_dtype, int64_t d_in, int64_t n_tok, int64_t ldx, float *absmax,
+                               double *abssum, hipStream_t stream) {
+    const char *fn = "gptq_channel_stats";
+    if (d_in <= 0 || n_tok < 0 || ldx < n_tok) return fail(GPTQ_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    if (x_dtype != GPTQ_DT_F32 && x_dtype != GPTQ_DT_BF16) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+    if ((n_tok > 0 && !X) || !absmax || !abssum) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if ((X && !aligned(X, 4)) || !aligned(absmax, 4) || !aligned(abssum, 8)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return hip_status(gptq::run_channel_stats(X, x_dtype, d_in, n_tok, ldx, absmax, abssum, stream), fn);
+}
+
+gptq_status gptq_smooth_scales(const float *act_absmax, const float *W, int64_t d_out, int64_t d_in, float alpha, float *s,
+                               void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_smooth_scales";
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(GPTQ_ERR_INVALID_ARG, "%s: alpha outside [0, 1]", fn);
+    if (!act_absmax || !W || !s) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(act_absmax, 4) || !aligned(W, 4) || !aligned(s, 4)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    const size_t need = gptq::smooth_ws_bytes(d_out, d_in);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_smooth_scales(act_absmax, W, d_out, d_in, alpha, s, ws, stream), fn);
+}
+
+gptq_status gptq_awq_search(const float *W, int64_t d_out, int64_t d_in, const float *H, const double *act_abssum,
+                            int64_t n_tok, const gptq_config *cfg, int32_t n_grid, float *s, double *losses,
+                            int32_t *best, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const char *fn = "gptq_awq_search";
+    if (d_out <= 0 || d_in <= 0 || n_tok <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    gptq_status st = check_cfg(cfg, d_in, fn);
+    if (st != GPTQ_OK) return st;
+    if (n_grid < 1 || n_grid > 64) return fail(GPTQ_ERR_INVALID_ARG, "%s: n_grid outside 1..64", fn);
+    if (!W || !H || !act_abssum || !s || !losses || !best) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(W, 4) || !aligned(H, 4) || !aligned(act_abssum, 8) || !aligned(s, 4) || !aligned(losses, 8) || !aligned(best, 4))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    const size_t need = gptq::awq_ws_bytes(d_out, d_in, *cfg);
+    if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_awq_search(W, d_out, d_in, H, act_abssum, n_tok, *cfg, n_grid, s, losses, best, ws, stream), fn);
+}
+
+gptq_status gptq_scale_layer(float *W, int64_t d_out, int64_t d_in, float *H, double *hdiag, const float *s,
+                             hipStream_t stream) {
+    const char *fn = "gptq_scale_layer";
+    if (d_in <= 0 || (W && d_out <= 0)) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    if (!s) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if ((W && !aligned(W, 4)) || (H && !aligned(H, 4)) || (hdiag && !aligned(hdiag, 8)) || !aligned(s, 4))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return hip_status(gptq::run_scale_layer(W, d_out, d_in, H, hdiag, s, stream), fn);
 }
 
 gptq_status gptq_pack_codes(const uint8_t *codes, int64_t d_out, int64_t d_in, int32_t bits, const int32_t *perm,

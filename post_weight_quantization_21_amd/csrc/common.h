@@ -103,6 +103,21 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
                      const uint32_t *packed, const float *scales, const float *zeros, int64_t g, int64_t d_out,
                      float *Y, int64_t ldy, void *ws, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Per-channel scaling before the pass (prepass.hip)
+// ---------------------------------------------------------------------------
+hipError_t run_channel_stats(const void *X, gptq_dtype dt, int64_t d_in, int64_t n_tok, int64_t ldx, float *absmax,
+                             double *abssum, hipStream_t s);
+size_t smooth_ws_bytes(int64_t d_out, int64_t d_in);
+hipError_t run_smooth_scales(const float *act_absmax, const float *W, int64_t d_out, int64_t d_in, float alpha,
+                             float *s_out, void *ws, hipStream_t s);
+hipError_t run_scale_layer(float *W, int64_t d_out, int64_t d_in, float *H, double *hdiag, const float *sv,
+                           hipStream_t s);
+size_t awq_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c);
+hipError_t run_awq_search(const float *W, int64_t d_out, int64_t d_in, const float *H, const double *act_abssum,
+                          int64_t n_tok, const gptq_config &c, int n_grid, float *s_out, double *loss_out,
+                          int32_t *best_out, void *ws, hipStream_t s);
+
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
