@@ -534,6 +534,152 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
     }
 }
 
+// More tokens (M > 32), groups of a multiple of 128: a tiled product.  A
+// workgroup computes 128 tokens x 128 features; wave (wm, wn) owns tokens
+// 64 wm .. + 63 and features 64 wn .. + 63 (two 32-row by two 32-column
+// blocks).  K advances in chunks of 64 columns: the activation tile
+// (128 x 64 fp16, rows padded by 16 bytes) is double-buffered in LDS, staged
+// through registers one chunk ahead; each lane reads its two features' packed
+// words of the chunk (16 bytes each: half h takes words 4 h .. 4 h + 3, and
+// MFMA step u uses word 4 h + u, columns 32 h + 8 u .. + 7, the activation
+// operand read to match) one chunk ahead; two chunks form a 128-column body,
+// inside one group, folded with its scale.
+constexpr int kWM = 128, kWN = 128, kWK = 64;  // tile tokens, features, K per chunk
+constexpr int kWP = kWK + 8;                   // LDS row pitch in halves (144 bytes)
+__global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
+                                                              int64_t d_in, const uint32_t *__restrict__ packed,
+                                                              int64_t ldp, const float *__restrict__ scales,
+                                                              const float *__restrict__ zeros, int64_t g, int64_t ng,
+                                                              int64_t d_out, int64_t kspan, float *__restrict__ out,
+                                                              int64_t ldo, int64_t split_stride) {
+    __shared__ __attribute__((aligned(16))) _Float16 xs[2][kWM][kWP];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kWM, n0 = (int64_t)blockIdx.x * kWN;
+    const int64_t kb = (int64_t)blockIdx.z * kspan;
+    const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
+    if (kb >= ke) return;  // uniform over the workgroup
+    const int64_t nchunk = (ke - kb) / kWK;  // even: the range holds whole 128-column bodies
+
+    // the lane's two features and their packed rows (+ word of the chunk)
+    const uint32_t *brow[2];
+    const float *srow[2], *zrow[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t o = n0 + 64 * wn + 32 * nb + l32;
+        const int64_t oc = o < d_out ? o : d_out - 1;
+        brow[nb] = packed + oc * ldp + kb / 8 + 4 * half;
+        srow[nb] = scales + oc * ng;
+        zrow[nb] = zeros + oc * ng;
+    }
+    // staging of the activation tile: thread t moves 16-byte pieces (row t / 8, piece t % 8) of 4 row groups
+    const int sr = tid / 8, sp = tid % 8;
+    // (four named registers rather than an array, which the compiler would keep on the stack)
+    uint4 sv0, sv1, sv2, sv3;
+    auto stage_piece = [&](int i, int64_t k) {
+        const int64_t m = m0 + sr + 32 * i;
+        return *reinterpret_cast<const uint4 *>(X + (m < M ? m : M - 1) * ldx + k + 8 * sp);
+    };
+    auto stage_load = [&](int64_t c) {
+        const int64_t k = kb + kWK * (c < nchunk ? c : nchunk - 1);
+        sv0 = stage_piece(0, k);
+        sv1 = stage_piece(1, k);
+        sv2 = stage_piece(2, k);
+        sv3 = stage_piece(3, k);
+    };
+    auto stage_store = [&](int buf) {
+        *reinterpret_cast<uint4 *>(&xs[buf][sr][8 * sp]) = sv0;
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 32][8 * sp]) = sv1;
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 64][8 * sp]) = sv2;
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 96][8 * sp]) = sv3;
+    };
+    uint4 bw[2][2];
+    auto load_b = [&](int slot, int64_t c) {
+        const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bw[slot][nb] = *reinterpret_cast<const uint4 *>(brow[nb] + 8 * cc);
+    };
+    float2 sz[2], szn[2];  // scale, zero per feature block: this body's, the next body's
+    auto load_sz = [&](float2(&dst)[2], int64_t c) {
+        const int64_t cc = c < nchunk ? c : nchunk - 1;
+        const int64_t gi = (kb + kWK * cc) / g;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) dst[nb] = make_float2(srow[nb][gi], zrow[nb][gi]);
+    };
+
+    floatx16 acc[2][2], accg[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = accg[a][b][r] = 0.0f;
+    uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
+    asm volatile("" : "+v"(magic));
+
+    stage_load(0);
+    load_b(0, 0);
+    load_sz(sz, 0);
+    stage_store(0);
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 2) {
+#pragma unroll
+      for (int buf = 0; buf < 2; ++buf) {  // unrolled: the register slot index is a constant
+        const int64_t c = c0 + buf;
+        // next chunk: activations into registers, weights into the other slot
+        stage_load(c + 1);
+        load_b(buf ^ 1, c + 1);
+        if (buf == 0) load_sz(szn, c + 2);  // the next body's scales, a body ahead
+        Bias bias[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bias[nb] = bias_of(sz[nb].y);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f16x8 a[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                a[mb] = *reinterpret_cast<const f16x8 *>(&xs[buf][64 * wm + 32 * mb + l32][32 * half + 8 * u]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const f16x8 bq = dequant8(word_at(bw[buf][nb], u), bias[nb], magic);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    accg[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], bq, accg[mb][nb], 0, 0, 0);
+            }
+        }
+        if (buf == 1) {  // a 128-column body ends: fold in its scales, then the next body's
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        acc[mb][nb][r] = fmaf(sz[nb].x, accg[mb][nb][r], acc[mb][nb][r]);
+                        accg[mb][nb][r] = 0.0f;
+                    }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) sz[nb] = szn[nb];
+        }
+        stage_store(buf ^ 1);  // the other buffer was last read before the previous barrier
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t o = n0 + 64 * wn + 32 * nb + l32;
+        if (o >= d_out) continue;
+        float *dst = out + (int64_t)blockIdx.z * split_stride + o;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + 64 * wm + 32 * mb + mfma32_row(r, lane);
+                if (m < M) dst[m * ldo] = acc[mb][nb][r];
+            }
+    }
+}
+
 // Y[m][o] = sum over splits of P[split][m][o], splits in order.
 __global__ __launch_bounds__(kThreads) void split_sum_kernel(const float *__restrict__ P, int splits, int64_t M,
                                                              int64_t d_out, float *__restrict__ Y, int64_t ldy) {
@@ -553,6 +699,7 @@ struct GemmPlan {
     int tm, u;
     bool xl;           // few tokens (M <= 32): activations through LDS
     bool chunk;        // few tokens, groups of a multiple of 128: w4a16_chunk_kernel
+    bool wide;         // more tokens, groups of a multiple of 128: w4a16_wide_kernel
     size_t lds_bytes;  // dynamic LDS per workgroup (few-token kernels)
     int64_t n_tiles, m_tiles, splits, kspan;
     size_t xp_bytes, part_bytes;
@@ -570,6 +717,13 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
     p.xl = M <= 32;
     p.chunk = p.xl && p.u == 4;
+    p.wide = !p.xl && p.u == 4;
+    if (p.wide) {  // 128 x 128 tiles; split K (whole 128-column bodies) while there are few tiles
+        p.n_tiles = ceil_div(d_out, kWN);
+        p.m_tiles = ceil_div(M, kWM);
+        const int64_t t = p.n_tiles * p.m_tiles;
+        sp = t >= 512 ? 1 : std::min<int64_t>(ceil_div(512, t), std::max<int64_t>(1, d_in / 512));
+    }
     if (p.chunk) {  // the activations of a whole split in 32 KB of LDS; no more splits than that needs
         const int64_t kmax = std::max<int64_t>(128, (int64_t)(kXlBytes / (2 * M)) - 8);
         sp = ceil_div(d_in, kmax);
@@ -636,7 +790,10 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
     hipLaunchKernelGGL((w4a16_kernel<TM, U>), grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales, \
                        zeros, g, ng, d_out, p.kspan, out, ldo, stride)
 #define W4A16_TM(U)                                                                                              \
-    if (p.chunk && !kperm)                                                                                       \
+    if (p.wide)                                                                                                  \
+        hipLaunchKernelGGL(w4a16_wide_kernel, grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales,     \
+                           zeros, g, ng, d_out, p.kspan, out, ldo, stride);                                    \
+    else if (p.chunk && !kperm)                                                                                       \
         hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
                            ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \
     else if (p.chunk)                                                                                            \
