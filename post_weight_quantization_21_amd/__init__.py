@@ -286,11 +286,13 @@ def pack_codes(codes, bits: int, packed=None, perm=None, stream=None):
 def w4a16_gemm(X, packed, scales, zeros, group_size: int, d_out: int, kperm=None, Y=None, ws=None, stream=None):
     """Y = X' W_hat^T with fp16 X [M][d_in] and 4-bit packed weights; Y fp32 [M][d_out]."""
     import torch
-    _need_cuda(X, packed, scales, zeros, kperm, Y)
+    _need_cuda(packed, scales, zeros, kperm, Y)
+    if not X.is_cuda:
+        raise ValueError("X must be a device tensor")
     if X.dtype != torch.float16:
         raise TypeError("X must be float16")
     M, d_in = X.shape
-    if X.stride(1) != 1:
+    if X.stride(1) != 1:  # rows may sit at any pitch (ldx = X.stride(0)); within a row, contiguous
         raise ValueError("X rows must be contiguous")
     if Y is None:
         Y = torch.empty(M, d_out, dtype=torch.float32, device=X.device)

@@ -263,9 +263,9 @@ gptq_status gptq_w4a16_gemm(const void *X, gptq_dtype x_dtype, int64_t M, int64_
     if (g % 32 != 0) return fail(GPTQ_ERR_UNSUPPORTED, "%s: group_size (or d_in when 0) must be a multiple of 32", fn);
     if (!X || !packed || !scales || !zeros || !Y) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (ldx < d_in || ldy < d_out) return fail(GPTQ_ERR_INVALID_ARG, "%s: ldx < d_in or ldy < d_out", fn);
-    if (!aligned(X) || ldx % 8 != 0 || !aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(Y, 4) ||
+    if (!aligned(X) || ldx % 8 != 0 || !aligned(packed) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(Y, 4) ||
         (kperm && !aligned(kperm, 4)))
-        return fail(GPTQ_ERR_INVALID_ARG, "%s: X must be 16-byte aligned with ldx a multiple of 8; other pointers 4-byte aligned", fn);
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: X and packed must be 16-byte aligned, ldx a multiple of 8; other pointers 4-byte aligned", fn);
     const size_t need = gptq::w4a16_ws_bytes(M, d_in, d_out, g);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_w4a16(X, M, d_in, ldx, kperm, packed, scales, zeros, g, d_out, Y, ldy, ws, stream), fn);

@@ -546,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
 // inside one group, folded with its scale.
 constexpr int kWM = 128, kWN = 128, kWK = 64;  // tile tokens, features, K per chunk
 constexpr int kWP = kWK + 8;                   // LDS row pitch in halves (144 bytes)
+template <bool IL>  // IL: X in its own column order, put in the operand order on the way into LDS
 __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                               int64_t d_in, const uint32_t *__restrict__ packed,
                                                               int64_t ldp, const float *__restrict__ scales,
@@ -556,7 +557,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int half = lane >> 5, l32 = lane & 31;
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kWM, n0 = (int64_t)blockIdx.x * kWN;
+    // token tiles first: the workgroups that share a weight tile run together
+    const int64_t m0 = (int64_t)blockIdx.x * kWM, n0 = (int64_t)blockIdx.y * kWN;
     const int64_t kb = (int64_t)blockIdx.z * kspan;
     const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
     if (kb >= ke) return;  // uniform over the workgroup
@@ -588,11 +590,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
         sv2 = stage_piece(2, k);
         sv3 = stage_piece(3, k);
     };
+    auto order = [](uint4 v) {  // halves 0..7 -> 0, 4, 1, 5, 2, 6, 3, 7 (or as they are)
+        if constexpr (!IL) return v;
+        return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                          __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+    };
     auto stage_store = [&](int buf) {
-        *reinterpret_cast<uint4 *>(&xs[buf][sr][8 * sp]) = sv0;
-        *reinterpret_cast<uint4 *>(&xs[buf][sr + 32][8 * sp]) = sv1;
-        *reinterpret_cast<uint4 *>(&xs[buf][sr + 64][8 * sp]) = sv2;
-        *reinterpret_cast<uint4 *>(&xs[buf][sr + 96][8 * sp]) = sv3;
+        *reinterpret_cast<uint4 *>(&xs[buf][sr][8 * sp]) = order(sv0);
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 32][8 * sp]) = order(sv1);
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 64][8 * sp]) = order(sv2);
+        *reinterpret_cast<uint4 *>(&xs[buf][sr + 96][8 * sp]) = order(sv3);
     };
     uint4 bw[2][2];
     auto load_b = [&](int slot, int64_t c) {
@@ -601,9 +608,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
         for (int nb = 0; nb < 2; ++nb) bw[slot][nb] = *reinterpret_cast<const uint4 *>(brow[nb] + 8 * cc);
     };
     float2 sz[2], szn[2];  // scale, zero per feature block: this body's, the next body's
+    const uint32_t body0 = (uint32_t)(kb / 128), bodies_per_group = (uint32_t)(g / 128);
     auto load_sz = [&](float2(&dst)[2], int64_t c) {
         const int64_t cc = c < nchunk ? c : nchunk - 1;
-        const int64_t gi = (kb + kWK * cc) / g;
+        const uint32_t gi = (body0 + (uint32_t)(cc / 2)) / bodies_per_group;  // 32-bit: a scalar division
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) dst[nb] = make_float2(srow[nb][gi], zrow[nb][gi]);
     };
@@ -614,7 +622,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = accg[a][b][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    const floatx16 zero16 = {};
     uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
     asm volatile("" : "+v"(magic));
 
@@ -644,8 +653,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
             for (int nb = 0; nb < 2; ++nb) {
                 const f16x8 bq = dequant8(word_at(bw[buf][nb], u), bias[nb], magic);
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    accg[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], bq, accg[mb][nb], 0, 0, 0);
+                for (int mb = 0; mb < 2; ++mb)  // a body's first product starts its sums from zero
+                    accg[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        a[mb], bq, (buf == 0 && u == 0) ? zero16 : accg[mb][nb], 0, 0, 0);
             }
         }
         if (buf == 1) {  // a 128-column body ends: fold in its scales, then the next body's
@@ -654,10 +664,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        acc[mb][nb][r] = fmaf(sz[nb].x, accg[mb][nb][r], acc[mb][nb][r]);
-                        accg[mb][nb][r] = 0.0f;
-                    }
+                    for (int r = 0; r < 16; ++r) acc[mb][nb][r] = fmaf(sz[nb].x, accg[mb][nb][r], acc[mb][nb][r]);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) sz[nb] = szn[nb];
         }
@@ -717,7 +724,7 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
     p.xl = M <= 32;
     p.chunk = p.xl && p.u == 4;
-    p.wide = !p.xl && p.u == 4;
+    p.wide = !p.xl && p.u == 4 && ceil_div(d_out, kWN) <= 65535;  // weight tiles along grid y
     if (p.wide) {  // 128 x 128 tiles; split K (whole 128-column bodies) while there are few tiles
         p.n_tiles = ceil_div(d_out, kWN);
         p.m_tiles = ceil_div(M, kWM);
@@ -771,7 +778,7 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
     const _Float16 *Xk = static_cast<const _Float16 *>(X);
     int64_t ldk = ldx;
     hipError_t e;
-    if (kperm || !p.chunk) {  // columns of X into the operand order (and the packed order), once
+    if (kperm || !(p.chunk || p.wide)) {  // columns of X into the operand order (and the packed order), once
         uint16_t *Xp = reinterpret_cast<uint16_t *>(wsb);
         const dim3 grid((unsigned)ceil_div(d_in, kThreads), (unsigned)std::min<int64_t>(M, 65535));
         hipLaunchKernelGGL(gather_cols_kernel, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(X), ldx, M, d_in,
@@ -790,9 +797,12 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
     hipLaunchKernelGGL((w4a16_kernel<TM, U>), grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales, \
                        zeros, g, ng, d_out, p.kspan, out, ldo, stride)
 #define W4A16_TM(U)                                                                                              \
-    if (p.wide)                                                                                                  \
-        hipLaunchKernelGGL(w4a16_wide_kernel, grid, dim3(kThreads), 0, s, Xk, ldk, M, d_in, packed, ldp, scales,     \
-                           zeros, g, ng, d_out, p.kspan, out, ldo, stride);                                    \
+    if (p.wide && !kperm)                                                                                        \
+        hipLaunchKernelGGL(w4a16_wide_kernel<true>, dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+                           d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
+    else if (p.wide)                                                                                             \
+        hipLaunchKernelGGL(w4a16_wide_kernel<false>, dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+                           d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.chunk && !kperm)                                                                                       \
         hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
                            ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \

@@ -90,6 +90,27 @@ def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     _check_product(host(Y), Yref, X, What, perm)
 
 
+@pytest.mark.parametrize("M,group", [(96, 128), (300, 256)])
+def test_w4a16_strided_rows(oracle_mod, M, group):
+    """Token rows with a pitch above d_in (a view into a wider buffer), read in place by the tiled
+    product without a column gather."""
+    torch = torch_mod()
+    d_out, d_in, pitch = 192, 1024, 1096
+    rng = np.random.default_rng(M)
+    codes, scales, zeros = _layer(rng, d_out, d_in, group)
+    Xw = rng.standard_normal((M, pitch)).astype(np.float16)
+    X = Xw[:, :d_in]
+    packed = oracle_mod.pack_codes(codes, 4)
+    Yref = oracle_mod.w4a16_matmul(np.ascontiguousarray(X), packed, scales, zeros, group)
+    Xd = cuda(Xw)[:, :d_in]
+    assert Xd.stride(0) == pitch
+    Y = gq.w4a16_gemm(Xd, cuda(packed.view(np.int32)), cuda(scales), cuda(zeros), group, d_out)
+    torch.cuda.synchronize()
+    gi = np.arange(d_in) // group
+    What = (codes.astype(np.float64) - zeros[:, gi]) * scales[:, gi]
+    _check_product(host(Y), Yref, X, What, None)
+
+
 def test_w4a16_full_size_decode(oracle_mod):
     """28672 x 8192 (the up_proj_70b layer), 16 tokens, groups of 128."""
     torch = torch_mod()
@@ -140,3 +161,7 @@ def test_w4a16_argument_checks():
     assert ei.value.status == gq.ERR_UNSUPPORTED
     with pytest.raises(TypeError):
         gq.w4a16_gemm(X.float(), packed, sc, sc, 32, 8)
+    shifted = torch.zeros(8 * 12 + 1, dtype=torch.int32, device="cuda")[1:].view(8, 12)  # 4-byte aligned only
+    with pytest.raises(gq.GptqError) as ei:
+        gq.w4a16_gemm(X, shifted, sc[:, :3].contiguous(), sc[:, :3].contiguous(), 32, 8)
+    assert ei.value.status == gq.ERR_INVALID_ARG
