@@ -38,14 +38,18 @@ constexpr int kCUs = 256;
 constexpr int kXCDs = 8;
 
 // LDS panels: NS stages x 256 rows x 64 B, unpadded.  Logical chunk c of row r
-// sits at position c ^ swz(r): the 16 rows that one LDS read cycle serves at a
-// common logical chunk then fall into 16 distinct 16-byte bank groups.
+// sits at position c ^ swz(r).  Row r starts in 16-byte bank group 4 (r % 4)
+// of the 64 four-byte banks, so the position has to separate rows that agree
+// mod 4: with swz(r) = (r / 4) % 4 the 32 rows one b128 read touches at a
+// common chunk spread over all 16 groups, and the read takes its minimum of
+// four LDS cycles (measured with a bank-conflict counter; a swizzle on bits 1
+// and 3 of the row took eight).
 struct SyrkSmem {
     uint4 a[NS][TS][CH];
     uint4 b[NS][TS][CH];
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ int64_t tile_linear(int ti, int tj, int nt) {
     return (int64_t)ti * nt - (int64_t)ti * (ti - 1) / 2 + (tj - ti);
