@@ -205,10 +205,10 @@ GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int6
  *           (DYNAMIC) or in original column order (STATIC); [d_out][1] (TENSOR).
  *   g_idx   [d_in] int32 out or NULL: group of each ORIGINAL column.
  *   ws      scratch of gptq_workspace_bytes(GPTQ_OP_QUANTIZE, d_out, d_in, 0, cfg).
- * GPTQ_ERR_UNSUPPORTED when block_size is not 32/64/128, or when group_size
+ * GPTQ_ERR_UNSUPPORTED when block_size is not 32/64/128, when group_size
  * is neither 0, nor a divisor of block_size in {32, 64, 128}, nor a multiple
- * of block_size (group_size 0 counts as d_in).  GPTQ_ERR_INVALID_ARG for an
- * unknown grid, or TENSOR with group_size != 0.
+ * of block_size (group_size 0 counts as d_in), or when d_out > 2^21.
+ * GPTQ_ERR_INVALID_ARG for an unknown grid, or TENSOR with group_size != 0.
  */
 GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
                                 const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros,

@@ -161,7 +161,7 @@ gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const flo
         return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     if (!gptq::quantize_supported(*cfg, d_in))
         return fail(GPTQ_ERR_UNSUPPORTED, "%s: block_size=%d group_size=%d not supported", fn, cfg->block_size, cfg->group_size);
-    if (d_out > ((int64_t)1 << 31) / 2) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_out too large", fn);
+    if (d_out > ((int64_t)1 << 21)) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_out above 2^21", fn);  // 64-row tiles on grid y
     const size_t need = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_quantize(W, d_out, d_in, U, perm, *cfg, codes, scales, zeros, g_idx, ws, stream), fn);

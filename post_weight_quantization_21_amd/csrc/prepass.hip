@@ -133,10 +133,11 @@ __global__ __launch_bounds__(kThreads) void scale_w_kernel(const float *__restri
 // Hd[i][j] = H[i][j] / (s_i s_j) on the upper triangle (Hd may be H); hdiag[j] /= s_j^2.
 __global__ __launch_bounds__(kThreads) void scale_h_kernel(const float *__restrict__ H, int64_t d,
                                                            const float *__restrict__ s, float *__restrict__ Hd) {
-    const int64_t i = blockIdx.y;
-    const float si = 1.0f / s[i];
-    for (int64_t j = i + (int64_t)blockIdx.x * kThreads + threadIdx.x; j < d; j += (int64_t)gridDim.x * kThreads)
-        Hd[i * d + j] = (H[i * d + j] * si) / s[j];
+    for (int64_t i = blockIdx.y; i < d; i += gridDim.y) {  // rows, grid-stride (grid y is capped)
+        const float si = 1.0f / s[i];
+        for (int64_t j = i + (int64_t)blockIdx.x * kThreads + threadIdx.x; j < d; j += (int64_t)gridDim.x * kThreads)
+            Hd[i * d + j] = (H[i * d + j] * si) / s[j];
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void scale_hdiag_kernel(double *__restrict__ hdiag, int64_t d,
@@ -239,7 +240,7 @@ hipError_t run_scale_layer(float *W, int64_t d_out, int64_t d_in, float *H, doub
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (H) {
-        hipLaunchKernelGGL(scale_h_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64), (unsigned)d_in),
+        hipLaunchKernelGGL(scale_h_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64), (unsigned)std::min<int64_t>(d_in, 65535)),
                            dim3(kThreads), 0, s, H, d_in, sv, H);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -274,7 +275,7 @@ hipError_t run_awq_search(const float *W, int64_t d_out, int64_t d_in, const flo
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(scale_w_kernel, dim3(grid_of(d_out * d_in)), dim3(kThreads), 0, s, W, d_out, d_in, sv, Wq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(scale_h_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64), (unsigned)d_in),
+        hipLaunchKernelGGL(scale_h_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64), (unsigned)std::min<int64_t>(d_in, 65535)),
                            dim3(kThreads), 0, s, H, d_in, sv, Hq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = run_rtn(Wq, d_out, d_in, rc, codes, sc, ze, s)) != hipSuccess) return e;

@@ -98,6 +98,8 @@ def test_argument_errors_are_synchronous():
     bad_grid.grid = 7
     assert _call_quantize(bad_grid) == gq.ERR_INVALID_ARG
     assert _call_quantize(gq.config(super_cols=-128)) == gq.ERR_INVALID_ARG
+    assert _call_quantize(gq.config(), d_out=(1 << 21) + 1) == gq.ERR_UNSUPPORTED  # beyond the row-tile grid
+    assert b"d_out" in lib.gptq_last_error()
     cfg = gq.config()
     p = ctypes.c_void_p(0x10000)
     assert lib.gptq_prepare_hinv(p, None, 0, ctypes.byref(cfg), p, p, p, p, 1 << 30, None) == gq.ERR_INVALID_ARG

@@ -130,6 +130,27 @@ def test_w4a16_full_size_decode(oracle_mod):
     _check_product(host(Y)[:, rows], Yref, X, What, None)
 
 
+def test_w4a16_full_size_prefill(oracle_mod):
+    """28672 x 8192, 2048 tokens (the tiled product the prefill bench times), groups of 128: sampled
+    output columns against the oracle."""
+    torch = torch_mod()
+    M, d_out, d_in, group = 2048, 28672, 8192, 128
+    rng = np.random.default_rng(6)
+    codes, scales, zeros = _layer(rng, d_out, d_in, group)
+    X = rng.standard_normal((M, d_in)).astype(np.float16)
+    packed = gq.pack_codes(cuda(codes), 4)
+    Y = gq.w4a16_gemm(cuda(X), packed, cuda(scales), cuda(zeros), group, d_out)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(d_out, 96, replace=False))
+    rows[:2] = (0, 127)  # the first weight tile's edges
+    rows = np.unique(np.concatenate([rows, [d_out - 1]]))
+    pk = oracle_mod.pack_codes(codes[rows], 4)
+    Yref = oracle_mod.w4a16_matmul(X, pk, scales[rows], zeros[rows], group)
+    gi = np.arange(d_in) // group
+    What = (codes[rows].astype(np.float64) - zeros[rows][:, gi]) * scales[rows][:, gi]
+    _check_product(host(Y)[:, rows], Yref, X, What, None)
+
+
 def test_w4a16_consumes_the_pass_output(oracle_mod):
     """GPTQ on the GPU (dynamic groups under act-order), codes packed in processing order, the product
     with the matching column gather: X W_hat^T with W_hat dequantized through g_idx."""
