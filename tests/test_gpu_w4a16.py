@@ -70,6 +70,8 @@ def _layer(rng, d_out, d_in, group):
     (2, 130, 384, 128, True),       # half a 256-column chunk at the end; column gather
     (5, 64, 640, 128, False),       # odd number of 128-column bodies
     (32, 200, 1024, 256, False),    # groups spanning two bodies
+    (33, 20, 256, 128, False),      # smallest tiled case; one wave's features all past d_out
+    (64, 64, 8192, 128, False),     # one tile, sixteen K splits summed in order
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
