@@ -150,6 +150,52 @@ def bench_w4a16(args) -> int:
     return 0
 
 
+def bench_tokens(args) -> int:
+    """H from token-major activations ([n_tok][d_in] bf16, one row per token, as a layer's inputs
+    arrive) on the workload's shape: per 65536-token block a transpose into a channel-major panel,
+    then the matrix-core SYRK.  Timed per call with X resident; H accumulates across calls."""
+    import torch
+
+    import datagen
+    import post_weight_quantization_21_amd as gq
+
+    gq.load_library()
+    dev = torch.device("cuda:0")
+    lay = datagen.make_layer(args.workload)
+    d_in, n = lay["d_in"], lay["n_tok"]
+    if lay["X"].dtype != np.uint16:
+        print(f"bench.py --tokens: the {args.workload} workload has fp32 activations; use a bf16 workload", file=sys.stderr)
+        return 2
+    Xt = torch.from_numpy(lay["X"].view(np.int16)).to(dev).view(torch.bfloat16).t().contiguous()  # [n][d]
+    del lay
+    H = torch.zeros(d_in, d_in, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(gq.workspace_bytes(gq.OP_HESSIAN_TOKENS, 0, d_in, n), 1), dtype=torch.uint8, device=dev)
+    run = lambda: gq.hessian_accumulate_tokens(H, Xt, ws=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = float(d_in) * (d_in + 1) * n  # the SYRK's multiply-adds (upper triangle incl. diagonal), x2
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"metric": "hessian_tokens_ms", "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "bf16->f32",
+           "data": "synthetic", "config": {"workload": args.workload + "_token_major", "d_in": d_in, "n_tok": n,
+                                           "x_layout": "token-major [n_tok][d_in]", "block_tokens": 65536},
+           "transpose_bytes": 4 * d_in * n,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "note": "SYRK flops over the whole call (transposes included): a lower bound"},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def bench_awq(args) -> int:
     """AWQ's scale search on the workload's layer: per-channel |x| statistics (outside the timed
     region, like H), then 20 alphas of scale, RTN and loss through the scaled H."""
@@ -209,6 +255,8 @@ def main() -> int:
                     help="instead: time the W4A16 product of M tokens with the packed 28672x8192 layer")
     ap.add_argument("--awq", action="store_true",
                     help="instead: time the AWQ scale search (20 alphas) on the workload's layer")
+    ap.add_argument("--tokens", action="store_true",
+                    help="instead: time H from the workload's activations laid out token-major")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this benchmark runs GPTQ on one GPU only "
@@ -219,6 +267,8 @@ def main() -> int:
         return bench_w4a16(args)
     if args.awq:
         return bench_awq(args)
+    if args.tokens:
+        return bench_tokens(args)
 
     import torch
 
