@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
     }
 }
 
-// More tokens (M > 32), groups of a multiple of 128: a tiled product.  A
+// More tokens (M > 32), groups of a multiple of 64: a tiled product.  A
 // workgroup computes 128 tokens x 128 features; wave (wm, wn) owns tokens
 // 64 wm .. + 63 and features 64 wn .. + 63 (two 32-row by two 32-column
 // blocks).  K advances in chunks of 64 columns: the activation tile
@@ -542,11 +542,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
 // through registers one chunk ahead; each lane reads its two features' packed
 // words of the chunk (16 bytes each: half h takes words 4 h .. 4 h + 3, and
 // MFMA step u uses word 4 h + u, columns 32 h + 8 u .. + 7, the activation
-// operand read to match) one chunk ahead; two chunks form a 128-column body,
-// inside one group, folded with its scale.
+// operand read to match) one chunk ahead.  A body (two chunks for groups of a
+// multiple of 128, one for a multiple of 64) lies inside one group: its sums
+// start from zero and are folded into the running ones with its scale.
 constexpr int kWM = 128, kWN = 128, kWK = 64;  // tile tokens, features, K per chunk
 constexpr int kWP = kWK + 8;                   // LDS row pitch in halves (144 bytes)
-template <bool IL>  // IL: X in its own column order, put in the operand order on the way into LDS
+// CPB: chunks per body, 2 for groups of a multiple of 128 columns, 1 for a
+// multiple of 64 (the body, the columns one scale covers, is then one chunk).
+template <bool IL, int CPB>  // IL: X in its own column order, put in the operand order on the way into LDS
 __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                               int64_t d_in, const uint32_t *__restrict__ packed,
                                                               int64_t ldp, const float *__restrict__ scales,
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
     const int64_t kb = (int64_t)blockIdx.z * kspan;
     const int64_t ke = std::min<int64_t>(d_in, kb + kspan);
     if (kb >= ke) return;  // uniform over the workgroup
-    const int64_t nchunk = (ke - kb) / kWK;  // even: the range holds whole 128-column bodies
+    const int64_t nchunk = (ke - kb) / kWK;  // the range holds whole bodies (an even count when CPB = 2)
 
     // the lane's two features and their packed rows (+ word of the chunk)
     const uint32_t *brow[2];
@@ -608,10 +611,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
         for (int nb = 0; nb < 2; ++nb) bw[slot][nb] = *reinterpret_cast<const uint4 *>(brow[nb] + 8 * cc);
     };
     float2 sz[2], szn[2];  // scale, zero per feature block: this body's, the next body's
-    const uint32_t body0 = (uint32_t)(kb / 128), bodies_per_group = (uint32_t)(g / 128);
+    constexpr int kBody = kWK * CPB;  // columns per body
+    const uint32_t body0 = (uint32_t)(kb / kBody), bodies_per_group = (uint32_t)(g / kBody);
     auto load_sz = [&](float2(&dst)[2], int64_t c) {
         const int64_t cc = c < nchunk ? c : nchunk - 1;
-        const uint32_t gi = (body0 + (uint32_t)(cc / 2)) / bodies_per_group;  // 32-bit: a scalar division
+        const uint32_t gi = (body0 + (uint32_t)(cc / CPB)) / bodies_per_group;  // 32-bit: a scalar division
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) dst[nb] = make_float2(srow[nb][gi], zrow[nb][gi]);
     };
@@ -636,10 +640,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
 #pragma unroll
       for (int buf = 0; buf < 2; ++buf) {  // unrolled: the register slot index is a constant
         const int64_t c = c0 + buf;
+        if constexpr (CPB == 1)
+            if (buf == 1 && c >= nchunk) break;  // an odd chunk count; uniform
+        const bool body_start = buf % CPB == 0, body_end = buf % CPB == CPB - 1;
         // next chunk: activations into registers, weights into the other slot
         stage_load(c + 1);
         load_b(buf ^ 1, c + 1);
-        if (buf == 0) load_sz(szn, c + 2);  // the next body's scales, a body ahead
+        if (body_start) load_sz(szn, c + CPB);  // the next body's scales, a body ahead
         Bias bias[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) bias[nb] = bias_of(sz[nb].y);
@@ -655,10 +662,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)  // a body's first product starts its sums from zero
                     accg[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        a[mb], bq, (buf == 0 && u == 0) ? zero16 : accg[mb][nb], 0, 0, 0);
+                        a[mb], bq, (body_start && u == 0) ? zero16 : accg[mb][nb], 0, 0, 0);
             }
         }
-        if (buf == 1) {  // a 128-column body ends: fold in its scales, then the next body's
+        if (body_end) {  // a body ends: fold in its scales, then the next body's
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -724,7 +731,7 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
     p.xl = M <= 32;
     p.chunk = p.xl && p.u == 4;
-    p.wide = !p.xl && p.u == 4 && ceil_div(d_out, kWN) <= 65535;  // weight tiles along grid y
+    p.wide = !p.xl && p.u >= 2 && ceil_div(d_out, kWN) <= 65535;  // weight tiles along grid y
     if (p.wide) {  // 128 x 128 tiles; split K (whole 128-column bodies) while there are few tiles
         p.n_tiles = ceil_div(d_out, kWN);
         p.m_tiles = ceil_div(M, kWM);
@@ -798,10 +805,10 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
                        zeros, g, ng, d_out, p.kspan, out, ldo, stride)
 #define W4A16_TM(U)                                                                                              \
     if (p.wide && !kperm)                                                                                        \
-        hipLaunchKernelGGL(w4a16_wide_kernel<true>, dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+        hipLaunchKernelGGL((w4a16_wide_kernel<true, ((U) >= 4 ? 2 : 1)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
                            d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.wide)                                                                                             \
-        hipLaunchKernelGGL(w4a16_wide_kernel<false>, dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+        hipLaunchKernelGGL((w4a16_wide_kernel<false, ((U) >= 4 ? 2 : 1)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
                            d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.chunk && !kperm)                                                                                       \
         hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \

@@ -72,6 +72,10 @@ def _layer(rng, d_out, d_in, group):
     (32, 200, 1024, 256, False),    # groups spanning two bodies
     (33, 20, 256, 128, False),      # smallest tiled case; one wave's features all past d_out
     (64, 64, 8192, 128, False),     # one tile, sixteen K splits summed in order
+    (100, 96, 640, 64, False),      # tiled, 64-column groups: one chunk per body
+    (48, 130, 448, 64, True),       # ... an odd chunk count, column gather, ragged features
+    (64, 64, 4544, 64, False),      # ... K splits of nine chunks (the last of eight)
+    (40, 64, 768, 192, False),      # ... groups of three bodies
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
