@@ -547,8 +547,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
 // start from zero and are folded into the running ones with its scale.
 constexpr int kWM = 128, kWN = 128, kWK = 64;  // tile tokens, features, K per chunk
 constexpr int kWP = kWK + 8;                   // LDS row pitch in halves (144 bytes)
-// CPB: chunks per body, 2 for groups of a multiple of 128 columns, 1 for a
-// multiple of 64 (the body, the columns one scale covers, is then one chunk).
+// CPB: chunks per body (the columns one scale covers), 2 for groups of a
+// multiple of 128 columns, 1 for a multiple of 64, 0 for 32-column bodies (two
+// per chunk).  With CPB = 0 the MFMA steps change: step s takes columns
+// 16 s + 8 h .. + 7 in lane half h, so its 16 K values lie in one 32-column
+// group; two v_permlane32_swap per 16-byte load move the words there (half 0
+// loaded words 0..3, half 1 words 4..7; step s needs word 2 s + h).
 template <bool IL, int CPB>  // IL: X in its own column order, put in the operand order on the way into LDS
 __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                               int64_t d_in, const uint32_t *__restrict__ packed,
@@ -611,13 +615,26 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
         for (int nb = 0; nb < 2; ++nb) bw[slot][nb] = *reinterpret_cast<const uint4 *>(brow[nb] + 8 * cc);
     };
     float2 sz[2], szn[2];  // scale, zero per feature block: this body's, the next body's
-    constexpr int kBody = kWK * CPB;  // columns per body
+    float2 szh[2][2], szhn[2][2];  // CPB = 0: [body of the chunk][feature block], this chunk's and the next
+    constexpr int kBody = CPB == 0 ? kWK / 2 : kWK * CPB;  // columns per body
     const uint32_t body0 = (uint32_t)(kb / kBody), bodies_per_group = (uint32_t)(g / kBody);
-    auto load_sz = [&](float2(&dst)[2], int64_t c) {
+    auto group_of = [&](int64_t c, int j) {  // group of body j of chunk c (j = 0 unless CPB = 0)
         const int64_t cc = c < nchunk ? c : nchunk - 1;
-        const uint32_t gi = (body0 + (uint32_t)(cc / CPB)) / bodies_per_group;  // 32-bit: a scalar division
+        const uint32_t b = CPB == 0 ? (uint32_t)(2 * cc + j) : (uint32_t)(cc / (CPB == 0 ? 1 : CPB));
+        return (body0 + b) / bodies_per_group;  // 32-bit: a scalar division
+    };
+    auto load_sz = [&](float2(&dst)[2], int64_t c) {
+        const uint32_t gi = group_of(c, 0);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) dst[nb] = make_float2(srow[nb][gi], zrow[nb][gi]);
+    };
+    auto load_szh = [&](float2(&dst)[2][2], int64_t c) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t gi = group_of(c, j);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) dst[j][nb] = make_float2(srow[nb][gi], zrow[nb][gi]);
+        }
     };
 
     floatx16 acc[2][2], accg[2][2];
@@ -633,20 +650,72 @@ __global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__
 
     stage_load(0);
     load_b(0, 0);
-    load_sz(sz, 0);
+    if constexpr (CPB == 0)
+        load_szh(szh, 0);
+    else
+        load_sz(sz, 0);
     stage_store(0);
     __syncthreads();
     for (int64_t c0 = 0; c0 < nchunk; c0 += 2) {
 #pragma unroll
       for (int buf = 0; buf < 2; ++buf) {  // unrolled: the register slot index is a constant
         const int64_t c = c0 + buf;
-        if constexpr (CPB == 1)
+        if constexpr (CPB <= 1)
             if (buf == 1 && c >= nchunk) break;  // an odd chunk count; uniform
-        const bool body_start = buf % CPB == 0, body_end = buf % CPB == CPB - 1;
         // next chunk: activations into registers, weights into the other slot
         stage_load(c + 1);
         load_b(buf ^ 1, c + 1);
-        if (body_start) load_sz(szn, c + CPB);  // the next body's scales, a body ahead
+        if constexpr (CPB == 0) {
+            load_szh(szhn, c + 1);  // the next chunk's two bodies
+            Bias bias[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) bias[j][nb] = bias_of(szh[j][nb].y);
+            uint4 wq[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {  // lane half h: words h, 2 + h, 4 + h, 6 + h for steps 0, 1, 2, 3
+                wq[nb] = bw[buf][nb];
+                const auto r01 = __builtin_amdgcn_permlane32_swap(wq[nb].x, wq[nb].y, false, false);
+                const auto r23 = __builtin_amdgcn_permlane32_swap(wq[nb].z, wq[nb].w, false, false);
+                wq[nb] = make_uint4(r01[0], r23[0], r01[1], r23[1]);
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int j = st >> 1;  // the body (32-column group) of this step
+                f16x8 a[2];
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    a[mb] = *reinterpret_cast<const f16x8 *>(&xs[buf][64 * wm + 32 * mb + l32][16 * st + 8 * half]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const f16x8 bq = dequant8(word_at(wq[nb], st), bias[j][nb], magic);
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)  // a body's first product starts its sums from zero
+                        accg[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            a[mb], bq, (st % 2 == 0) ? zero16 : accg[mb][nb], 0, 0, 0);
+                }
+                if (st % 2 == 1) {  // body j ends: fold it in with its scales
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                acc[mb][nb][r] = fmaf(szh[j][nb].x, accg[mb][nb][r], acc[mb][nb][r]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) szh[j][nb] = szhn[j][nb];
+            stage_store(buf ^ 1);  // the other buffer was last read before the previous barrier
+            __syncthreads();
+            continue;
+        }
+        constexpr int kCpb = CPB == 0 ? 1 : CPB;
+        const bool body_start = buf % kCpb == 0, body_end = buf % kCpb == kCpb - 1;
+        if (body_start) load_sz(szn, c + kCpb);  // the next body's scales, a body ahead
         Bias bias[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) bias[nb] = bias_of(sz[nb].y);
@@ -731,8 +800,9 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
     p.xl = M <= 32;
     p.chunk = p.xl && p.u == 4;
-    p.wide = !p.xl && p.u >= 2 && ceil_div(d_out, kWN) <= 65535;  // weight tiles along grid y
-    if (p.wide) {  // 128 x 128 tiles; split K (whole 128-column bodies) while there are few tiles
+    // weight tiles along grid y; whole 64-column chunks
+    p.wide = !p.xl && d_in % kWK == 0 && ceil_div(d_out, kWN) <= 65535;
+    if (p.wide) {  // 128 x 128 tiles; split K (whole bodies and chunks) while there are few tiles
         p.n_tiles = ceil_div(d_out, kWN);
         p.m_tiles = ceil_div(M, kWM);
         const int64_t t = p.n_tiles * p.m_tiles;
@@ -745,7 +815,8 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
         const int64_t kmax = std::max<int64_t>(32 * p.u, std::min<int64_t>((int64_t)(kXlBytes / (2 * M)) - 8, 30 * g));
         sp = std::max<int64_t>(sp, ceil_div(d_in, kmax));
     }
-    p.kspan = ceil_div(ceil_div(d_in, sp), 32 * p.u) * 32 * p.u;  // whole bodies
+    const int64_t unit = p.wide ? std::max<int64_t>(32 * p.u, kWK) : 32 * p.u;  // whole bodies (and chunks)
+    p.kspan = ceil_div(ceil_div(d_in, sp), unit) * unit;
     if (p.chunk)
         while ((size_t)M * (size_t)(p.kspan + 8) * 2 > kXlBytes && p.kspan > 128) p.kspan -= 128;
     else if (p.xl)
@@ -805,10 +876,10 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
                        zeros, g, ng, d_out, p.kspan, out, ldo, stride)
 #define W4A16_TM(U)                                                                                              \
     if (p.wide && !kperm)                                                                                        \
-        hipLaunchKernelGGL((w4a16_wide_kernel<true, ((U) >= 4 ? 2 : 1)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+        hipLaunchKernelGGL((w4a16_wide_kernel<true, ((U) >= 4 ? 2 : (U) == 2 ? 1 : 0)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
                            d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.wide)                                                                                             \
-        hipLaunchKernelGGL((w4a16_wide_kernel<false, ((U) >= 4 ? 2 : 1)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
+        hipLaunchKernelGGL((w4a16_wide_kernel<false, ((U) >= 4 ? 2 : (U) == 2 ? 1 : 0)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
                            d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.chunk && !kperm)                                                                                       \
         hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \

@@ -76,6 +76,10 @@ def _layer(rng, d_out, d_in, group):
     (48, 130, 448, 64, True),       # ... an odd chunk count, column gather, ragged features
     (64, 64, 4544, 64, False),      # ... K splits of nine chunks (the last of eight)
     (40, 64, 768, 192, False),      # ... groups of three bodies
+    (48, 100, 512, 32, False),      # tiled, 32-column groups: two bodies per chunk, words swapped across lane halves
+    (96, 130, 448, 32, True),       # ... an odd chunk count, column gather
+    (64, 64, 4544, 32, False),      # ... K splits of nine chunks
+    (40, 64, 768, 96, False),       # ... groups of three 32-column bodies
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
