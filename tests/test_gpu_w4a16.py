@@ -80,6 +80,8 @@ def _layer(rng, d_out, d_in, group):
     (96, 130, 448, 32, True),       # ... an odd chunk count, column gather
     (64, 64, 4544, 32, False),      # ... K splits of nine chunks
     (40, 64, 768, 96, False),       # ... groups of three 32-column bodies
+    (40, 70, 352, 32, False),       # d_in not a multiple of 64: the generic kernel, two token blocks
+    (200, 64, 96, 32, True),        # ... four token blocks, column gather
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
