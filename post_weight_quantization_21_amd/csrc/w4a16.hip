@@ -477,9 +477,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
 
     const int64_t mc = (lane & 31) < M ? (lane & 31) : M - 1;
     const _Float16 *arow = xs + mc * ldxs + 64 * half;  // + 128 body + 8 i
-    floatx16 acc, accg;
+    floatx16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = accg[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const floatx16 zero16 = {};
     uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves, kept in a register
     asm volatile("" : "+v"(magic));
 
@@ -494,25 +495,34 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
         x = make_uint4(xv[0], xv[1], xv[2], xv[3]);
         y = make_uint4(yv[0], yv[1], yv[2], yv[3]);
     };
-    auto body = [&](const uint4 &w0, const uint4 &w1, int64_t b, float2 v) {  // 128 columns, words w0 (i < 4), w1
-        const int64_t bc = b < nbody ? b : nbody - 1;
-        const float s = b < nbody ? v.x : 0.0f;
-        const Bias bias = bias_of(v.y);
-        const _Float16 *ap = arow + 128 * bc;
-        f16x8 a[8];
+    // The chunk's two bodies, their MFMAs interleaved: two independent sums, so
+    // each MFMA issues without waiting for the previous one's result.  Each
+    // body's sum and the folds keep their order (body b, then b + 1).
+    auto bodies = [&](const uint4 (&w)[4], int64_t b, const float2 (&v)[2]) {
+        float s[2];
+        Bias bias[2];
+        const _Float16 *ap[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f16x8 *>(ap + 8 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 &wv = i < 4 ? w0 : w1;
-            const f16x8 bq = dequant8(word_at(wv, i & 3), bias, magic);
-            accg = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bq, accg, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+            const int64_t bc = b + h < nbody ? b + h : nbody - 1;
+            s[h] = b + h < nbody ? v[h].x : 0.0f;
+            bias[h] = bias_of(v[h].y);
+            ap[h] = arow + 128 * bc;
         }
+        floatx16 g[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            acc[r] = fmaf(s, accg[r], acc[r]);
-            accg[r] = 0.0f;
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f16x8 a = *reinterpret_cast<const f16x8 *>(ap[h] + 8 * i);
+                const uint4 &wv = w[2 * h + (i < 4 ? 0 : 1)];
+                const f16x8 bq = dequant8(word_at(wv, i & 3), bias[h], magic);
+                g[h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq, i == 0 ? zero16 : g[h], 0, 0, 0);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(s[h], g[h][r], acc[r]);
     };
     for (int64_t c = 0; c < nchunks; c += 2) {
 #pragma unroll
@@ -521,8 +531,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
             uint4(&w)[4] = q[sl];
             swap(w[0], w[2]);
             swap(w[1], w[3]);
-            body(w[0], w[1], 2 * (c + sl), sz[sl][0]);
-            body(w[2], w[3], 2 * (c + sl) + 1, sz[sl][1]);
+            bodies(w, 2 * (c + sl), sz[sl]);
         }
     }
     if (o >= d_out) return;
