@@ -563,7 +563,7 @@ constexpr int kWP = kWK + 8;                   // LDS row pitch in halves (144 b
 // group; two v_permlane32_swap per 16-byte load move the words there (half 0
 // loaded words 0..3, half 1 words 4..7; step s needs word 2 s + h).
 template <bool IL, int CPB>  // IL: X in its own column order, put in the operand order on the way into LDS
-__global__ __launch_bounds__(kThreads) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
+__global__ __launch_bounds__(kThreads, 2) void w4a16_wide_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                               int64_t d_in, const uint32_t *__restrict__ packed,
                                                               int64_t ldp, const float *__restrict__ scales,
                                                               const float *__restrict__ zeros, int64_t g, int64_t ng,
