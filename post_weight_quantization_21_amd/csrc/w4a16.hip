@@ -410,7 +410,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_few_kernel(const _Float16 *__r
 // two bodies' scales and zeros are read while the current chunk is used; the
 // activation operand comes from LDS, staged once (IL: straight from X, put in
 // the operand order on the way).  Bodies past the end fold with scale 0.
-template <bool IL>
+// GB: columns per group fold, 128 for groups of a multiple of 128; 64 or 32
+// for smaller groups.  Then MFMA step i of a body takes columns 16 i + 8 h ..
+// + 7 in lane half h (word 2 i + h), so a step lies inside one group: four more
+// swaps per body (word pairs (j, j + 1), j even) put the even words in half 0
+// and the odd words in half 1, and the body's sum is folded at every group end.
+template <bool IL, int GB>
 __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                                int64_t d_in, const uint32_t *__restrict__ packed,
                                                                int64_t ldp, const float *__restrict__ scales,
@@ -430,8 +435,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
     const uint32_t *brow = packed + oc * ldp + kb / 8;
     const int64_t wlast = (ke - kb) / 8 - 16;  // last 16-word piece that stays inside the range
     const float *srow = scales + oc * ng, *zrow = zeros + oc * ng;
+    constexpr int NG = 128 / GB;  // groups per body
     uint4 q[2][4];
-    float2 sz[2][2];  // [slot][body of the chunk]: scale (0 past the end), zero
+    float2 sz[2][2][NG];  // [slot][body of the chunk][group of the body]: scale (0 past the end), zero
     auto load = [&](int slot, int64_t c) {
         const int64_t cc = c < nchunks ? c : nchunks - 1;
         const int64_t w = std::min<int64_t>(32 * cc + 16 * half, wlast);
@@ -441,8 +447,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t b = 2 * c + h, bc = b < nbody ? b : nbody - 1;
-            const int64_t gi = (kb + 128 * bc) / g;
-            sz[slot][h] = make_float2(srow[gi], zrow[gi]);
+#pragma unroll
+            for (int k = 0; k < NG; ++k) {
+                const int64_t gi = (kb + 128 * bc + GB * k) / g;
+                sz[slot][h][k] = make_float2(srow[gi], zrow[gi]);
+            }
         }
     };
     load(0, 0);  // the first chunk is in flight during the staging
@@ -476,7 +485,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
     __syncthreads();
 
     const int64_t mc = (lane & 31) < M ? (lane & 31) : M - 1;
-    const _Float16 *arow = xs + mc * ldxs + 64 * half;  // + 128 body + 8 i
+    // + 128 body + 8 i (GB = 128: columns 64 h + 8 i), else + 128 body + 16 i (columns 16 i + 8 h)
+    const _Float16 *arow = xs + mc * ldxs + (GB == 128 ? 64 : 8) * half;
     floatx16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -498,31 +508,39 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
     // The chunk's two bodies, their MFMAs interleaved: two independent sums, so
     // each MFMA issues without waiting for the previous one's result.  Each
     // body's sum and the folds keep their order (body b, then b + 1).
-    auto bodies = [&](const uint4 (&w)[4], int64_t b, const float2 (&v)[2]) {
-        float s[2];
-        Bias bias[2];
+    auto bodies = [&](const uint4 (&w)[4], int64_t b, const float2 (&v)[2][NG]) {
+        constexpr int kSteps = 8 / NG;  // MFMA steps per group
         const _Float16 *ap[2];
+        bool live[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int64_t bc = b + h < nbody ? b + h : nbody - 1;
-            s[h] = b + h < nbody ? v[h].x : 0.0f;
-            bias[h] = bias_of(v[h].y);
-            ap[h] = arow + 128 * bc;
+            live[h] = b + h < nbody;
+            ap[h] = arow + 128 * (live[h] ? b + h : nbody - 1);
         }
         floatx16 g[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int k = 0; k < NG; ++k) {
+            Bias bias[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f16x8 a = *reinterpret_cast<const f16x8 *>(ap[h] + 8 * i);
-                const uint4 &wv = w[2 * h + (i < 4 ? 0 : 1)];
-                const f16x8 bq = dequant8(word_at(wv, i & 3), bias[h], magic);
-                g[h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq, i == 0 ? zero16 : g[h], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) bias[h] = bias_of(v[h][k].y);
+#pragma unroll
+            for (int i = k * kSteps; i < (k + 1) * kSteps; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(ap[h] + (GB == 128 ? 8 : 16) * i);
+                    // GB = 128: word 8 h + i; else word 2 i + h, in register (i < 4 ? 2 i : 2 (i - 4) + 1)
+                    const int rj = GB == 128 ? i : (i < 4 ? 2 * i : 2 * (i - 4) + 1);
+                    const uint4 &wv = w[2 * h + (rj < 4 ? 0 : 1)];
+                    const f16x8 bq = dequant8(word_at(wv, rj & 3), bias[h], magic);
+                    g[h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq, i == k * kSteps ? zero16 : g[h], 0, 0, 0);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // group k of both bodies ends: fold with its scale
+                const float sc = live[h] ? v[h][k].x : 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = fmaf(sc, g[h][r], acc[r]);
             }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = fmaf(s[h], g[h][r], acc[r]);
+        }
     };
     for (int64_t c = 0; c < nchunks; c += 2) {
 #pragma unroll
@@ -531,6 +549,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *_
             uint4(&w)[4] = q[sl];
             swap(w[0], w[2]);
             swap(w[1], w[3]);
+            if constexpr (GB < 128) {  // word pairs (j, j + 1), j even: even words to half 0, odd to half 1
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint4 &x = w[t];
+                    const auto r01 = __builtin_amdgcn_permlane32_swap(x.x, x.y, false, false);
+                    const auto r23 = __builtin_amdgcn_permlane32_swap(x.z, x.w, false, false);
+                    x = make_uint4(r01[0], r01[1], r23[0], r23[1]);
+                }
+            }
             bodies(w, 2 * (c + sl), sz[sl]);
         }
     }
@@ -808,7 +835,9 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
     int64_t sp = tiles >= 1024 ? 1 : ceil_div(1024, tiles);
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, d_in / 256));
     p.xl = M <= 32;
-    p.chunk = p.xl && p.u == 4;
+    // whole 128-column bodies (folded per group inside them); with groups under 128
+    // columns only up to 4 tokens, where the streamed words win over scales in LDS
+    p.chunk = p.xl && d_in % 128 == 0 && (p.u == 4 || M <= 4);
     // weight tiles along grid y; whole 64-column chunks
     p.wide = !p.xl && d_in % kWK == 0 && ceil_div(d_out, kWN) <= 65535;
     if (p.wide) {  // 128 x 128 tiles; split K (whole bodies and chunks) while there are few tiles
@@ -824,7 +853,7 @@ GemmPlan plan_gemm(int64_t M, int64_t d_in, int64_t d_out, int64_t g) {
         const int64_t kmax = std::max<int64_t>(32 * p.u, std::min<int64_t>((int64_t)(kXlBytes / (2 * M)) - 8, 30 * g));
         sp = std::max<int64_t>(sp, ceil_div(d_in, kmax));
     }
-    const int64_t unit = p.wide ? std::max<int64_t>(32 * p.u, kWK) : 32 * p.u;  // whole bodies (and chunks)
+    const int64_t unit = p.wide ? std::max<int64_t>(32 * p.u, kWK) : p.chunk ? 128 : 32 * p.u;  // whole bodies (and chunks)
     p.kspan = ceil_div(ceil_div(d_in, sp), unit) * unit;
     if (p.chunk)
         while ((size_t)M * (size_t)(p.kspan + 8) * 2 > kXlBytes && p.kspan > 128) p.kspan -= 128;
@@ -891,10 +920,10 @@ hipError_t run_w4a16(const void *X, int64_t M, int64_t d_in, int64_t ldx, const 
         hipLaunchKernelGGL((w4a16_wide_kernel<false, ((U) >= 4 ? 2 : (U) == 2 ? 1 : 0)>), dim3(grid.y, grid.x, grid.z), dim3(kThreads), 0, s, Xk, ldk, M,\
                            d_in, packed, ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);           \
     else if (p.chunk && !kperm)                                                                                       \
-        hipLaunchKernelGGL(w4a16_chunk_kernel<true>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
+        hipLaunchKernelGGL((w4a16_chunk_kernel<true, ((U) >= 4 ? 128 : (U) == 2 ? 64 : 32)>), grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
                            ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \
     else if (p.chunk)                                                                                            \
-        hipLaunchKernelGGL(w4a16_chunk_kernel<false>, grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
+        hipLaunchKernelGGL((w4a16_chunk_kernel<false, ((U) >= 4 ? 128 : (U) == 2 ? 64 : 32)>), grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, \
                            ldp, scales, zeros, g, ng, d_out, p.kspan, out, ldo, stride);                       \
     else if (p.xl)                                                                                               \
         hipLaunchKernelGGL((w4a16_few_kernel<U>), grid, dim3(kThreads), p.lds_bytes, s, Xk, ldk, M, d_in, packed, ldp, \

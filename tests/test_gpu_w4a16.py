@@ -62,7 +62,8 @@ def _layer(rng, d_out, d_in, group):
 
 @pytest.mark.parametrize("M,d_out,d_in,group,with_perm", [
     (1, 256, 1024, 128, False),     # decode, one token
-    (3, 100, 512, 32, False),       # ragged tokens and features; 32-column groups (two-MFMA steps)
+    (3, 100, 512, 32, False),       # ragged tokens and features; 32-column groups, streamed words
+    (12, 100, 512, 32, False),      # ... more tokens: scales staged in LDS
     (16, 384, 2048, 64, True),      # column gather
     (40, 128, 768, 0, False),       # one group per row; two token blocks
     (200, 160, 1024, 128, True),    # four token blocks, ragged
@@ -80,6 +81,9 @@ def _layer(rng, d_out, d_in, group):
     (96, 130, 448, 32, True),       # ... an odd chunk count, column gather
     (64, 64, 4544, 32, False),      # ... K splits of nine chunks
     (40, 64, 768, 96, False),       # ... groups of three 32-column bodies
+    (8, 130, 640, 64, False),       # few tokens, 64-column groups: even/odd words across lane halves, five bodies
+    (1, 96, 1024, 32, True),        # one token, 32-column groups, column gather
+    (4, 50, 352, 32, False),        # few tokens, d_in not a multiple of 128: scales staged in LDS
     (40, 70, 352, 32, False),       # d_in not a multiple of 64: the generic kernel, two token blocks
     (200, 64, 96, 32, True),        # ... four token blocks, column gather
 ])
