@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_few_kernel(const _Float16 *__r
 // swaps per body (word pairs (j, j + 1), j even) put the even words in half 0
 // and the odd words in half 1, and the body's sum is folded at every group end.
 template <bool IL, int GB>
-__global__ __launch_bounds__(kThreads) void w4a16_chunk_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
+__global__ __launch_bounds__(kThreads, 2) void w4a16_chunk_kernel(const _Float16 *__restrict__ X, int64_t ldx, int64_t M,
                                                                int64_t d_in, const uint32_t *__restrict__ packed,
                                                                int64_t ldp, const float *__restrict__ scales,
                                                                const float *__restrict__ zeros, int64_t g, int64_t ng,
