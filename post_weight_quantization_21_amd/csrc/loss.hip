@@ -12,23 +12,23 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void deq_diff_kernel(const float *__restrict__ W, const uint8_t *__restrict__ codes,
                                                             const float *__restrict__ scales, const float *__restrict__ zeros,
-                                                            const int32_t *__restrict__ g_idx, int64_t d_in, int64_t g,
+                                                            const int32_t *__restrict__ g_idx, int64_t d_out, int64_t d_in, int64_t g,
                                                             int64_t ng, float *__restrict__ D) {
 #pragma clang fp contract(off)
-    const int64_t r = blockIdx.y;
-    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < d_in; c += (int64_t)gridDim.x * kThreads) {
-        int64_t gi = g_idx ? (int64_t)g_idx[c] : c / g;
-        gi = gi < 0 ? 0 : (gi >= ng ? ng - 1 : gi);  // malformed g_idx: wrong values, no wild access
-        const float s = scales[r * ng + gi], z = zeros[r * ng + gi];
-        const float wh = ((float)codes[r * d_in + c] - z) * s;
-        D[r * d_in + c] = wh - W[r * d_in + c];
-    }
+    for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y)  // rows grid-stride (grid y is capped)
+        for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < d_in; c += (int64_t)gridDim.x * kThreads) {
+            int64_t gi = g_idx ? (int64_t)g_idx[c] : c / g;
+            gi = gi < 0 ? 0 : (gi >= ng ? ng - 1 : gi);  // malformed g_idx: wrong values, no wild access
+            const float s = scales[r * ng + gi], z = zeros[r * ng + gi];
+            const float wh = ((float)codes[r * d_in + c] - z) * s;
+            D[r * d_in + c] = wh - W[r * d_in + c];
+        }
 }
 
 __global__ __launch_bounds__(kThreads) void symmetrize_kernel(const float *__restrict__ H, int64_t d, float *__restrict__ Hs) {
-    const int64_t i = blockIdx.y;
-    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < d; j += (int64_t)gridDim.x * kThreads)
-        Hs[i * d + j] = i <= j ? H[i * d + j] : H[j * d + i];
+    for (int64_t i = blockIdx.y; i < d; i += gridDim.y)  // rows grid-stride (grid y is capped)
+        for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < d; j += (int64_t)gridDim.x * kThreads)
+            Hs[i * d + j] = i <= j ? H[i * d + j] : H[j * d + i];
 }
 
 __global__ __launch_bounds__(kThreads) void sum_partials_kernel(const double *__restrict__ p, int64_t n, double *__restrict__ out) {
@@ -71,11 +71,12 @@ hipError_t run_loss(const float *W, const uint8_t *codes, const float *scales, c
     double *part = reinterpret_cast<double *>(base + l.p_off);
     const int64_t g = group_size > 0 ? group_size : d_in;
     const unsigned gx = (unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64);
-    hipLaunchKernelGGL(deq_diff_kernel, dim3(gx, (unsigned)d_out), dim3(kThreads), 0, s, W, codes, scales, zeros, g_idx,
-                       d_in, g, d_in / g, D);
+    hipLaunchKernelGGL(deq_diff_kernel, dim3(gx, (unsigned)std::min<int64_t>(d_out, 65535)), dim3(kThreads), 0, s, W, codes,
+                       scales, zeros, g_idx, d_out, d_in, g, d_in / g, D);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(symmetrize_kernel, dim3(gx, (unsigned)d_in), dim3(kThreads), 0, s, H, d_in, Hs);
+    hipLaunchKernelGGL(symmetrize_kernel, dim3(gx, (unsigned)std::min<int64_t>(d_in, 65535)), dim3(kThreads), 0, s, H, d_in,
+                       Hs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmDesc gd;
     gd.M = d_out;

@@ -63,20 +63,21 @@ __global__ __launch_bounds__(kThreads) void scatter_rank_kernel(const int32_t *_
     if (i < d) perm[rank[i]] = (int32_t)i;
 }
 
-// A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper triangle.
+// A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper
+// triangle.  Rows a are grid-stride (grid y is capped).
 __global__ __launch_bounds__(kThreads) void gather_sym_kernel(const float *__restrict__ H, const int32_t *__restrict__ perm,
                                                               int64_t d, int64_t lda, float *__restrict__ A) {
-    const int64_t a = blockIdx.y;
-    for (int64_t b = a + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < d; b += (int64_t)gridDim.x * kThreads) {
-        int64_t pa = perm ? min(max((int64_t)perm[a], (int64_t)0), d - 1) : a;
-        int64_t pb = perm ? min(max((int64_t)perm[b], (int64_t)0), d - 1) : b;
-        if (pa > pb) {
-            int64_t t = pa;
-            pa = pb;
-            pb = t;
+    for (int64_t a = blockIdx.y; a < d; a += gridDim.y)
+        for (int64_t b = a + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < d; b += (int64_t)gridDim.x * kThreads) {
+            int64_t pa = perm ? min(max((int64_t)perm[a], (int64_t)0), d - 1) : a;
+            int64_t pb = perm ? min(max((int64_t)perm[b], (int64_t)0), d - 1) : b;
+            if (pa > pb) {
+                int64_t t = pa;
+                pa = pb;
+                pb = t;
+            }
+            A[a * lda + b] = H[pa * d + pb];
         }
-        A[a * lda + b] = H[pa * d + pb];
-    }
 }
 
 // lambda = damp_rel * mean(diag A) (fp64, fixed tree); A[i][i] += lambda.  One workgroup.
@@ -802,8 +803,8 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned gx = (unsigned)((d + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(gather_sym_kernel, dim3(gx, (unsigned)d), dim3(kThreads), 0, s, H, act_order ? perm : nullptr,
-                       d, lda, A);
+    hipLaunchKernelGGL(gather_sym_kernel, dim3(gx, (unsigned)std::min<int64_t>(d, 65535)), dim3(kThreads), 0, s, H,
+                       act_order ? perm : nullptr, d, lda, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, A, d, lda, damp_rel);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -228,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void copy_tail_kernel(const float *__rest
 // W[r][k] = Wsrc[r][perm[k]]
 __global__ __launch_bounds__(kThreads) void permute_cols_kernel(const float *__restrict__ src, const int32_t *__restrict__ perm,
                                                                 int64_t d_out, int64_t d_in, float *__restrict__ W) {
-    const int64_t r = blockIdx.y;
-    for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < d_in; k += (int64_t)gridDim.x * kThreads)
-        W[r * d_in + k] = src[r * d_in + clamp_col(perm[k], d_in)];
+    for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y)  // rows grid-stride (grid y is capped)
+        for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < d_in; k += (int64_t)gridDim.x * kThreads)
+            W[r * d_in + k] = src[r * d_in + clamp_col(perm[k], d_in)];
 }
 
 // W[r][k] = W[r][perm[k]] in place, one row at a time through LDS (d_in floats,
@@ -427,7 +427,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         const unsigned gx = (unsigned)std::min<int64_t>(ceil_div(d_in, kThreads), 64);
-        hipLaunchKernelGGL(permute_cols_kernel, dim3(gx, (unsigned)d_out), dim3(kThreads), 0, s, Wc, pp, d_out, d_in, W);
+        hipLaunchKernelGGL(permute_cols_kernel, dim3(gx, (unsigned)std::min<int64_t>(d_out, 65535)), dim3(kThreads), 0, s, Wc, pp, d_out, d_in, W);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (g_idx) {
