@@ -17,7 +17,7 @@ import pytest
 
 import datagen
 import post_weight_quantization_21_amd as gq
-from gpu_util import compare_layer, cuda, host, log, torch_mod
+from gpu_util import compare_layer, cuda, host, log, torch_mod, assert_grid_parity
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -96,5 +96,5 @@ def test_full_size_layer(oracle_mod, name):
     rel_loss = abs(gout["loss"] - ref["loss"]) / ref["loss"]
     log(f"  {name}: {st} loss gpu={gout['loss']:.6e} ref={ref['loss']:.6e} rel={rel_loss:.2e} ({time.time() - t0:.0f}s)")
     assert st["match"] >= 0.999
-    assert st["scale_rel_clean"] <= 1e-5 and st["zero_rel_clean"] == 0.0
+    assert_grid_parity(st)
     assert rel_loss <= 1e-3
