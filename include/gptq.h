@@ -215,6 +215,28 @@ GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, 
                                 int32_t *g_idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * gptq_quantize_layer for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid device allocation.  It
+ * takes no workspace: its scratch memory is a fixed array of
+ * GPTQ_NOALLOC_SCRATCH_BYTES in the library's device image, one per device
+ * (placed by the runtime when the library first runs on that device, held
+ * until the process ends); it calls no allocator.  Arguments, results and
+ * kernels are those of gptq_quantize_layer (the same bits), without ws.
+ *   Returns GPTQ_ERR_WORKSPACE, launching nothing, when the layer needs more
+ *   scratch than the array holds: gptq_workspace_bytes(GPTQ_OP_QUANTIZE, ...)
+ *   > GPTQ_NOALLOC_SCRATCH_BYTES (e.g. 4096 x 4096 or 8192 x 8192 layers in
+ *   natural order fit: 16 and 32 MiB; act-order adds d_out x d_in bytes).
+ *   Nothing in the array needs to start at zero.  Every call on one device
+ *   shares that device's array: calls that overlap in time on one device (on
+ *   different streams, or from several host threads) race and give wrong
+ *   results; calls on one stream are ordered and safe.
+ */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+GPTQ_API gptq_status gptq_quantize_layer_noalloc(float *W, int64_t d_out, int64_t d_in, const float *U,
+                                                 const int32_t *perm, const gptq_config *cfg, uint8_t *codes,
+                                                 float *scales, float *zeros, int32_t *g_idx, hipStream_t stream);
+
+/*
  * Round-to-nearest baseline (page "PTQ 权重量化：从 GPTQ 到 AWQ", section on
  * RTN's limits: every weight rounded on its own): same grids as above fitted
  * on the original W, no error feedback, natural column order.  Uses bits,

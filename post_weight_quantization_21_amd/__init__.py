@@ -26,7 +26,9 @@ EXPORTED = (
     "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
     "gptq_pack_codes", "gptq_w4a16_gemm", "gptq_hessian_accumulate_tokens",
     "gptq_channel_stats", "gptq_smooth_scales", "gptq_awq_search", "gptq_scale_layer",
+    "gptq_quantize_layer_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GPTQ_NOALLOC_SCRATCH_BYTES
 
 
 class GptqError(RuntimeError):
@@ -69,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_hessian_accumulate": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
         "gptq_prepare_hinv": [vp, vp, i64, cfgp, vp, vp, vp, vp, sz, vp],
         "gptq_quantize_layer": [vp, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp, sz, vp],
+        "gptq_quantize_layer_noalloc": [vp, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp],
         "gptq_rtn_quantize": [vp, i64, i64, cfgp, vp, vp, vp, vp],
         "gptq_layer_loss": [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, vp],
         "gptq_workspace_bytes": [ctypes.c_int, i64, i64, i64, cfgp, ctypes.POINTER(sz)],
@@ -185,6 +188,15 @@ def quantize_layer(W, U, cfg: Config, codes, scales, zeros, perm=None, g_idx=Non
     _check(load_library().gptq_quantize_layer(_ptr(W), d_out, d_in, _ptr(U), _ptr(perm), ctypes.byref(cfg),
                                               _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(ws),
                                               ws.numel(), _stream(stream)))
+
+
+def quantize_layer_noalloc(W, U, cfg: Config, codes, scales, zeros, perm=None, g_idx=None, stream=None) -> None:
+    """quantize_layer without a workspace: the library's fixed scratch array (NOALLOC_SCRATCH_BYTES)."""
+    _need_cuda(W, U, codes, scales, zeros, perm, g_idx)
+    d_out, d_in = W.shape
+    _check(load_library().gptq_quantize_layer_noalloc(_ptr(W), d_out, d_in, _ptr(U), _ptr(perm), ctypes.byref(cfg),
+                                                      _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                                      _stream(stream)))
 
 
 def rtn_quantize(W, cfg: Config, codes, scales, zeros, stream=None) -> None:

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -37,6 +38,50 @@ gptq_status check_cfg(const gptq_config *c, int64_t d_in, const char *fn) {
     if (c->grid == GPTQ_GRID_TENSOR && c->group_size != 0)
         return fail(GPTQ_ERR_INVALID_ARG, "%s: a per-tensor grid needs group_size 0", fn);
     return GPTQ_OK;
+}
+
+gptq_status check_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
+                           const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros, int32_t *g_idx,
+                           const char *fn) {
+    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
+    gptq_status st = check_cfg(cfg, d_in, fn);
+    if (st != GPTQ_OK) return st;
+    if (!W || !U || !codes || !scales || !zeros) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (cfg->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "%s: act_order needs perm", fn);
+    if (!aligned(W) || !aligned(U) || !aligned(scales, 4) || !aligned(zeros, 4) || (perm && !aligned(perm, 4)) ||
+        (g_idx && !aligned(g_idx, 4)))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (!gptq::quantize_supported(*cfg, d_in))
+        return fail(GPTQ_ERR_UNSUPPORTED, "%s: block_size=%d group_size=%d not supported", fn, cfg->block_size, cfg->group_size);
+    if (d_out > ((int64_t)1 << 21)) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_out above 2^21", fn);  // 64-row tiles on grid y
+    return GPTQ_OK;
+}
+
+// Scratch memory of gptq_quantize_layer_noalloc: one fixed array per device,
+// part of the library's device image (the runtime places it on each device
+// the library runs on, for the life of the process).  In host code `scratch`
+// names a host-side stand-in: the device copy's address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GPTQ_NOALLOC_SCRATCH_BYTES];
+
+hipError_t scratch_address(void **out) {
+    constexpr int kMaxDevices = 64;
+    static void *addr[kMaxDevices] = {};
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -151,19 +196,26 @@ gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const flo
                                 const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros, int32_t *g_idx,
                                 void *ws, size_t ws_bytes, hipStream_t stream) {
     const char *fn = "gptq_quantize_layer";
-    if (d_out <= 0 || d_in <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: sizes must be > 0", fn);
-    gptq_status st = check_cfg(cfg, d_in, fn);
+    gptq_status st = check_quantize(W, d_out, d_in, U, perm, cfg, codes, scales, zeros, g_idx, fn);
     if (st != GPTQ_OK) return st;
-    if (!W || !U || !codes || !scales || !zeros) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (cfg->act_order && !perm) return fail(GPTQ_ERR_INVALID_ARG, "%s: act_order needs perm", fn);
-    if (!aligned(W) || !aligned(U) || !aligned(scales, 4) || !aligned(zeros, 4) || (perm && !aligned(perm, 4)) ||
-        (g_idx && !aligned(g_idx, 4)))
-        return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-    if (!gptq::quantize_supported(*cfg, d_in))
-        return fail(GPTQ_ERR_UNSUPPORTED, "%s: block_size=%d group_size=%d not supported", fn, cfg->block_size, cfg->group_size);
-    if (d_out > ((int64_t)1 << 21)) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_out above 2^21", fn);  // 64-row tiles on grid y
     const size_t need = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_quantize(W, d_out, d_in, U, perm, *cfg, codes, scales, zeros, g_idx, ws, stream), fn);
+}
+
+gptq_status gptq_quantize_layer_noalloc(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
+                                        const gptq_config *cfg, uint8_t *codes, float *scales, float *zeros,
+                                        int32_t *g_idx, hipStream_t stream) {
+    const char *fn = "gptq_quantize_layer_noalloc";
+    gptq_status st = check_quantize(W, d_out, d_in, U, perm, cfg, codes, scales, zeros, g_idx, fn);
+    if (st != GPTQ_OK) return st;
+    const size_t need = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
+    if (need > GPTQ_NOALLOC_SCRATCH_BYTES)
+        return fail(GPTQ_ERR_WORKSPACE, "%s: this layer needs %zu scratch bytes, above the fixed %zu of the entry point",
+                    fn, need, (size_t)GPTQ_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    st = hip_status(scratch_address(&ws), fn);
+    if (st != GPTQ_OK) return st;
     return hip_status(gptq::run_quantize(W, d_out, d_in, U, perm, *cfg, codes, scales, zeros, g_idx, ws, stream), fn);
 }
 
