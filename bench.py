@@ -5,7 +5,12 @@ resident in HBM: H = 2 X X^T over all calibration tokens, damping + inverse
 factor, and the column pass with lazy batch updates (W restored from a pristine
 device copy first).  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload q_proj_7b] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload up_proj_70b] [--no-cpu-baseline]
+
+The default workload is the largest single-GPU one, up_proj_70b (W 28672 x 8192, X 8192 x 131072 bf16,
+4-bit symmetric groups of 128, Hessian column order).  Kernel times for the roofline objects come from HIP
+events recorded on the streams the kernels run on: around the Hessian call, and (library timing, see
+gptq_timing_enable) around every lazy-update product and batch kernel of the column pass.
 """
 from __future__ import annotations
 
@@ -29,28 +34,46 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per hessian_accumulate call from the committed counter runs, if they were
-    taken on this workload with the current kernel source; else None."""
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch (kind "hessian": one hessian_accumulate call; "lazy": the lazy-update products
+    of one layer) from the committed counter runs, if they were taken on this workload with the current
+    kernel sources; else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hessian_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, rec["kernel_source"]), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != sha:
+    srcs = rec.get("kernel_sources") or [rec["kernel_source"]]
+    shas = rec.get("kernel_sources_sha256") or [rec["kernel_source_sha256"]]
+    for src, want in zip(srcs, shas):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != want:
+                return None
+    if rec.get("workload") != workload:
         return None
     return int(rec["traffic_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
-    """The oracle as it stands, timed on a bounded sample of the same workload."""
+    """The oracle as it stands, timed on a bounded sample of the same workload and scaled to one layer:
+    H on the first tokens (fp64 X X^T scales linearly in tokens), the full factor, the column pass on the
+    first rows (rows are independent given U)."""
     import oracle
     d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
-    n_s = min(n, 262144)
-    rows = min(d_out, 1024)
+    n_s = min(n, max(4096, int(262144 * (4096 / d_in) ** 2 / 4)))  # about 10 s of fp64 products
+    rows = min(d_out, max(128, int(1024 * (4096 / d_in) ** 2)))
     t0 = time.perf_counter()
     H = oracle.hessian(lay["X"][:, :n_s])
     t_h = time.perf_counter() - t0
@@ -67,7 +90,7 @@ def cpu_baseline(lay: dict, cfg_d: dict) -> dict:
     t_q = time.perf_counter() - t0
     est_ms = 1e3 * (t_h * n / n_s + t_p + t_q * d_out / rows)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": cores, "kind": "oracle",
+    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": cores, "cpu": cpu_model(), "kind": "oracle",
             "sample": (f"H on {n_s} of {n} tokens (x{n / n_s:g}), full {d_in}x{d_in} factor, column pass on "
                        f"{rows} of {d_out} rows (x{d_out / rows:g}); measured {t_h:.2f}+{t_p:.2f}+{t_q:.2f} s")}
 
@@ -249,7 +272,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="q_proj_7b")
+    ap.add_argument("--workload", default="up_proj_70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a16", type=int, default=0, metavar="M",
                     help="instead: time the W4A16 product of M tokens with the packed 28672x8192 layer")
@@ -344,9 +367,37 @@ def main() -> int:
     t_h, t_p, t_c, t_q = ph.mean(axis=0)
     log(f"phases (ms): hessian {t_h:.3f}  prepare {t_p:.3f}  copy {t_c:.3f}  quantize {t_q:.3f}  step {ms_step:.3f}")
 
+    # Kernel times of the column pass: the same steps again with the library's event timing on
+    # (two event records per launch, on the launch's own stream).
+    gq.timing_enable(True)
+    gq.timing_read(gq.TIMED_LAZY)
+    gq.timing_read(gq.TIMED_BATCH)
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    lazy_ms, lazy_n = gq.timing_read(gq.TIMED_LAZY)
+    batch_ms, batch_n = gq.timing_read(gq.TIMED_BATCH)
+    gq.timing_enable(False)
+    lazy_ms /= args.steps
+    batch_ms /= args.steps
+    log(f"column pass kernels per step: lazy-update products {lazy_ms:.3f} ms ({lazy_n // args.steps} launches), "
+        f"batch kernels {batch_ms:.3f} ms ({batch_n // args.steps} launches)")
+
     syrk_flops = float(d_in) * (d_in + 1) * n
     lazy_flops = float(d_out) * d_in * max(0, d_in - lay["block"])
-    achieved = syrk_flops / (t_h * 1e-3) / 1e12
+    syrk_tf = syrk_flops / (t_h * 1e-3) / 1e12
+    lazy_tf = lazy_flops / (lazy_ms * 1e-3) / 1e12 if lazy_ms > 0 else 0.0
+    roof_syrk = {"bound": "mfma", "achieved": round(syrk_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(syrk_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload, "hessian"),
+                 "kernel": "hessian_accumulate (syrk_bf16_kernel + split-K reduce" +
+                           (" + fp64 diagonal)" if lay["act_order"] else ")"),
+                 "flops_per_launch": syrk_flops, "ms_per_launch": round(t_h, 3)}
+    roof_lazy = {"bound": "mfma", "achieved": round(lazy_tf, 1), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(lazy_tf / PEAK_F32_TFLOPS, 4), "traffic": measured_traffic(args.workload, "lazy"),
+                 "kernel": "gemm_f32_kernel (the column pass's lazy-update products, all launches of one layer)",
+                 "flops_per_launch": lazy_flops, "ms_per_launch": round(lazy_ms, 3),
+                 "launches_per_layer": lazy_n // args.steps}
+    dominant = roof_lazy if lazy_ms > t_h else roof_syrk
     out = {
         "metric": METRIC,
         "value": round(ms_step, 3),
@@ -364,16 +415,11 @@ def main() -> int:
                    "bits": lay["bits"], "symmetric": lay["sym"], "group_size": lay["group"],
                    "block_size": lay["block"], "damp_rel": lay["damp"], "act_order": lay["act_order"],
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload),
-                     "kernel": "hessian_accumulate (syrk_bf16_kernel + split-K reduce)",
-                     "flops_per_launch": syrk_flops},
+        "roofline": dominant,
+        "rooflines": {"xxt_syrk": roof_syrk, "lazy_update": roof_lazy},
         "phases_ms": {"hessian": round(t_h, 3), "prepare": round(t_p, 3), "restore_w": round(t_c, 3),
-                      "quantize": round(t_q, 3)},
-        "lazy_update": {"flops": lazy_flops,
-                        "tflops_lower_bound": round(lazy_flops / (t_q * 1e-3) / 1e12, 2),
-                        "peak": PEAK_F32_TFLOPS,
-                        "note": "lazy-update flops over the whole column-pass phase (batch kernels included)"},
+                      "quantize": round(t_q, 3), "quantize_batch_kernels": round(batch_ms, 3),
+                      "quantize_lazy_products": round(lazy_ms, 3)},
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()

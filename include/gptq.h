@@ -99,7 +99,11 @@ typedef struct {
     int32_t bits;       /* 2..8 */
     int32_t symmetric;  /* 1: symmetric grid, 0: asymmetric grid (see above) */
     int32_t group_size; /* 0 (one group per row) or a divisor of d_in */
-    int32_t block_size; /* lazy batch width B: 32, 64 or 128 */
+    int32_t block_size; /* lazy batch width B: 1 (the unblocked update) or a
+                           multiple of 32.  Every B gives the same sums in
+                           another fp32 order; the batch kernel runs batches of
+                           the largest of 128, 96, 64, 32 dividing B (128 for
+                           B = 1), and B > 128 forms blocks of such batches. */
     float damp_rel;     /* lambda = damp_rel * mean(diag H), >= 0 */
     int32_t act_order;  /* 1: process columns by descending diag(H) */
     int32_t grid;       /* gptq_grid: when the grids are fitted */
@@ -178,8 +182,10 @@ GPTQ_API gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, con
  * Part of the inverse's assembly runs on a second stream of the library's own
  * (one per device, created on first use, default priority), forked from and
  * joined back to `stream` with events, so the call stays ordered on `stream`.
- * Calls on one device from several host threads share that stream and are
- * serialized on it.
+ * Calls on one device from several host threads share that stream: each call
+ * enqueues its fork, side work and join under a per-device lock, so the calls'
+ * side work runs one after the other, each after its own stream's earlier
+ * work, and each caller's stream waits for its own side work.
  */
 GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg,
                               float *U, int32_t *perm, int32_t *info_dev,
@@ -205,9 +211,11 @@ GPTQ_API gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int6
  *           (DYNAMIC) or in original column order (STATIC); [d_out][1] (TENSOR).
  *   g_idx   [d_in] int32 out or NULL: group of each ORIGINAL column.
  *   ws      scratch of gptq_workspace_bytes(GPTQ_OP_QUANTIZE, d_out, d_in, 0, cfg).
- * GPTQ_ERR_UNSUPPORTED when block_size is not 32/64/128, when group_size
- * is neither 0, nor a divisor of block_size in {32, 64, 128}, nor a multiple
- * of block_size (group_size 0 counts as d_in), or when d_out > 2^21.
+ * GPTQ_ERR_UNSUPPORTED when block_size is neither 1 nor a multiple of 32,
+ * when group_size (0 counts as d_in) is neither a divisor in {32, 64, 128} of
+ * the batch width w (the largest of 128, 96, 64, 32 dividing block_size; 128
+ * for block_size 1) nor a multiple of w nor d_in (one group per row), or when
+ * d_out > 2^21.
  * GPTQ_ERR_INVALID_ARG for an unknown grid, or TENSOR with group_size != 0.
  */
 GPTQ_API gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const float *U, const int32_t *perm,
@@ -339,6 +347,23 @@ GPTQ_API gptq_status gptq_w4a16_gemm(const void *X, gptq_dtype x_dtype, int64_t 
                                      const int32_t *kperm, const uint32_t *packed, const float *scales,
                                      const float *zeros, int32_t group_size, int64_t d_out, float *Y, int64_t ldy,
                                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Kernel timing for benchmarks (off by default).  While enabled, the column
+ * pass records a pair of HIP events around each of its kernel launches of the
+ * kinds below, on the stream the kernel runs on:
+ *   GPTQ_TIMED_LAZY   the trailing-update products of the lazy batches (fp32
+ *                     matrix cores);
+ *   GPTQ_TIMED_BATCH  the batch kernels of the column pass.
+ * gptq_timing_read(op, ms, count) waits for the recorded events of that kind,
+ * returns their summed elapsed milliseconds and how many launches they cover
+ * (host pointers), and forgets them.  Launches that run beside each other on
+ * different streams are timed each on its own.  Process-wide; recording adds
+ * two event records per launch.
+ */
+typedef enum { GPTQ_TIMED_LAZY = 0, GPTQ_TIMED_BATCH = 1 } gptq_timed_op;
+GPTQ_API gptq_status gptq_timing_enable(int32_t on);
+GPTQ_API gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count);
 
 /* Scratch bytes needed by `op` for these sizes (cfg may be NULL for
  * GPTQ_OP_HESSIAN and GPTQ_OP_LOSS).  `out` is a host pointer. */

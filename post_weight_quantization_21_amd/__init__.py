@@ -26,8 +26,9 @@ EXPORTED = (
     "gptq_layer_loss", "gptq_workspace_bytes", "gptq_status_string", "gptq_last_error",
     "gptq_pack_codes", "gptq_w4a16_gemm", "gptq_hessian_accumulate_tokens",
     "gptq_channel_stats", "gptq_smooth_scales", "gptq_awq_search", "gptq_scale_layer",
-    "gptq_quantize_layer_noalloc",
+    "gptq_quantize_layer_noalloc", "gptq_timing_enable", "gptq_timing_read",
 )
+TIMED_LAZY, TIMED_BATCH = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GPTQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_scale_layer": [vp, i64, i64, vp, vp, vp, vp],
         "gptq_hessian_accumulate_tokens": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
         "gptq_w4a16_gemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i64, vp, i64, vp, sz, vp],
+        "gptq_timing_enable": [i32],
+        "gptq_timing_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         "gptq_status_string": [ctypes.c_int],
         "gptq_last_error": [],
     }
@@ -113,6 +116,18 @@ def _need_cuda(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("tensors must be contiguous device tensors")
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record HIP events around the column pass's update products and batch kernels (benchmarks)."""
+    _check(load_library().gptq_timing_enable(int(bool(on))))
+
+
+def timing_read(op: int):
+    """(summed milliseconds, launches) of the recorded kernels of one kind, then forget them."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load_library().gptq_timing_read(int(op), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def workspace_bytes(op: int, d_out: int, d_in: int, n_tok: int = 0, cfg: Config | None = None) -> int:

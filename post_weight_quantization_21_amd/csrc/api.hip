@@ -101,6 +101,18 @@ const char *gptq_status_string(gptq_status st) {
 
 const char *gptq_last_error(void) { return g_last_error; }
 
+gptq_status gptq_timing_enable(int32_t on) {
+    gptq::timing_set(on != 0);
+    return GPTQ_OK;
+}
+
+gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count) {
+    const char *fn = "gptq_timing_read";
+    if (op < 0 || op >= gptq::kTimedOps) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown op %d", fn, op);
+    if (!ms || !count) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    return hip_status(gptq::timing_read(static_cast<gptq::TimedOp>(op), ms, count), fn);
+}
+
 gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_tok, const gptq_config *cfg, size_t *out) {
     if (!out) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: out is NULL");
     if (d_in <= 0 || d_out < 0 || n_tok < 0) return fail(GPTQ_ERR_INVALID_ARG, "gptq_workspace_bytes: bad sizes");

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "gptq.h"
 
@@ -117,6 +118,40 @@ size_t awq_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c);
 hipError_t run_awq_search(const float *W, int64_t d_out, int64_t d_in, const float *H, const double *act_abssum,
                           int64_t n_tok, const gptq_config &c, int n_grid, float *s_out, double *loss_out,
                           int32_t *best_out, void *ws, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Second streams (streams.hip): one per device and purpose, created on first
+// use (default priority).  A call holds `mu` over its whole enqueue sequence
+// on the side stream, so the shared events are recorded and waited on in one
+// host thread's order at a time.
+// ---------------------------------------------------------------------------
+enum SidePurpose { kSidePrepare = 0, kSidePurposes = 1 };
+struct SideStream {
+    static constexpr int kEvents = 4;
+    hipStream_t st = nullptr;
+    hipEvent_t ev[kEvents] = {};
+    std::mutex mu;
+};
+hipError_t side_stream(SidePurpose purpose, SideStream *&out);
+// `to` continues once `from` has reached this point.
+hipError_t signal_wait(hipEvent_t ev, hipStream_t from, hipStream_t to);
+
+// Optional event timing of kernel groups (gptq_timing_enable / gptq_timing_read).
+enum TimedOp { kTimedLazy = 0, kTimedBatch = 1, kTimedOps = 2 };
+void timing_set(bool on);
+hipError_t timing_read(TimedOp op, double *ms, int64_t *count);
+class TimedScope {
+  public:
+    TimedScope(TimedOp op, hipStream_t s);
+    ~TimedScope();
+    TimedScope(const TimedScope &) = delete;
+    TimedScope &operator=(const TimedScope &) = delete;
+
+  private:
+    TimedOp op_;
+    hipStream_t s_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -248,6 +248,191 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     }
 }
 
+// The same product for operands that are both contiguous along the tile's
+// wide dimension (A stored K-major [k][m], B stored [k][n]; the lazy batch
+// update's E^T and U rows), 128 x 128 tiles, with the K slabs streamed
+// straight from global memory into a ring of LDS stages
+// (global_load_lds_dwordx4) three stages ahead of the matrix cores: no
+// staging registers, one barrier per 16-deep stage.  Needs 16-byte aligned
+// operands, leading dimensions and wide extents that are multiples of 4, and
+// K (after the triangular trim) a multiple of 16.
+//
+// Stage layout: [16 k][128 wide] fp32; the 16-byte chunk holding wide columns
+// 4c .. 4c+3 of row k sits at position c ^ (8 (k & 1)), so the two k rows one
+// MFMA operand read touches (lanes 0-31 and 32-63) fall in complementary
+// halves of the 64 LDS banks.
+constexpr int LKS = 16;  // K per stage
+constexpr int LNS = 4;   // stages in the ring
+constexpr int LT = 128;  // tile edge
+
+struct LdsGemmSmem {
+    float a[LNS][LKS][LT];
+    float b[LNS][LKS][LT];
+};
+
+__device__ __forceinline__ int lds_pos(int k, int w) { return ((((w >> 2) ^ ((k & 1) << 3)) << 2) | (w & 3)); }
+
+// Wave `wave` loads rows 4 wave .. 4 wave + 3 of one operand's stage (two
+// instructions of 1 KB: rows 4 wave + 2 i + lane / 32).  Wide chunks past
+// `wide_lim` read the row's first chunk instead (valid memory; the products
+// land in outputs that are never stored).
+__device__ __forceinline__ void lds_stage_load(float (*dst)[LT], const float *src, int64_t ld, int64_t k0, int64_t wide0,
+                                               int64_t wide_lim, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int kk = 4 * wave + 2 * i + (lane >> 5);
+        const int c = (lane & 31) ^ ((kk & 1) << 3);  // logical chunk at this lane's LDS position
+        int64_t w = wide0 + 4 * c;
+        w = w < wide_lim ? w : wide0;
+        const float *g = src + (k0 + kk) * ld + w;
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(g),
+                                         (__attribute__((address_space(3))) void *)(&dst[4 * wave + 2 * i][0]), 16, 0, 0);
+    }
+}
+
+// s_waitcnt: at most n vector-memory operations outstanding, and lgkmcnt(0).
+template <int n>
+__device__ __forceinline__ void lds_wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+}
+
+__device__ __forceinline__ void lds_bar() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
+    constexpr int QB = 2, HW = 64;
+    int tm = blockIdx.y, tn = blockIdx.x;
+    if (g.b_upper) {
+        const int id = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;
+        tn = (int)gridDim.x - 1 - id / (int)gridDim.y;
+        tm = id % (int)gridDim.y;
+    }
+    const int bz = blockIdx.z;
+    if (g.upper_only && tm > tn) return;
+    const int64_t m0 = (int64_t)tm * LT, n0 = (int64_t)tn * LT;
+    const float *A = g.A + bz * g.strideA;
+    const float *B = g.B + bz * g.strideB;
+    float *C = g.C + bz * g.strideC;
+    int64_t kbeg = 0, kend = g.K;
+    if (g.a_upper) kbeg = m0 < kbeg ? kbeg : m0;
+    if (g.b_upper) kend = (n0 + LT) < kend ? (n0 + LT) : kend;
+    kbeg = (kbeg / LKS) * LKS;
+    const int nst = kend > kbeg ? (int)((kend - kbeg) / LKS) : 0;
+
+    __shared__ LdsGemmSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    floatx16 acc[QB][QB];
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    float cold[QB][QB][16];
+    if (EPI == EPI_STORE && g.beta != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
+                    cold[i][j][r] = (m < g.M && n < g.N) ? C[m * g.ldc + n] : 0.0f;
+                }
+    }
+
+    if (nst > 0) {
+        // One stage (four loads per wave) is issued per iteration; past the
+        // end the last stage again, into a slot nobody reads, so the number of
+        // loads in flight at each wait is fixed.
+        auto issue = [&](int st, int slot) {
+            const int64_t k0 = kbeg + (int64_t)(st < nst ? st : nst - 1) * LKS;
+            lds_stage_load(sm.a[slot], A, g.lda, k0, m0, g.M, wave, lane);
+            lds_stage_load(sm.b[slot], B, g.ldb, k0, n0, g.N, wave, lane);
+        };
+#pragma unroll
+        for (int st = 0; st < LNS - 1; ++st) issue(st, st);
+        const int kr = lane >> 5, c = lane & 31;
+        for (int st = 0; st < nst; ++st) {
+            const int slot = st % LNS;
+            lds_wait_vm<8>();  // this wave's loads of stage st landed (two later stages may be in flight),
+                               // its operand reads of the previous stage are done
+            lds_bar();         // ... and every wave's; slot (st - 1) % LNS is free
+            issue(st + LNS - 1, (st + LNS - 1) % LNS);
+            float op[2][2 * QB];
+            auto rd = [&](int kk, float(&o)[2 * QB]) {
+                const int k = kk + kr;
+#pragma unroll
+                for (int i = 0; i < QB; ++i) o[i] = sm.a[slot][k][lds_pos(k, wm * HW + i * 32 + c)];
+#pragma unroll
+                for (int j = 0; j < QB; ++j) o[QB + j] = sm.b[slot][k][lds_pos(k, wn * HW + j * 32 + c)];
+            };
+            rd(0, op[0]);
+#pragma unroll
+            for (int kk = 0; kk < LKS; kk += 2) {
+                const int cur = (kk >> 1) & 1;
+                if (kk + 2 < LKS) rd(kk + 2, op[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < QB; ++i)
+#pragma unroll
+                    for (int j = 0; j < QB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[cur][i], op[cur][QB + j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lds_wait_vm<0>();
+    }
+
+    if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
+                    if (m < g.M && n < g.N && (!g.upper_only || m <= n)) {
+                        float v = g.alpha * acc[i][j][r];
+                        if (g.beta != 0.0f) v += g.beta * cold[i][j][r];
+                        C[m * g.ldc + n] = v;
+                    }
+                }
+    } else {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * HW + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = n0 + wn * HW + j * 32 + mfma32_col(lane);
+                    if (m < g.M && n < g.N) s += (double)acc[i][j][r] * (double)g.Dm[m * g.ldd + n];
+                }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        __shared__ double red[kThreads / kWave];
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        if (tid == 0) {
+            double t = 0.0;
+            for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+            g.partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+        }
+    }
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <int EPI, int T>
@@ -278,15 +463,29 @@ hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s) {
     const bool k4 = g.K % 4 == 0;
     const int va = aligned16(g.A) && g.lda % 4 == 0 && (!bz || g.strideA % 4 == 0) && (g.a_trans ? g.M % 4 == 0 : k4);
     const int vb = aligned16(g.B) && g.ldb % 4 == 0 && (!bz || g.strideB % 4 == 0) && (g.b_trans ? k4 : g.N % 4 == 0);
+    // Both operands contiguous along the tile's wide dimension, aligned, K a
+    // multiple of the stage depth: the direct-to-LDS kernel (128 x 128 tiles).
+    // (The triangular trims start and end K at multiples of the 128-wide tile.)
+    const bool lds_ok = va && vb && g.a_trans && !g.b_trans;
+    const bool kfit = g.K % LKS == 0;
     if (g.epilogue == EPI_DOT) {
-        launch_tile<EPI_DOT, kGemmTile>(g, va, vb, s);
+        if (lds_ok && kfit) {
+            dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
+            hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI_DOT>), grid, dim3(kThreads), 0, s, g);
+        } else {
+            launch_tile<EPI_DOT, kGemmTile>(g, va, vb, s);
+        }
     } else {
         // 64-wide tiles when 128-wide ones would give fewer than two per CU.
         const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128) * g.batch;
-        if (tiles128 < 2 * kCUs)
+        if (tiles128 < 2 * kCUs) {
             launch_tile<EPI_STORE, 64>(g, va, vb, s);
-        else
+        } else if (lds_ok && kfit) {
+            dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
+            hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI_STORE>), grid, dim3(kThreads), 0, s, g);
+        } else {
             launch_tile<EPI_STORE, 128>(g, va, vb, s);
+        }
     }
     return hipGetLastError();
 }

@@ -6,10 +6,12 @@
 // section).  Those rows, scaled by their diagonal's square root, are the rows
 // of U.  Route (2/3 d^3 flops, fp32):
 //   1. H_d = P H P^T + lambda I           (gather + one-workgroup damping)
-//   2. UL-Cholesky H_d = T T^T, T upper   (blocked, from the bottom-right
-//      corner, blocks of 64: one fused kernel per block solves the block's
-//      panel by back substitution, applies the rank-64 update to the leading
-//      block on matrix cores, and factors the next diagonal block on one wave)
+//   2. UL-Cholesky H_d = T T^T, T upper   (blocked on two levels, from the
+//      bottom-right corner: panels of 256 columns, each factored in steps of
+//      64, one launch per step -- the step's column of T by back substitution,
+//      the rank-64 update of the panel's remaining columns on matrix cores, the
+//      next diagonal block factored by one workgroup -- then one rank-256
+//      update of the whole leading block by the fp32 matrix-core GEMM)
 //   3. U = T^-1                           (the diagonal blocks are inverted
 //      all at once after the factorization; the off-diagonal blocks are merged
 //      pairwise by the block formula inv([[A, B], [0, C]]) =
@@ -20,7 +22,6 @@
 #include "quad.h"
 
 #include <algorithm>
-#include <mutex>
 
 namespace gptq {
 namespace {
@@ -474,25 +475,33 @@ struct StepSmem {
     TkkSmem tk;
 };
 
-__device__ __forceinline__ void tile_upper(int64_t t, int nt, int &ti, int &tj) {
-    int i = 0;
-    int64_t before = 0;
-    while (before + (nt - i) <= t) {
-        before += nt - i;
-        ++i;
+// Upper tiles (ti <= tj) of tile columns tj_lo .. nt-1, column by column, rows
+// top to bottom: t -> (ti, tj).  Column tj holds tj + 1 tiles.
+__device__ __forceinline__ void tile_upper_cols(int64_t t, int tj_lo, int nt, int &ti, int &tj) {
+    int j = tj_lo;
+    while (j < nt - 1 && t >= (int64_t)(j + 1)) {
+        t -= j + 1;
+        ++j;
     }
-    ti = i;
-    tj = i + (int)(t - before);
+    tj = j;
+    ti = (int)t;
+}
+
+// Tiles of a step restricted to tile columns tj_lo .. nt-1.
+__host__ __device__ inline int64_t step_tiles(int tj_lo, int nt) {
+    return ((int64_t)nt * (nt + 1) - (int64_t)tj_lo * (tj_lo + 1)) / 2;
 }
 
 template <bool PRE>
 __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, float *__restrict__ Tf,
                                                          const float *__restrict__ Pt, int64_t lda, int64_t k0, int nb,
-                                                         int nt, int32_t *__restrict__ info) {
+                                                         int nt, int tj_lo, int32_t *__restrict__ info) {
     // Tiles in reverse order: workgroup 0 takes the last diagonal tile, whose
-    // factorization of the next block is the step's longest chain.
+    // factorization of the next block is the step's longest chain.  Only the
+    // tile columns tj_lo .. nt-1 (the rest of the current 256-column panel) are
+    // updated; the columns left of the panel get the panel's whole product later.
     int ti, tj;
-    tile_upper((int64_t)nt * (nt + 1) / 2 - 1 - blockIdx.x, nt, ti, tj);
+    tile_upper_cols(step_tiles(tj_lo, nt) - 1 - blockIdx.x, tj_lo, nt, ti, tj);
     const bool diag = ti == tj;
     const bool last = diag && ti == nt - 1;
     const int64_t r0 = (int64_t)ti * FT, s0 = (int64_t)tj * FT;
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
             sm.pi[q + 4 * t][rr] = ai[t];
             if (!diag) sm.pj[q + 4 * t][rr] = aj[t];
         }
-        if (diag && r0 + rr < k0) {  // this row block's P goes into the factor
+        if (tj == nt - 1 && r0 + rr < k0) {  // this row block's P goes into the factor (one tile per row block)
 #pragma unroll
             for (int t = 0; t < NB / 4; ++t)
                 if (q + 4 * t < nb) Tf[(r0 + rr) * lda + k0 + q + 4 * t] = ai[t];
@@ -736,42 +745,16 @@ hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
     return hipSuccess;
 }
 
-// A second stream per device for the inverse's assembly, with the events that
-// fork it from and join it to the caller's stream (default priority).
-struct SideStream {
-    hipStream_t st = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-hipError_t side_stream(SideStream *&out) {
-    static SideStream ss[64];
-    static std::mutex mu;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    SideStream &s = ss[dev];
-    if (!s.st) {
-        if ((e = hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
-    }
-    out = &s;
-    return hipSuccess;
-}
-
-// The side stream continues once the caller's stream has reached this point.
-hipError_t fork_to(const SideStream &ss, hipStream_t s) {
-    hipError_t e = hipEventRecord(ss.fork, s);
-    if (e != hipSuccess) return e;
-    return hipStreamWaitEvent(ss.st, ss.fork, 0);
-}
+// The inverse's assembly runs on the library's second stream for this step
+// (default priority), forked from and joined to the caller's stream with its
+// events: ev[0] forks, ev[1] joins.
+hipError_t fork_to(SideStream &ss, hipStream_t s) { return signal_wait(ss.ev[0], s, ss.st); }
 
 int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
 
-// From this leading size on, P is formed once per row block (p_kernel) rather
-// than by every tile of its row and column.
-constexpr int64_t kPrecomputeP = 2048;
+// Outer level of the factorization: the leading block gets each panel's
+// product at once.
+constexpr int64_t kPanel = 256;  // columns per panel of the outer level
 
 }  // namespace
 
@@ -813,47 +796,77 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                        U, nU, 0.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // UL-Cholesky from the bottom-right corner: factor the last diagonal block,
-    // then one fused step per block: solve its panel, update the leading
-    // block and factor the next diagonal block.  For large leading blocks the
-    // panel solve runs first, once per row block (p_kernel).
-    const int64_t nblk = ceil_div(d, NB);
-    {
-        const int64_t k0 = (nblk - 1) * NB;
-        hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kThreads), 0, s, A, Tf, lda, k0, (int)(d - k0), info);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    // UL-Cholesky from the bottom-right corner, panel by panel (kPanel columns,
+    // aligned from column 0).  Inside a panel, steps of NB columns: the first
+    // diagonal block is factored by panel_kernel; for block k0, step_kernel
+    // forms its column of T for every row above it (back substitution against
+    // T_kk, once per tile and row block; the tiles of the last column store it),
+    // subtracts the rank-NB product from the panel's remaining columns (all
+    // rows above them) and factors the next diagonal block; the panel's last
+    // block has no remaining columns, and p_kernel forms its column of T.  Then
+    // the panel's whole column of T updates the leading block on matrix cores
+    // (K = kPanel): the leading block is read and written once per panel
+    // instead of once per NB columns.
     SideStream *ss = nullptr;
-    if ((e = side_stream(ss)) != hipSuccess) return e;
-    for (int64_t kb = nblk - 1; kb >= 1; --kb) {
-        const int64_t k0 = kb * NB;
-        const int nb = (int)std::min<int64_t>(NB, d - k0);
-        const int nt = (int)ceil_div(k0, FT);
-        const dim3 grid((unsigned)((int64_t)nt * (nt + 1) / 2));
-        if (k0 >= kPrecomputeP) {
-            hipLaunchKernelGGL(p_kernel, dim3((unsigned)kb), dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb);
+    if ((e = side_stream(kSidePrepare, ss)) != hipSuccess) return e;
+    std::lock_guard<std::mutex> side_lock(ss->mu);  // every fork, record and wait below, up to the join
+    const int64_t npan = ceil_div(d, kPanel);
+    for (int64_t q = npan - 1; q >= 0; --q) {
+        const int64_t p0 = q * kPanel, p1 = std::min<int64_t>(p0 + kPanel, d);
+        const int64_t kb_top = ceil_div(p1, NB) - 1, kb_lo = p0 / NB;
+        {
+            const int64_t k0 = kb_top * NB;
+            hipLaunchKernelGGL(panel_kernel, dim3(1), dim3(kThreads), 0, s, A, Tf, lda, k0, (int)std::min<int64_t>(NB, d - k0),
+                               info);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(step_kernel<true>, grid, dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb, nt, info);
-        } else {
-            hipLaunchKernelGGL(step_kernel<false>, grid, dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb, nt, info);
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        // T is complete from column k0 - NB on, and in every column from k0
-        // on: the inverse's work at k0 can start beside the next steps.  (The
-        // right products write Tw only in columns >= k0; the steps still to
-        // come stage P^T there in columns < k0.)
-        if (k0 % kRegion == 0) {
-            if ((e = fork_to(*ss, s)) != hipSuccess) return e;
-            if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st)) != hipSuccess) return e;
+        for (int64_t kb = kb_top; kb >= kb_lo; --kb) {
+            const int64_t k0 = kb * NB;
+            const int nb = (int)std::min<int64_t>(NB, d - k0);
+            if (kb > kb_lo) {
+                // one launch: every tile solves its two row blocks of P, the
+                // tiles of the last column write them into T, the last diagonal
+                // tile factors the next block
+                const int nt = (int)kb, tj_lo = (int)kb_lo;
+                hipLaunchKernelGGL(step_kernel<false>, dim3((unsigned)step_tiles(tj_lo, nt)), dim3(kFThreads), 0, s, A, Tf,
+                                   Tw, lda, k0, nb, nt, tj_lo, info);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            } else if (kb >= 1) {
+                // the panel's last block: its column of T for every row above
+                hipLaunchKernelGGL(p_kernel, dim3((unsigned)kb), dim3(kFThreads), 0, s, A, Tf, Tw, lda, k0, nb);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            // T is complete in every column from k0 on: the inverse's work at
+            // k0 can start beside the next steps.  (The right products write Tw
+            // only in rows >= k0; p_kernel stages P^T in Tw's first NB rows.)
+            if (k0 > 0 && k0 % kRegion == 0) {
+                if ((e = fork_to(*ss, s)) != hipSuccess) return e;
+                if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st)) != hipSuccess) return e;
+            }
+        }
+        if (p0 > 0) {  // A[0:p0, 0:p0] -= T[0:p0, p0:p1] T[0:p0, p0:p1]^T (upper tiles)
+            GemmDesc g;
+            g.M = p0;
+            g.N = p0;
+            g.K = p1 - p0;
+            g.A = Tf + p0;
+            g.lda = lda;
+            g.B = Tf + p0;
+            g.ldb = lda;
+            g.b_trans = 1;
+            g.C = A;
+            g.ldc = lda;
+            g.alpha = -1.0f;
+            g.beta = 1.0f;
+            g.upper_only = 1;
+            if ((e = launch_gemm_f32(g, s)) != hipSuccess) return e;
         }
     }
     // The rest of U = T^-1 once T is complete, then the caller's stream waits
     // for all of it.
     if ((e = fork_to(*ss, s)) != hipSuccess) return e;
     if ((e = assemble_at(Tf, U, Tw, d, lda, 0, ss->st)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ss->join, ss->st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
-    return hipSuccess;
+    return signal_wait(ss->ev[1], ss->st, s);
 }
 
 }  // namespace gptq

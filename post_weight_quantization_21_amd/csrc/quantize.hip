@@ -301,9 +301,27 @@ __global__ __launch_bounds__(kThreads) void gidx_kernel(const int32_t *__restric
     if (k < d_in) g_idx[perm ? clamp_col(perm[k], d_in) : k] = (int32_t)(k / g);
 }
 
+// Columns per batch kernel launch for a lazy batch width B.  Every B gives
+// the same sums (in another fp32 order): the batches only decide when the
+// accumulated errors reach the later columns.  B = 1 (the unblocked update)
+// runs as batches of 128; a multiple of 32 as batches of the largest of 128,
+// 96, 64, 32 that divides it (B > 128: blocks of B made of such batches).
+int64_t batch_cols(const gptq_config &c) {
+    const int64_t B = c.block_size;
+    if (B == 1) return 128;
+    for (int64_t w : {128, 96, 64, 32})
+        if (B % w == 0) return w;
+    return 0;
+}
+
+// The batch kernel's compiled width for batches of bw columns (a batch may be
+// partial: the columns past it are masked).
+int batch_template(int64_t bw) { return bw <= 32 ? 32 : bw <= 64 ? 64 : 128; }
+
 int group_tile(const gptq_config &c, int64_t d_in) {
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
-    return (g <= c.block_size && c.block_size % g == 0) ? (int)g : 0;
+    const int64_t bw = batch_cols(c);
+    return (g <= bw && bw % g == 0) ? (int)g : 0;
 }
 
 // E^T rows are padded to whole workgroups so the batch kernel stores without a row test.
@@ -319,7 +337,9 @@ constexpr int64_t kSuperCols = 1024;  // default columns per superblock of the t
 int64_t super_cols(const gptq_config &c, int64_t d_in, int gt) {
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
     const bool refit = c.grid == GPTQ_GRID_DYNAMIC && gt == 0 && g < d_in;  // g is a multiple of B here
-    const int64_t unit = refit ? g : c.block_size;
+    const int64_t bw = batch_cols(c);
+    const int64_t blk = c.block_size > bw ? c.block_size : bw;  // a lazy block of B > 128 columns
+    const int64_t unit = refit ? g : blk;
     const int64_t want = c.super_cols > 0 ? c.super_cols : kSuperCols;
     const int64_t sc = unit >= want ? unit : (want / unit) * unit;
     return sc;
@@ -339,7 +359,10 @@ struct QuantLayout {
 QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     QuantLayout l;
     l.sc = super_cols(c, d_in, group_tile(c, d_in));
-    l.et_rows = l.sc < d_in ? l.sc : c.block_size;
+    // the batch kernel writes rows for every column of its compiled width, so the
+    // last batch of a stack may write past it by the width minus the batch
+    const int64_t bw = batch_cols(c);
+    l.et_rows = (l.sc < d_in ? l.sc : bw) + (batch_template(bw) - bw);
     l.et_off = 0;
     l.wc_off = align_up((size_t)l.et_rows * (size_t)et_ld(d_out) * sizeof(float), 256);
     const bool copy = c.act_order && d_in > kRowPermMax;  // aligned W assumed (checked at the boundary)
@@ -359,6 +382,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
 hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, int64_t ldet, const float *U, int64_t k0,
                        int64_t k, int64_t c1, int64_t n, hipStream_t s) {
     if (n <= 0 || k <= 0) return hipSuccess;
+    TimedScope ts(kTimedLazy, s);
     GemmDesc g;
     g.M = d_out;
     g.N = n;
@@ -378,10 +402,12 @@ hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, i
 }  // namespace
 
 int quantize_supported(const gptq_config &c, int64_t d_in) {
-    if (c.block_size != 32 && c.block_size != 64 && c.block_size != 128) return 0;
+    const int64_t bw = batch_cols(c);
+    if (bw == 0 || c.block_size > (1 << 20)) return 0;
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
-    if (g <= c.block_size) return c.block_size % g == 0 && (g == 32 || g == 64 || g == 128);
-    return g % c.block_size == 0;
+    if (g <= bw) return bw % g == 0 && (g == 32 || g == 64 || g == 128);
+    // one group per row: fitted once, at column 0, for any row length
+    return g % bw == 0 || g == d_in;
 }
 
 size_t quantize_ws_bytes(int64_t d_out, int64_t d_in, const gptq_config &c) { return quant_layout(d_out, d_in, c).total; }
@@ -391,7 +417,8 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
                         void *ws, hipStream_t s) {
     const int64_t g = c.group_size > 0 ? c.group_size : d_in;
     const int64_t ng = d_in / g;
-    const int B = c.block_size;
+    const int64_t B = batch_cols(c);  // columns per batch kernel launch
+    const int BT = batch_template(B);
     const int gt = group_tile(c, d_in);
     const QuantLayout lay = quant_layout(d_out, d_in, c);
     char *wsb = static_cast<char *>(ws);
@@ -483,12 +510,15 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             a.sym = c.symmetric ? 1 : 0;
             a.vec = vec;
             const int bgt = src == kColumnGrids ? 0 : gt;
-            if (B == 32)
-                e = launch_block_32(a, bgt, src, s);
-            else if (B == 64)
-                e = launch_block_64(a, bgt, src, s);
-            else
-                e = launch_block_128(a, bgt, src, s);
+            {
+                TimedScope ts(kTimedBatch, s);
+                if (BT == 32)
+                    e = launch_block_32(a, bgt, src, s);
+                else if (BT == 64)
+                    e = launch_block_64(a, bgt, src, s);
+                else
+                    e = launch_block_128(a, bgt, src, s);
+            }
             if (e != hipSuccess) return e;
             // the rest of the superblock
             const int64_t c1 = c0 + nc;

@@ -129,6 +129,52 @@ def test_prepare_reports_non_positive_pivot():
     assert int(host(ok)[0]) == 0
 
 
+def test_prepare_concurrent_host_threads(oracle_mod):
+    """Two host threads call prepare on different Hessians, each on its own stream, several times over:
+    every U equals, bit for bit, the one a lone call gives (the calls share the library's side stream and
+    its events)."""
+    import threading
+    torch = torch_mod()
+    d, reps = 1536, 6  # three 512-column regions: the side stream is forked several times per call
+    cfg = gq.config(4, False, 0, 128, 0.01, False)
+    Hs = [cuda(np.triu(_spd_h(oracle_mod, d, 20 + i)).astype(np.float32)) for i in range(2)]
+    nws = gq.workspace_bytes(gq.OP_PREPARE, 0, d, 0, cfg)
+    refs = []
+    for H in Hs:
+        U = torch.empty(d, d, dtype=torch.float32, device="cuda")
+        gq.prepare_hinv(H, cfg, U)
+        refs.append(U)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in Hs]
+    outs = [[torch.empty(d, d, dtype=torch.float32, device="cuda") for _ in range(reps)] for _ in Hs]
+    infos = [[torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(reps)] for _ in Hs]
+    wss = [torch.empty(nws, dtype=torch.uint8, device="cuda") for _ in Hs]
+    errors = []
+    start = threading.Barrier(len(Hs))
+
+    def worker(i):
+        try:
+            start.wait()
+            for r in range(reps):
+                gq.prepare_hinv(Hs[i], cfg, outs[i][r], info=infos[i][r], ws=wss[i], stream=streams[i])
+            streams[i].synchronize()
+        except Exception as exc:  # reported by the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(Hs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(Hs)):
+        want = host(refs[i])
+        for r in range(reps):
+            assert int(host(infos[i][r])[0]) == 0
+            assert np.array_equal(host(outs[i][r]), want), (i, r)
+
+
 # ----------------------------------------------------------------------------
 # RTN baseline: bit-exact
 # ----------------------------------------------------------------------------
@@ -203,6 +249,72 @@ def test_column_pass_with_oracle_factor(oracle_mod, bits, sym, group, block, d_o
     same = (gout["codes"] == ref["codes"]).all(axis=1)
     wq = host(Wd).astype(np.float64)
     assert np.abs(wq[same] - ref["w_at_q"][same]).max() <= 1e-4 * np.abs(ref["w_at_q"]).max()
+
+
+def test_column_pass_many_rows_wide_updates(oracle_mod):
+    """4000 rows (a ragged last 128-row tile) and 3072 columns: the superblock updates are wide enough to
+    run on the direct-to-LDS product (128 x 128 tiles, K streamed in 16-deep stages).  Rows are
+    independent given U, so sampled rows, the ragged tail among them, are compared with the oracle."""
+    torch = torch_mod()
+    d_out, d_in, group, block = 4000, 3072, 128, 128
+    log(f"pass {d_out}x{d_in} wide updates")
+    H = _spd_h(oracle_mod, d_in, 5, "q_proj_7b")
+    U32 = oracle_mod.inv_chol_upper(oracle_mod.damp(H, 0.01)).astype(np.float32)
+    rng = np.random.default_rng(4000)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    rows = np.unique(np.concatenate([rng.choice(d_out, 56, replace=False), np.arange(3968, 4000, 4)]))
+    ref = oracle_mod.gptq_pass(W[rows], U32.astype(np.float64), 4, False, group)
+    cfg = gq.config(4, False, group, block, 0.01, False)
+    ng = d_in // group
+    Wd = cuda(W)
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    ze = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    gq.quantize_layer(Wd, cuda(U32), cfg, codes, sc, ze)
+    torch.cuda.synchronize()
+    gout = dict(codes=host(codes)[rows], scales=host(sc)[rows], zeros=host(ze)[rows])
+    st = compare_layer(gout, dict(codes=ref["codes"], scales=ref["scales"], zeros=ref["zeros"], perm=np.arange(d_in)),
+                       group, d_in)
+    log(f"  {st}")
+    assert st["match"] >= 0.999
+    assert_grid_parity(st)
+    same = (gout["codes"] == ref["codes"]).all(axis=1)
+    wq = host(Wd)[rows].astype(np.float64)
+    assert np.abs(wq[same] - ref["w_at_q"][same]).max() <= 1e-4 * np.abs(ref["w_at_q"]).max()
+
+
+# (block_size, group, bits, sym, d_out, d_in): B = 1 (the unblocked update), multiples of 32 that are not a
+# compiled batch width (96: partial 128-wide batches; 160: batches of 32; 192: of 96), blocks wider than a
+# batch (256), and ragged ends
+BLOCK_CASES = [(1, 128, 4, False, 96, 640), (1, 32, 3, True, 64, 1312), (1, 0, 4, False, 64, 1100),
+               (96, 32, 4, False, 80, 704), (160, 32, 4, True, 64, 1600), (192, 32, 3, False, 64, 1344),
+               (256, 128, 4, False, 72, 1536), (256, 512, 4, True, 48, 2048)]
+
+
+@pytest.mark.parametrize("block,group,bits,sym,d_out,d_in", BLOCK_CASES)
+def test_block_sizes_against_blocked_oracle(oracle_mod, block, group, bits, sym, d_out, d_in):
+    """Any lazy batch width gives the oracle's blocked pass with the same width (the same sums)."""
+    torch = torch_mod()
+    log(f"block {block} g={group} bits={bits} sym={sym} {d_out}x{d_in}")
+    H = _spd_h(oracle_mod, d_in, 7, "q_proj_7b")
+    U32 = oracle_mod.inv_chol_upper(oracle_mod.damp(H, 0.01)).astype(np.float32)
+    rng = np.random.default_rng(block * 7 + d_in)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    ref = oracle_mod.gptq_pass(W, U32.astype(np.float64), bits, sym, group, block)
+    cfg = gq.config(bits, sym, group, block, 0.01, False)
+    ng = gq.n_groups(d_in, group)
+    Wd = cuda(W)
+    codes = torch.empty(d_out, d_in, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    ze = torch.empty(d_out, ng, dtype=torch.float32, device="cuda")
+    gq.quantize_layer(Wd, cuda(U32), cfg, codes, sc, ze)
+    torch.cuda.synchronize()
+    gout = dict(codes=host(codes), scales=host(sc), zeros=host(ze))
+    st = compare_layer(gout, dict(codes=ref["codes"], scales=ref["scales"], zeros=ref["zeros"], perm=np.arange(d_in)),
+                       group, d_in)
+    log(f"  {st}")
+    assert st["match"] >= 0.999
+    assert_grid_parity(st)
 
 
 @pytest.mark.parametrize("super_cols", [128, 512, 0, 2048, 4096])
