@@ -274,6 +274,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="up_proj_70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--super-cols", type=int, default=0,
+                    help="columns per superblock of the two-level lazy update (0: the library default, 1024)")
     ap.add_argument("--w4a16", type=int, default=0, metavar="M",
                     help="instead: time the W4A16 product of M tokens with the packed 28672x8192 layer")
     ap.add_argument("--awq", action="store_true",
@@ -307,7 +309,8 @@ def main() -> int:
     d_out, d_in, n = lay["d_out"], lay["d_in"], lay["n_tok"]
     cfg_d = dict(bits=lay["bits"], sym=lay["sym"], group=lay["group"], block=lay["block"], damp=lay["damp"],
                  act_order=lay["act_order"])
-    cfg = gq.config(lay["bits"], lay["sym"], lay["group"], lay["block"], lay["damp"], lay["act_order"])
+    cfg = gq.config(lay["bits"], lay["sym"], lay["group"], lay["block"], lay["damp"], lay["act_order"],
+                    super_cols=args.super_cols)
 
     if lay["X"].dtype == np.uint16:
         X = torch.from_numpy(lay["X"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -414,7 +417,7 @@ def main() -> int:
         "config": {"workload": args.workload, "d_out": d_out, "d_in": d_in, "n_tok": n, "x_dtype": lay["x_dtype"],
                    "bits": lay["bits"], "symmetric": lay["sym"], "group_size": lay["group"],
                    "block_size": lay["block"], "damp_rel": lay["damp"], "act_order": lay["act_order"],
-                   "parallelism": "none (1 GPU)"},
+                   "super_cols": args.super_cols or 1024, "parallelism": "none (1 GPU)"},
         "roofline": dominant,
         "rooflines": {"xxt_syrk": roof_syrk, "lazy_update": roof_lazy},
         "phases_ms": {"hessian": round(t_h, 3), "prepare": round(t_p, 3), "restore_w": round(t_c, 3),

@@ -248,45 +248,68 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
     }
 }
 
-// The same product for operands that are both contiguous along the tile's
-// wide dimension (A stored K-major [k][m], B stored [k][n]; the lazy batch
-// update's E^T and U rows), 128 x 128 tiles, with the K slabs streamed
-// straight from global memory into a ring of LDS stages
-// (global_load_lds_dwordx4) three stages ahead of the matrix cores: no
-// staging registers, one barrier per 16-deep stage.  Needs 16-byte aligned
-// operands, leading dimensions and wide extents that are multiples of 4, and
-// K (after the triangular trim) a multiple of 16.
+// The same product with K streamed straight from global memory into a ring of
+// LDS stages (global_load_lds_dwordx4), three 16-deep stages ahead of the
+// matrix cores: no staging registers, one barrier per stage; 128 x 128 tiles.
+// Each operand is either K-major (stored [k][wide]: A with a_trans, B without
+// b_trans) or K-contiguous (stored [wide][k]).  Needs 16-byte aligned
+// operands, leading dimensions that are multiples of 4, K-major wide extents
+// that are multiples of 4, and K (after the triangular trims, which start and
+// end at multiples of the tile) a multiple of 16.
 //
-// Stage layout: [16 k][128 wide] fp32; the 16-byte chunk holding wide columns
-// 4c .. 4c+3 of row k sits at position c ^ (8 (k & 1)), so the two k rows one
-// MFMA operand read touches (lanes 0-31 and 32-63) fall in complementary
-// halves of the 64 LDS banks.
+// Stage layouts (8 KB per operand):
+//   K-major      [16 k][128 wide]; the 16-byte chunk of wide columns 4c .. 4c+3
+//                of row k sits at position c ^ (8 (k & 1)), so the two k rows
+//                one operand read touches (lanes 0-31 and 32-63) fall in
+//                complementary halves of the 64 LDS banks;
+//   K-contiguous [128 wide][16 k]; the chunk of k values 4c .. 4c+3 of row r
+//                sits at position c ^ ((r / 4) % 4), so one operand read (32
+//                rows at two k) takes two LDS cycles.
 constexpr int LKS = 16;  // K per stage
 constexpr int LNS = 4;   // stages in the ring
 constexpr int LT = 128;  // tile edge
 
 struct LdsGemmSmem {
-    float a[LNS][LKS][LT];
-    float b[LNS][LKS][LT];
+    float a[LNS][LKS * LT];
+    float b[LNS][LKS * LT];
 };
 
-__device__ __forceinline__ int lds_pos(int k, int w) { return ((((w >> 2) ^ ((k & 1) << 3)) << 2) | (w & 3)); }
+// LDS index of (k, w) in a stage (w: wide index in the tile).
+template <int KM>
+__device__ __forceinline__ int lds_index(int k, int w) {
+    if constexpr (KM)
+        return k * LT + ((((w >> 2) ^ ((k & 1) << 3)) << 2) | (w & 3));
+    else
+        return w * LKS + ((((k >> 2) ^ ((w >> 2) & 3)) << 2) | (k & 3));
+}
 
-// Wave `wave` loads rows 4 wave .. 4 wave + 3 of one operand's stage (two
-// instructions of 1 KB: rows 4 wave + 2 i + lane / 32).  Wide chunks past
-// `wide_lim` read the row's first chunk instead (valid memory; the products
-// land in outputs that are never stored).
-__device__ __forceinline__ void lds_stage_load(float (*dst)[LT], const float *src, int64_t ld, int64_t k0, int64_t wide0,
+// Wave `wave` loads its quarter of one operand's stage in two instructions of
+// 1 KB.  Wide rows/columns past `wide_lim` read the tile's first one instead
+// (valid memory; the products land in outputs that are never stored).
+template <int KM>
+__device__ __forceinline__ void lds_stage_load(float *dst, const float *src, int64_t ld, int64_t k0, int64_t wide0,
                                                int64_t wide_lim, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int kk = 4 * wave + 2 * i + (lane >> 5);
-        const int c = (lane & 31) ^ ((kk & 1) << 3);  // logical chunk at this lane's LDS position
-        int64_t w = wide0 + 4 * c;
-        w = w < wide_lim ? w : wide0;
-        const float *g = src + (k0 + kk) * ld + w;
-        __builtin_amdgcn_global_load_lds(static_cast<const void *>(g),
-                                         (__attribute__((address_space(3))) void *)(&dst[4 * wave + 2 * i][0]), 16, 0, 0);
+        const float *gp;
+        int base;  // first float of this instruction's 1 KB window
+        if constexpr (KM) {
+            const int kk = 4 * wave + 2 * i + (lane >> 5);
+            const int c = (lane & 31) ^ ((kk & 1) << 3);  // logical chunk at this lane's position
+            int64_t w = wide0 + 4 * c;
+            w = w < wide_lim ? w : wide0;
+            gp = src + (k0 + kk) * ld + w;
+            base = (4 * wave + 2 * i) * LT;
+        } else {
+            const int r = 32 * wave + 16 * i + (lane >> 2);
+            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            int64_t w = wide0 + r;
+            w = w < wide_lim ? w : wide0;
+            gp = src + w * ld + k0 + 4 * c;
+            base = (32 * wave + 16 * i) * LKS;
+        }
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(gp),
+                                         (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
     }
 }
 
@@ -303,7 +326,7 @@ __device__ __forceinline__ void lds_bar() {
     asm volatile("" ::: "memory");
 }
 
-template <int EPI>
+template <int EPI, int AKM, int BKM>
 __global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
     constexpr int QB = 2, HW = 64;
     int tm = blockIdx.y, tn = blockIdx.x;
@@ -356,8 +379,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
         // loads in flight at each wait is fixed.
         auto issue = [&](int st, int slot) {
             const int64_t k0 = kbeg + (int64_t)(st < nst ? st : nst - 1) * LKS;
-            lds_stage_load(sm.a[slot], A, g.lda, k0, m0, g.M, wave, lane);
-            lds_stage_load(sm.b[slot], B, g.ldb, k0, n0, g.N, wave, lane);
+            lds_stage_load<AKM>(sm.a[slot], A, g.lda, k0, m0, g.M, wave, lane);
+            lds_stage_load<BKM>(sm.b[slot], B, g.ldb, k0, n0, g.N, wave, lane);
         };
 #pragma unroll
         for (int st = 0; st < LNS - 1; ++st) issue(st, st);
@@ -372,9 +395,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
             auto rd = [&](int kk, float(&o)[2 * QB]) {
                 const int k = kk + kr;
 #pragma unroll
-                for (int i = 0; i < QB; ++i) o[i] = sm.a[slot][k][lds_pos(k, wm * HW + i * 32 + c)];
+                for (int i = 0; i < QB; ++i) o[i] = sm.a[slot][lds_index<AKM>(k, wm * HW + i * 32 + c)];
 #pragma unroll
-                for (int j = 0; j < QB; ++j) o[QB + j] = sm.b[slot][k][lds_pos(k, wn * HW + j * 32 + c)];
+                for (int j = 0; j < QB; ++j) o[QB + j] = sm.b[slot][lds_index<BKM>(k, wn * HW + j * 32 + c)];
             };
             rd(0, op[0]);
 #pragma unroll
@@ -433,6 +456,20 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
     }
 }
 
+template <int EPI>
+void launch_lds(const GemmDesc &g, hipStream_t s) {
+    dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
+    const int akm = g.a_trans ? 1 : 0, bkm = g.b_trans ? 0 : 1;
+    if (akm && bkm)
+        hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI, 1, 1>), grid, dim3(kThreads), 0, s, g);
+    else if (akm)
+        hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI, 1, 0>), grid, dim3(kThreads), 0, s, g);
+    else if (bkm)
+        hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI, 0, 1>), grid, dim3(kThreads), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI, 0, 0>), grid, dim3(kThreads), 0, s, g);
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <int EPI, int T>
@@ -463,29 +500,22 @@ hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s) {
     const bool k4 = g.K % 4 == 0;
     const int va = aligned16(g.A) && g.lda % 4 == 0 && (!bz || g.strideA % 4 == 0) && (g.a_trans ? g.M % 4 == 0 : k4);
     const int vb = aligned16(g.B) && g.ldb % 4 == 0 && (!bz || g.strideB % 4 == 0) && (g.b_trans ? k4 : g.N % 4 == 0);
-    // Both operands contiguous along the tile's wide dimension, aligned, K a
-    // multiple of the stage depth: the direct-to-LDS kernel (128 x 128 tiles).
-    // (The triangular trims start and end K at multiples of the 128-wide tile.)
-    const bool lds_ok = va && vb && g.a_trans && !g.b_trans;
-    const bool kfit = g.K % LKS == 0;
+    // Aligned operands and K a multiple of the stage depth: the direct-to-LDS
+    // kernel (128 x 128 tiles); the register-staged one otherwise, and with
+    // 64 x 64 tiles when 128-wide ones would give fewer than two per CU.
+    const bool lds_ok = va && vb && g.K % LKS == 0;
+    const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128) * g.batch;
     if (g.epilogue == EPI_DOT) {
-        if (lds_ok && kfit) {
-            dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
-            hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI_DOT>), grid, dim3(kThreads), 0, s, g);
-        } else {
+        if (lds_ok)
+            launch_lds<EPI_DOT>(g, s);
+        else
             launch_tile<EPI_DOT, kGemmTile>(g, va, vb, s);
-        }
+    } else if (tiles128 < 2 * kCUs) {
+        launch_tile<EPI_STORE, 64>(g, va, vb, s);
+    } else if (lds_ok) {
+        launch_lds<EPI_STORE>(g, s);
     } else {
-        // 64-wide tiles when 128-wide ones would give fewer than two per CU.
-        const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128) * g.batch;
-        if (tiles128 < 2 * kCUs) {
-            launch_tile<EPI_STORE, 64>(g, va, vb, s);
-        } else if (lds_ok && kfit) {
-            dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
-            hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI_STORE>), grid, dim3(kThreads), 0, s, g);
-        } else {
-            launch_tile<EPI_STORE, 128>(g, va, vb, s);
-        }
+        launch_tile<EPI_STORE, 128>(g, va, vb, s);
     }
     return hipGetLastError();
 }
