@@ -128,7 +128,7 @@ hipError_t run_awq_search(const float *W, int64_t d_out, int64_t d_in, const flo
 enum SidePurpose { kSidePrepare = 0, kSidePurposes = 1 };
 struct SideStream {
     static constexpr int kEvents = 4;
-    hipStream_t st = nullptr;
+    hipStream_t st = nullptr, st2 = nullptr;
     hipEvent_t ev[kEvents] = {};
     std::mutex mu;
 };

@@ -810,6 +810,11 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     SideStream *ss = nullptr;
     if ((e = side_stream(kSidePrepare, ss)) != hipSuccess) return e;
     std::lock_guard<std::mutex> side_lock(ss->mu);  // every fork, record and wait below, up to the join
+    // ev[2]: a panel's column of T is complete; ev[3]: the far part of the last
+    // panel update (second side stream) has ended.
+    hipEvent_t ev_panel = ss->ev[2], ev_rest = ss->ev[3];
+    if ((e = hipEventRecord(ev_rest, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->st2, ev_rest, 0)) != hipSuccess) return e;  // after the damping
     const int64_t npan = ceil_div(d, kPanel);
     for (int64_t q = npan - 1; q >= 0; --q) {
         const int64_t p0 = q * kPanel, p1 = std::min<int64_t>(p0 + kPanel, d);
@@ -844,29 +849,56 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                 if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st)) != hipSuccess) return e;
             }
         }
-        if (p0 > 0) {  // A[0:p0, 0:p0] -= T[0:p0, p0:p1] T[0:p0, p0:p1]^T (upper tiles)
+        if (p0 > 0) {
+            // A[0:p0, 0:p0] -= T[0:p0, p0:p1] T[0:p0, p0:p1]^T (upper part), in two
+            // parts: the next panel's columns [n0, p0) on this stream (the next
+            // steps need them; the previous panel's far part wrote them too, so
+            // it must have ended), and the rest, columns [0, n0), on the
+            // second side stream beside the next panel's steps.
+            const int64_t n0 = std::max<int64_t>(p0 - kPanel, 0);
+            if ((e = hipEventRecord(ev_panel, s)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(s, ev_rest, 0)) != hipSuccess) return e;
             GemmDesc g;
             g.M = p0;
-            g.N = p0;
+            g.N = p0 - n0;
             g.K = p1 - p0;
             g.A = Tf + p0;
             g.lda = lda;
-            g.B = Tf + p0;
+            g.B = Tf + n0 * lda + p0;
             g.ldb = lda;
             g.b_trans = 1;
-            g.C = A;
+            g.C = A + n0;
             g.ldc = lda;
             g.alpha = -1.0f;
-            g.beta = 1.0f;
-            g.upper_only = 1;
+            g.beta = 1.0f;  // the strictly lower part of A is never read
             if ((e = launch_gemm_f32(g, s)) != hipSuccess) return e;
+            if (n0 > 0) {
+                if ((e = hipStreamWaitEvent(ss->st2, ev_panel, 0)) != hipSuccess) return e;
+                GemmDesc r;
+                r.M = n0;
+                r.N = n0;
+                r.K = p1 - p0;
+                r.A = Tf + p0;
+                r.lda = lda;
+                r.B = Tf + p0;
+                r.ldb = lda;
+                r.b_trans = 1;
+                r.C = A;
+                r.ldc = lda;
+                r.alpha = -1.0f;
+                r.beta = 1.0f;
+                r.upper_only = 1;
+                if ((e = launch_gemm_f32(r, ss->st2)) != hipSuccess) return e;
+                if ((e = hipEventRecord(ev_rest, ss->st2)) != hipSuccess) return e;
+            }
         }
     }
     // The rest of U = T^-1 once T is complete, then the caller's stream waits
     // for all of it.
     if ((e = fork_to(*ss, s)) != hipSuccess) return e;
     if ((e = assemble_at(Tf, U, Tw, d, lda, 0, ss->st)) != hipSuccess) return e;
-    return signal_wait(ss->ev[1], ss->st, s);
+    if ((e = signal_wait(ss->ev[1], ss->st, s)) != hipSuccess) return e;
+    return hipStreamWaitEvent(s, ev_rest, 0);
 }
 
 }  // namespace gptq

@@ -1,4 +1,4 @@
-// The second stream of the library, and optional event timing of kernel groups.
+// The side streams of the library, and optional event timing of kernel groups.
 #include <mutex>
 #include <vector>
 
@@ -17,10 +17,12 @@ hipError_t side_stream(SidePurpose purpose, SideStream *&out) {
     std::lock_guard<std::mutex> lock(mu);
     SideStream &s = ss[purpose][dev];
     if (!s.st) {
-        hipStream_t st = nullptr;
+        hipStream_t st = nullptr, st2 = nullptr;
         if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&st2, hipStreamNonBlocking)) != hipSuccess) return e;
         for (int i = 0; i < SideStream::kEvents; ++i)
             if ((e = hipEventCreateWithFlags(&s.ev[i], hipEventDisableTiming)) != hipSuccess) return e;
+        s.st2 = st2;
         s.st = st;
     }
     out = &s;
