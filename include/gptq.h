@@ -141,17 +141,18 @@ GPTQ_API gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void
  * Step 1 from token-major activations, as a layer's inputs arrive during
  * calibration (page "量化经典：LLM.int8 / GPTQ / AWQ", §二 step 1; page "LLM
  * 量化方法原理与实现详解", §4.1: H = 2 X X^T over all calibration tokens).
- * Same result as gptq_hessian_accumulate on the transposed activations.
+ * The SYRK reads the token-major tiles itself (no transposed copy of X).
  *
  *   H      [d_in][d_in] fp32 in/out, upper triangle: H[i][j] += 2 sum_t X[t][i] X[t][j].
  *   hdiag  [d_in] fp64 in/out or NULL, as in gptq_hessian_accumulate.
- *   X      [n_tok][ldx] one row per token, d_in channels used per row; bf16
- *          (raw 16-bit patterns) or fp32; 4-byte aligned, ldx >= d_in.
- *   ws     scratch of gptq_workspace_bytes(GPTQ_OP_HESSIAN_TOKENS, 0, d_in, n_tok, NULL):
- *          a channel-major panel of at most 65536 tokens plus the SYRK's own scratch.
- * Tokens are taken in blocks of 65536, each transposed into the panel and
- * accumulated in turn; repeated calls accumulate further chunks.  The sums
- * equal those of gptq_hessian_accumulate called once per such block.
+ *   X      [n_tok][ldx] one row per token, d_in channels used per row, ldx >= d_in;
+ *          bf16 (raw 16-bit patterns): 8-byte aligned, ldx a multiple of 4;
+ *          fp32: 4-byte aligned.
+ *   ws     scratch of gptq_workspace_bytes(GPTQ_OP_HESSIAN_TOKENS, 0, d_in, n_tok, NULL),
+ *          the same size as gptq_hessian_accumulate's (may be NULL when 0).
+ * For bf16, H equals, bit for bit, that of gptq_hessian_accumulate called with
+ * the same tokens in channel-major layout (hdiag: to fp64 rounding, summed in
+ * another order).  Repeated calls accumulate further chunks.
  */
 GPTQ_API gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *X, gptq_dtype x_dtype,
                                                     int64_t d_in, int64_t n_tok, int64_t ldx, void *ws,

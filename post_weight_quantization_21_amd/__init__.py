@@ -162,7 +162,8 @@ def hessian_accumulate(H, X, hdiag=None, ws=None, stream=None) -> None:
 
 
 def hessian_accumulate_tokens(H, X, hdiag=None, ws=None, stream=None) -> None:
-    """H (fp32 [d,d], upper) += 2 X^T X for token-major X: bf16 or fp32 [n_tok][d], one row per token."""
+    """H (fp32 [d,d], upper) += 2 X^T X for token-major X: bf16 or fp32 [n_tok][d], one row per token.
+    bf16 rows must be a multiple of 4 elements apart (X.stride(0) % 4 == 0) and 8-byte aligned."""
     import torch
     _need_cuda(H, hdiag)
     if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:

@@ -134,8 +134,7 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
         *out = gptq::loss_ws_bytes(d_out, d_in);
         return GPTQ_OK;
     case GPTQ_OP_HESSIAN_TOKENS:
-        *out = gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
-        if (n_tok > 0) *out = std::max(*out, gptq::hessian_tokens_ws_bytes(d_in, n_tok, GPTQ_DT_F32));
+        *out = gptq::hessian_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
         return GPTQ_OK;
     case GPTQ_OP_SMOOTH:
         *out = gptq::smooth_ws_bytes(d_out, d_in);
@@ -169,7 +168,7 @@ gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void *X, gptq
     const size_t need = gptq::hessian_ws_bytes(d_in, n_tok, x_dtype);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
-    return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, ws, stream), fn);
+    return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, false, ws, stream), fn);
 }
 
 gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *X, gptq_dtype x_dtype, int64_t d_in,
@@ -179,13 +178,17 @@ gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *
     if (x_dtype != GPTQ_DT_F32 && x_dtype != GPTQ_DT_BF16) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown dtype", fn);
     if (ldx < d_in) return fail(GPTQ_ERR_INVALID_ARG, "%s: ldx < d_in", fn);
     if (!H || (n_tok > 0 && !X)) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (!aligned(H) || (X && !aligned(X, 4)) || (hdiag && !aligned(hdiag, 8)))
+    if (!aligned(H) || (hdiag && !aligned(hdiag, 8)))
         return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    // bf16: each lane loads 4 channels of a token as one 8-byte word
+    if (x_dtype == GPTQ_DT_BF16 && ((X && !aligned(X, 8)) || ldx % 4 != 0))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: bf16 X must be 8-byte aligned with ldx a multiple of 4", fn);
+    if (x_dtype == GPTQ_DT_F32 && X && !aligned(X, 4)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned X", fn);
     if (n_tok == 0) return GPTQ_OK;
-    const size_t need = gptq::hessian_tokens_ws_bytes(d_in, n_tok, x_dtype);
-    if (!ws || ws_bytes < need)
+    const size_t need = gptq::hessian_ws_bytes(d_in, n_tok, x_dtype);
+    if (need > 0 && (!ws || ws_bytes < need))
         return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
-    return hip_status(gptq::run_hessian_tokens(H, hdiag, X, x_dtype, d_in, n_tok, ldx, ws, stream), fn);
+    return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, true, ws, stream), fn);
 }
 
 gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg, float *U,

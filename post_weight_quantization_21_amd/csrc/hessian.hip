@@ -1,28 +1,48 @@
 // Step 1 of GPTQ: H += 2 X X^T from calibration activations (page "LLM 量化方法
-// 原理与实现详解", §4.1: the layer objective's Hessian is 2 X X^T).
+// 原理与实现详解", §4.1: the layer objective's Hessian is 2 X X^T; page "量化经典：
+// LLM.int8 / GPTQ / AWQ", §二 step 1: the calibration set is run through the layer
+// and its inputs collected, token by token).
 //
 // bf16 activations: a symmetric rank-k update on gfx950 matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate), 256 x 256 tiles per 4-wave
 // workgroup with 128 x 128 per wave (accumulators in AGPRs), so each 16-byte
-// LDS read feeds four MFMAs.  X is [d_in][ldx], one row per channel, tokens
-// contiguous, so both MFMA operands of a tile are row panels of X read along
-// K.  Only tiles on or above the diagonal are computed (the algorithmic
-// d(d+1)/2 * N multiply-adds).  When a layer has too few tiles to fill the
-// chip, tokens are split across workgroups and the partial tiles are summed in
-// a fixed order by a second kernel, so H is bit-reproducible.
+// LDS read feeds four MFMAs.  Only tiles on or above the diagonal are computed
+// (the algorithmic d(d+1)/2 * N multiply-adds).  When a layer has too few tiles
+// to fill the chip, tokens are split across workgroups and the partial tiles
+// are summed in a fixed order by a second kernel, so H is bit-reproducible.
 //
-// Pipeline: the panels stream through a ring of four 32-token LDS stages
-// filled by direct global->LDS loads, three stages ahead of the matrix cores;
-// the MFMA operands of the next 16-token step are read from LDS while the
-// current step's MFMAs run; the LDS reads and global->LDS loads are issued one
-// per MFMA.  Work order: workgroup b runs on XCD b % 8.  The upper tiles, in
-// bands of four tile rows taken column by column, are cut into eight
-// contiguous groups, one per XCD, and every XCD walks its group split after
-// split: the tiles an XCD holds at once share a few row panels in its L2, and
-// all XCDs read the same token range at the same time, so L2 misses are
-// mostly served by the shared last-level cache rather than HBM.
+// Two input layouts share one kernel and one LDS image (per stage, 256 rows =
+// channels of 32 tokens, as four 16-byte chunks of 8 tokens):
+//   channel-major X[d][ldx] (tokens contiguous): each row's 64 bytes of a
+//     stage go straight from global memory into LDS (global_load_lds_dwordx4);
+//   token-major X[n][ldx] (channels contiguous, as a layer's inputs arrive):
+//     each lane loads 8 tokens x 4 channels (8-byte loads, 512 contiguous
+//     bytes per token and wave), transposes them in registers with byte
+//     permutes and writes four 16-byte chunks, one per channel.  No transposed
+//     copy of X is ever made.
+// The LDS image, and so the MFMA operands, are the same in both cases, so both
+// layouts give the same H bit for bit.
+//
+// Pipeline: a ring of four LDS stages, filled ahead of the matrix cores
+// (channel-major: by direct loads, three stages ahead; token-major: through
+// registers, three stages of loads in flight); the MFMA operands of the next
+// 16-token step are read from LDS while the current step's MFMAs run; loads,
+// LDS reads and writes are issued between the MFMAs.  Work order: workgroup b runs
+// on XCD b % 8.  The upper tiles, in bands of four tile rows taken column by
+// column, are cut into eight contiguous groups, one per XCD, and every XCD
+// walks its group split after split: the tiles an XCD holds at once share a
+// few row panels in its L2, and all XCDs read the same token range at the same
+// time, so L2 misses are mostly served by the shared last-level cache.
+//
+// With act-order the fp64 diagonal (the ordering key) is a separate pass over
+// X: summed inside the diagonal tiles, the fp64 work (conversions and fused
+// multiply-adds) did not hide under the MFMAs and made those tiles twice as
+// long, which cost more than reading X once more.
 //
 // fp32 activations go through the fp32 matrix-core GEMM (upper tiles only).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -30,23 +50,26 @@ namespace {
 
 constexpr int TS = 256;        // output tile edge (4 waves, each 128 x 128)
 constexpr int KT = 32;         // tokens per LDS stage: 64 bytes of bf16 per row
-constexpr int CH = KT / 8;     // 16-byte chunks per row and stage
-constexpr int NS = 4;          // LDS ring depth (stages)
 constexpr int BAND = 4;        // tile rows per band of the work order
 constexpr int kThreads = 256;
 constexpr int kCUs = 256;
 constexpr int kXCDs = 8;
 
-// LDS panels: NS stages x 256 rows x 64 B, unpadded.  Logical chunk c of row r
-// sits at position c ^ swz(r).  Row r starts in 16-byte bank group 4 (r % 4)
-// of the 64 four-byte banks, so the position has to separate rows that agree
-// mod 4: with swz(r) = (r / 4) % 4 the 32 rows one b128 read touches at a
-// common chunk spread over all 16 groups, and the read takes its minimum of
-// four LDS cycles (measured with a bank-conflict counter; a swizzle on bits 1
-// and 3 of the row took eight).
+// LDS panels: NS stages of 16 KB per panel.
+// Channel-major image: 256 rows (channels) x 64 B (32 tokens).  Logical chunk
+// c (tokens 8c .. 8c+7) of row r sits at position c ^ swz(r).  Row r starts in
+// 16-byte bank group 4 (r % 4) of the 64 four-byte banks, so the position has
+// to separate rows that agree mod 4: with swz(r) = (r / 4) % 4 the 32 rows one
+// b128 read touches at a common chunk spread over all 16 groups, and the read
+// takes its minimum of four LDS cycles (measured with a bank-conflict counter;
+// a swizzle on bits 1 and 3 of the row took eight).
+// The token-major writes (lane l writes rows 4 l .. 4 l + 3 at one chunk, in an
+// order that depends on (l / 4) % 4) hit groups 4 j' + (t ^ l % 4), distinct
+// over every 16 lanes.
+constexpr int NS = 4;
 struct SyrkSmem {
-    uint4 a[NS][TS][CH];
-    uint4 b[NS][TS][CH];
+    uint4 a[NS][TS][4];
+    uint4 b[NS][TS][4];
 };
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
@@ -95,13 +118,13 @@ __device__ __forceinline__ void tile_of_band(int64_t t, int nt, int &ti, int &tj
     }
 }
 
-// One 1 KB piece of a stage of a 256-row panel, straight from global memory
-// into LDS (global_load_lds_dwordx4: lane l of a wave writes LDS bytes
-// [16 l, 16 l + 16) of the wave's window, i.e. 16 rows of 64 B).  Wave w fills
-// rows 64 w .. 64 w + 63 in four pieces i = 0..3; each lane fetches the global
-// chunk that belongs at its LDS position.  Rows past d are clamped to row d-1
-// (valid memory; those outputs are discarded).
-__device__ __forceinline__ void panel_piece(uint4 (*dst)[CH], const uint16_t *X, int64_t ldx, int64_t d,
+// Channel-major: one 1 KB piece of a stage of a 256-row panel, straight from
+// global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes LDS
+// bytes [16 l, 16 l + 16) of the wave's window, i.e. 16 rows of 64 B).  Wave w
+// fills rows 64 w .. 64 w + 63 in four pieces i = 0..3; each lane fetches the
+// global chunk that belongs at its LDS position.  Rows past d are clamped to
+// row d-1 (valid memory; those outputs are discarded).
+__device__ __forceinline__ void panel_piece(uint4 (*dst)[4], const uint16_t *X, int64_t ldx, int64_t d,
                                             int64_t row0, int64_t k0, int wave, int lane, int i) {
     const int row = wave * 64 + i * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(row);
@@ -112,12 +135,12 @@ __device__ __forceinline__ void panel_piece(uint4 (*dst)[CH], const uint16_t *X,
                                      (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 16][0]), 16, 0, 0);
 }
 
-// The same LDS image of a partial stage (tokens k0 .. kend-1, the rest zero)
-// from masked register loads.
-__device__ __forceinline__ void panel_tail(uint4 (*dst)[CH], const uint16_t *X, int64_t ldx, int64_t d, int64_t row0,
+// Channel-major: the same LDS image of a partial stage (tokens k0 .. kend-1,
+// the rest zero) from masked register loads.
+__device__ __forceinline__ void panel_tail(uint4 (*dst)[4], const uint16_t *X, int64_t ldx, int64_t d, int64_t row0,
                                            int64_t k0, int64_t kend, int tid) {
-    for (int e = tid; e < TS * CH; e += kThreads) {
-        const int row = e / CH, pos = e % CH;
+    for (int e = tid; e < TS * 4; e += kThreads) {
+        const int row = e / 4, pos = e % 4;
         const int c = pos ^ swz(row);
         const int64_t gr = row0 + row, gk = k0 + c * 8;
         uint32_t w[4];
@@ -129,6 +152,40 @@ __device__ __forceinline__ void panel_tail(uint4 (*dst)[CH], const uint16_t *X, 
         }
         dst[row][pos] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+// Token-major: tokens t0 .. t0+7 of four channels, one 8-byte word per token.
+struct TokUnit {
+    uint2 x[8];
+};
+
+// Chunk j of a unit (channel jr = j ^ r of the lane's four, r = (l / 4) % 4,
+// token 2m in the low half of dword m as in memory order along tokens) into
+// row 4 l + jr of a stage at logical chunk tg.  The lanes of a store write the
+// four channels of their quad in different orders, which keeps every store
+// free of bank conflicts.  The unit's dwords are pre-swapped when r / 2 = 1
+// (tok_swap), so the dword choice is fixed per j and only the half-word
+// choice (the byte-permute selector `sel`) depends on the lane.
+__device__ __forceinline__ void tok_swap(TokUnit &u, bool swap) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t a = u.x[i].x, b = u.x[i].y;
+        u.x[i].x = swap ? b : a;
+        u.x[i].y = swap ? a : b;
+    }
+}
+
+__device__ __forceinline__ void tok_store_chunk(uint4 (*dst)[4], const TokUnit &u, int l, int tg, int j,
+                                                uint32_t sel) {
+    const int jr = j ^ ((l >> 2) & 3);
+    uint32_t w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = (j >> 1) ? u.x[2 * m].y : u.x[2 * m].x;
+        const uint32_t hi = (j >> 1) ? u.x[2 * m + 1].y : u.x[2 * m + 1].x;
+        w[m] = __builtin_amdgcn_perm(hi, lo, sel);
+    }
+    dst[4 * l + jr][tg ^ (l & 3)] = make_uint4(w[0], w[1], w[2], w[3]);  // position: tg ^ swz(4 l + jr)
 }
 
 // s_waitcnt with lgkmcnt(0) and at most n vector-memory operations outstanding.
@@ -151,10 +208,14 @@ struct Frags {
     bf16x8 a[4], b[4];
 };
 
-// grid.x = 8 * ceil(tiles / 8) * splits.  Each wave owns a
-// 128 x 128 quarter of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16
-// accumulators.  out_partial == nullptr: H += 2 acc (upper triangle); else the
-// raw partial tile goes to out_partial[split * ntiles + row-major tile index].
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// grid.x = 8 * ceil(tiles / 8) * splits.  Each wave owns a 128 x 128 quarter
+// of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators.
+// out_partial == nullptr: H += 2 acc (upper triangle); else the raw partial
+// tile goes to out_partial[split * ntiles + row-major tile index].
+template <bool TOK>
 __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx, int64_t d,
                                                              int64_t n_tok, int64_t kchunk, int nt, int64_t ntiles,
                                                              int splits, float *__restrict__ H,
@@ -174,7 +235,8 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
     const bool has_tail = kend > kbeg + (int64_t)nfull * KT;
 
     __shared__ SyrkSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     // In a diagonal tile the lower-left quarter lies below the diagonal: it is
     // computed with the others (uniform control flow) and never stored.
@@ -192,70 +254,172 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
     // multiples of 32, so they share one swizzle; logical chunk 2 ks + lane / 32.
     const int lrow = lane & 31, half = lane >> 5;
     const int sw = swz(lrow);
-    // Stage st of both panels into ring slot `slot` (diagonal tiles load their
-    // one panel twice, which keeps the load count per stage uniform: 8 per wave).
-    auto issue_piece = [&](int st, int slot, int p) {
-        const int64_t k0 = kbeg + (int64_t)st * KT;
-        if (p < 4)
-            panel_piece(sm.a[slot], X, ldx, d, r0, k0, wave, lane, p);
-        else
-            panel_piece(sm.b[slot], X, ldx, d, c0, k0, wave, lane, p - 4);
-    };
     // Operand p of a 16-token step: p < 4 is A row block p, else B row block p-4.
-    auto read_frag = [&](int slot, int ks, int p, Frags &f) {
+    auto read_frag = [&](int slot_, int ks, int p, Frags &f) {
         const int pos = (2 * ks + half) ^ sw;
         if (p < 4)
-            f.a[p] = __builtin_bit_cast(bf16x8, sm.a[slot][wm * 128 + p * 32 + lrow][pos]);
+            f.a[p] = __builtin_bit_cast(bf16x8, sm.a[slot_][wm * 128 + p * 32 + lrow][pos]);
         else
-            f.b[p - 4] = __builtin_bit_cast(bf16x8, sm.b[slot][wn * 128 + (p - 4) * 32 + lrow][pos]);
+            f.b[p - 4] = __builtin_bit_cast(bf16x8, sm.b[slot_][wn * 128 + (p - 4) * 32 + lrow][pos]);
     };
     auto mfma = [&](const Frags &f, int q) {
         acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
     };
 
+    // Token-major staging: wave w loads and stores units u = 0, 1 of a stage:
+    // panel A (waves 0, 1) or B (waves 2, 3), 8-token chunk tg = 2 (w % 2) + u,
+    // this lane's 4 channels.  Each token's row is addressed from a wave-uniform
+    // base plus the lane's offset, past d clamped in bounds (discarded).
+    const bool tok_b = wave >= 2;
+    const int64_t tok_base = tok_b ? c0 : r0;
+    const int tok_off = (int)min<int64_t>(4 * lane, ldx - 4 - tok_base);
+    const uint32_t sel0 = (lane >> 2) & 1 ? 0x07060302u : 0x05040100u;  // chunk j: j & 1 ? sel1 : sel0
+    const uint32_t sel1 = (lane >> 2) & 1 ? 0x05040100u : 0x07060302u;
+    const bool tok_swapped = (lane >> 3) & 1;
+    auto tok_load_one = [&](int st, TokUnit &r, int u, int i) {
+        const int64_t t = kbeg + (int64_t)min(st, nfull - 1) * KT + 8 * (2 * (wave & 1) + u) + i;
+        const uint16_t *rowp = X + t * ldx + tok_base;
+        r.x[i] = *reinterpret_cast<const uint2 *>(rowp + tok_off);
+    };
+    auto tok_put_chunk = [&](int slot_, const TokUnit &r, int u, int j) {
+        tok_store_chunk(tok_b ? sm.b[slot_] : sm.a[slot_], r, lane, 2 * (wave & 1) + u, j, (j & 1) ? sel1 : sel0);
+    };
+
     if (nfull > 0) {
-        // Exactly one stage is issued per step (past the end: the last stage
-        // again, into a slot nobody reads), so the in-flight count is fixed:
-        // at each wait, the stage being waited for is followed by one more.
+        if constexpr (!TOK) {
+            // Exactly one stage is issued per step (past the end: the last
+            // stage again, into a slot nobody reads), so the in-flight count is
+            // fixed: at each wait, the stage being waited for is followed by one
+            // more.
+            auto issue_piece = [&](int st, int slot_, int p) {
+                const int64_t k0 = kbeg + (int64_t)st * KT;
+                if (p < 4)
+                    panel_piece(sm.a[slot_], X, ldx, d, r0, k0, wave, lane, p);
+                else
+                    panel_piece(sm.b[slot_], X, ldx, d, c0, k0, wave, lane, p - 4);
+            };
 #pragma unroll
-        for (int st = 0; st < NS - 1; ++st)
+            for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
-            for (int p = 0; p < 8; ++p) issue_piece(min(st, nfull - 1), st, p);
-        wait_vm_lgkm0<16>();  // stage 0 landed
-        bar();
-        Frags f0, f1;
+                for (int p = 0; p < 8; ++p) issue_piece(min(st, nfull - 1), st, p);
+            wait_vm_lgkm0<16>();  // stage 0 landed
+            bar();
+            Frags f0, f1;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) read_frag(0, 0, p, f0);
-        // Each step is two half-steps of 16 MFMAs; the LDS reads of the other
-        // half's operands and the global->LDS loads of the stage NS-1 ahead
-        // are issued one per MFMA (the scheduling fences hold that order), so
-        // the matrix core never waits on instruction issue.
-        for (int k = 0; k < nfull; ++k) {
-            const int cur = k % NS, nxt = (k + 1) % NS;
+            for (int p = 0; p < 8; ++p) read_frag(0, 0, p, f0);
+            // Each step is two half-steps of 16 MFMAs; the LDS reads of the
+            // other half's operands and the global->LDS loads of the stage NS-1
+            // ahead are issued one per MFMA (the scheduling fences hold that
+            // order), so the matrix core never waits on instruction issue.
+            for (int k = 0; k < nfull; ++k) {
+                const int cur = k % NS, nxt = (k + 1) % NS;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                mfma(f0, q);
-                if (q >= 1 && q <= 8) read_frag(cur, 1, q - 1, f1);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f0, q);
+                    if (q >= 1 && q <= 8) read_frag(cur, 1, q - 1, f1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                wait_vm_lgkm0<8>();  // stage k+1 landed (and this wave's operand reads are done)
+                bar();               // ... for every wave; slot (k-1) % NS is free
+                const int st = min(k + NS - 1, nfull - 1), slot_ = (k + NS - 1) % NS;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f1, q);
+                    if (q >= 1 && q <= 8) issue_piece(st, slot_, q - 1);
+                    if (q >= 7 && q <= 14) read_frag(nxt, 0, q - 7, f0);  // unused after the last step
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            wait_vm_lgkm0<8>();  // stage k+1 landed (and this wave's operand reads are done)
-            bar();               // ... for every wave; slot (k-1) % NS is free
-            const int st = min(k + NS - 1, nfull - 1), slot = (k + NS - 1) % NS;
+            wait_vm_lgkm0<0>();
+        } else {
+            // Stage s: loaded into registers R[s % 3] during the second half of
+            // step s - 5 (the prologue for s < 5), one token row per MFMA;
+            // transposed into LDS slot s % 4 during the first half of step
+            // s - 2, one chunk per MFMA; read from the second half of step s - 1
+            // on.  Slot s % 4 last held stage s - 4, whose reads ended in step
+            // s - 4, before the barrier of step s - 3 that every wave writing in
+            // step s - 2 has passed.
+            TokUnit R[3][2];
+            auto load_stage = [&](int st, TokUnit(&r)[2]) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                mfma(f1, q);
-                if (q >= 1 && q <= 8) issue_piece(st, slot, q - 1);
-                if (q >= 7 && q <= 14) read_frag(nxt, 0, q - 7, f0);  // unused after the last step
-                __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) tok_load_one(st, r[u], u, i);
+            };
+            auto put_stage = [&](int slot_, TokUnit(&r)[2]) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    tok_swap(r[u], tok_swapped);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) tok_put_chunk(slot_, r[u], u, j);
+                }
+            };
+            load_stage(0, R[0]);
+            load_stage(1, R[1]);
+            load_stage(2, R[2]);
+            put_stage(0, R[0]);
+            load_stage(3, R[0]);
+            put_stage(1, R[1]);
+            load_stage(4, R[1]);
+            wait_vm_lgkm0<63>();
+            bar();
+            Frags f0, f1;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) read_frag(0, 0, p, f0);
+            auto step = [&](int k, auto rbc) {
+                constexpr int RB = decltype(rbc)::value;  // (k + 2) % 3
+                TokUnit(&r)[2] = R[RB];
+                const int cur = k % NS, nxt = (k + 1) % NS, put = (k + 2) % NS;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f0, q);
+                    if (q >= 1 && q <= 8) read_frag(cur, 1, q - 1, f1);
+                    if (q == 5) tok_swap(r[0], tok_swapped);  // stage k + 2
+                    if (q == 7) tok_swap(r[1], tok_swapped);
+                    if (q >= 8) tok_put_chunk(put, r[(q - 8) >> 2], (q - 8) >> 2, (q - 8) & 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
+                bar();                // ... every wave's: stage k + 1 is complete in LDS
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f1, q);
+                    tok_load_one(k + 5, r[q >> 3], q >> 3, q & 7);
+                    if (q >= 7 && q <= 14) read_frag(nxt, 0, q - 7, f0);  // unused after the last step
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            int k = 0;
+            for (; k + 2 < nfull; k += 3) {
+                step(k, IC<2>());
+                step(k + 1, IC<0>());
+                step(k + 2, IC<1>());
             }
+            if (k < nfull) step(k, IC<2>());
+            if (k + 1 < nfull) step(k + 1, IC<0>());
+            wait_vm_lgkm0<0>();
         }
-        wait_vm_lgkm0<0>();
     }
     if (has_tail) {
         const int64_t k0 = kbeg + (int64_t)nfull * KT;
         __syncthreads();  // every wave is done with the ring
-        panel_tail(sm.a[0], X, ldx, d, r0, k0, kend, tid);
-        panel_tail(sm.b[0], X, ldx, d, c0, k0, kend, tid);
+        if constexpr (!TOK) {
+            panel_tail(sm.a[0], X, ldx, d, r0, k0, kend, tid);
+            panel_tail(sm.b[0], X, ldx, d, c0, k0, kend, tid);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                TokUnit t;
+                const int64_t t0 = k0 + 8 * (2 * (wave & 1) + u);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    t.x[i] = t0 + i < kend ? *reinterpret_cast<const uint2 *>(X + (t0 + i) * ldx + tok_base + tok_off)
+                                           : make_uint2(0u, 0u);
+                tok_swap(t, tok_swapped);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tok_put_chunk(0, t, u, j);
+            }
+        }
         __syncthreads();
         Frags f;
 #pragma unroll
@@ -303,6 +467,16 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
         }
 }
 
+// hdiag[i] += 2 * sum_s part[s][i]  (fixed summation order).
+__global__ __launch_bounds__(kThreads) void diag_reduce_kernel(const double *__restrict__ part, int splits, int64_t d,
+                                                               double *__restrict__ hdiag) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= d) return;
+    double s = 0.0;
+    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * d + i];
+    hdiag[i] += 2.0 * s;
+}
+
 // H[upper] += 2 * sum_s partial[s][tile]  (fixed summation order).
 __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(const float *__restrict__ part, int splits,
                                                                int64_t ntiles, int nt, int64_t d,
@@ -331,53 +505,46 @@ __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(const float *__re
     }
 }
 
-// hdiag[i] += 2 * sum_t X[i][t]^2 in fp64.  One workgroup per channel; rows
-// are read in 16-byte pieces (X and ldx*sizeof(T) are 16-byte aligned at the
-// boundary), four pieces in flight per thread, the ragged end element-wise.
+// hdiag[i] += 2 * sum_t x_it^2 in fp64 (the act-order key), a pass of its own.
 template <typename T>
-__device__ __forceinline__ float widen_elem(T v) {
-    if constexpr (sizeof(T) == 2) {
-        return __uint_as_float((uint32_t)v << 16);
-    } else {
-        return v;
-    }
+__device__ __forceinline__ double widen(T v) {
+    if constexpr (sizeof(T) == 2)
+        return (double)__uint_as_float((uint32_t)v << 16);
+    else
+        return (double)v;
 }
 
+// Channel-major X[d][ldx]: one workgroup per channel; the row is read in
+// 16-byte pieces (X and ldx * element size are 16-byte aligned), four pieces in
+// flight per thread, the ragged end element-wise, then a tree sum.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void diag_f64_kernel(const T *__restrict__ X, int64_t ldx, int64_t n_tok,
-                                                            double *__restrict__ hdiag) {
+__global__ __launch_bounds__(kThreads) void diag_rows_kernel(const T *__restrict__ X, int64_t ldx, int64_t n_tok,
+                                                             double *__restrict__ hdiag) {
     constexpr int kPer = 16 / sizeof(T);  // elements per 16-byte piece
     constexpr int kUnroll = 4;
     const int64_t i = blockIdx.x;
     const T *row = X + i * ldx;
     const int64_t npieces = n_tok / kPer;
     double s = 0.0;
+    auto add_piece = [&](const uint4 &v) {
+        const T *e = reinterpret_cast<const T *>(&v);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const double x = widen<T>(e[k]);
+            s = fma(x, x, s);
+        }
+    };
     int64_t p = threadIdx.x;
     for (; p + (kUnroll - 1) * kThreads < npieces; p += kUnroll * kThreads) {
         uint4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) v[u] = *reinterpret_cast<const uint4 *>(row + (p + u * kThreads) * kPer);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const T *e = reinterpret_cast<const T *>(&v[u]);
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const double x = (double)widen_elem<T>(e[k]);
-                s = fma(x, x, s);
-            }
-        }
+        for (int u = 0; u < kUnroll; ++u) add_piece(v[u]);
     }
-    for (; p < npieces; p += kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + p * kPer);
-        const T *e = reinterpret_cast<const T *>(&v);
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const double x = (double)widen_elem<T>(e[k]);
-            s = fma(x, x, s);
-        }
-    }
+    for (; p < npieces; p += kThreads) add_piece(*reinterpret_cast<const uint4 *>(row + p * kPer));
     for (int64_t t = npieces * kPer + threadIdx.x; t < n_tok; t += kThreads) {
-        const double x = (double)widen_elem<T>(row[t]);
+        const double x = widen<T>(row[t]);
         s = fma(x, x, s);
     }
     __shared__ double red[kThreads];
@@ -388,6 +555,53 @@ __global__ __launch_bounds__(kThreads) void diag_f64_kernel(const T *__restrict_
         __syncthreads();
     }
     if (threadIdx.x == 0) hdiag[i] += 2.0 * red[0];
+}
+
+// Token-major X[n][ldx]: a workgroup takes 64 EPL channels (EPL per lane: bf16
+// four, one 8-byte load per token; fp32 one) over tokens [y tchunk, (y+1) tchunk)
+// in four token phases, one per wave, summed in a fixed order.  part == nullptr:
+// hdiag += 2 s; else part[y][c] = s for a fixed-order reduce.
+template <typename T, int EPL>
+__global__ __launch_bounds__(kThreads) void diag_cols_kernel(const T *__restrict__ X, int64_t ldx, int64_t d,
+                                                             int64_t n_tok, int64_t tchunk,
+                                                             double *__restrict__ hdiag, double *__restrict__ part) {
+    const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
+    const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * EPL;
+    const int64_t t0 = (int64_t)blockIdx.y * tchunk;
+    const int64_t t1 = min(n_tok, t0 + tchunk);
+    double s[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s[e] = 0.0;
+    if (c < d) {
+#pragma unroll 4
+        for (int64_t t = t0 + ph; t < t1; t += 4) {
+            if constexpr (EPL == 4) {  // bf16, c + 4 <= ldx (ldx a multiple of 4)
+                const uint2 v = *reinterpret_cast<const uint2 *>(X + t * ldx + c);
+                const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double x = (double)__uint_as_float(e & 1 ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+                    s[e] = fma(x, x, s[e]);
+                }
+            } else {
+                const double x = widen<T>(X[t * ldx + c]);
+                s[0] = fma(x, x, s[0]);
+            }
+        }
+    }
+    __shared__ double red[4][64 * EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) red[ph][lane * EPL + e] = s[e];
+    __syncthreads();
+    for (int k = threadIdx.x; k < 64 * EPL; k += kThreads) {
+        const int64_t ch = (int64_t)blockIdx.x * 64 * EPL + k;
+        if (ch >= d) continue;
+        const double v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+        if (part)
+            part[(int64_t)blockIdx.y * d + ch] = v;
+        else
+            hdiag[ch] += 2.0 * v;
+    }
 }
 
 struct SyrkPlan {
@@ -424,60 +638,111 @@ SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
     return p;
 }
 
+// Token splits of the token-major diagonal pass: about 2048 workgroups, at
+// least 1024 tokens each, at most 64 splits.
+struct DiagPlan {
+    int splits;
+    int64_t tchunk;
+};
+
+DiagPlan plan_diag_cols(int64_t d, int64_t n_tok, int epl) {
+    const int64_t blocks = ceil_div(d, 64 * epl);
+    int64_t s = std::min<int64_t>({(int64_t)64, ceil_div(n_tok, 1024), ceil_div(2048, blocks)});
+    if (s < 1) s = 1;
+    DiagPlan p;
+    p.tchunk = ceil_div(n_tok, s);
+    p.splits = (int)ceil_div(n_tok, p.tchunk);
+    return p;
+}
+
+size_t syrk_part_bytes(const SyrkPlan &p) {
+    return p.splits > 1 ? align_up((size_t)p.splits * (size_t)p.ntiles * TS * TS * sizeof(float), 256) : 0;
+}
+
+size_t diag_part_bytes(int64_t d, int64_t n_tok, gptq_dtype dt) {
+    const DiagPlan q = plan_diag_cols(d, n_tok, dt == GPTQ_DT_BF16 ? 4 : 1);
+    return q.splits > 1 ? (size_t)q.splits * (size_t)d * sizeof(double) : 0;
+}
+
 }  // namespace
 
+// The same for both layouts: the SYRK's partial tiles, then the token-major
+// diagonal pass's partial sums.
 size_t hessian_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt) {
-    if (dt != GPTQ_DT_BF16 || n_tok <= 0) return 0;
-    SyrkPlan p = plan_syrk(d_in, n_tok);
-    if (p.splits <= 1) return 0;
-    return (size_t)p.splits * (size_t)p.ntiles * TS * TS * sizeof(float);
+    if (n_tok <= 0) return 0;
+    const size_t syrk = dt == GPTQ_DT_BF16 ? syrk_part_bytes(plan_syrk(d_in, n_tok)) : 0;
+    return syrk + diag_part_bytes(d_in, n_tok, dt);
 }
 
 hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, int64_t d, int64_t n_tok, int64_t ldx,
-                       void *ws, hipStream_t s) {
+                       bool token_major, void *ws, hipStream_t s) {
     if (n_tok <= 0) return hipSuccess;
+    hipError_t e;
+    size_t syrk_bytes = 0;
     if (dt == GPTQ_DT_BF16) {
         SyrkPlan p = plan_syrk(d, n_tok);
+        syrk_bytes = syrk_part_bytes(p);
         float *part = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
-        hipLaunchKernelGGL(syrk_bf16_kernel, dim3((unsigned)(kXCDs * ceil_div(p.ntiles, kXCDs) * p.splits)),
-                           dim3(kThreads), 0, s,
-                           static_cast<const uint16_t *>(X), ldx, d, n_tok, p.kchunk, p.nt, p.ntiles, p.splits, H,
-                           part);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const dim3 grid((unsigned)(kXCDs * ceil_div(p.ntiles, kXCDs) * p.splits));
+        const uint16_t *Xb = static_cast<const uint16_t *>(X);
+        if (token_major)
+            hipLaunchKernelGGL(syrk_bf16_kernel<true>, grid, dim3(kThreads), 0, s, Xb, ldx, d, n_tok, p.kchunk, p.nt,
+                               p.ntiles, p.splits, H, part);
+        else
+            hipLaunchKernelGGL(syrk_bf16_kernel<false>, grid, dim3(kThreads), 0, s, Xb, ldx, d, n_tok, p.kchunk, p.nt,
+                               p.ntiles, p.splits, H, part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         if (part) {
             hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)(p.ntiles * (TS * TS / (kThreads * 4)))), dim3(kThreads),
                                0, s, part, p.splits, p.ntiles, p.nt, d, H);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if (hdiag) {
-            hipLaunchKernelGGL(diag_f64_kernel<uint16_t>, dim3((unsigned)d), dim3(kThreads), 0, s,
-                               static_cast<const uint16_t *>(X), ldx, n_tok, hdiag);
-            e = hipGetLastError();
-        }
-        return e;
+    } else {
+        // fp32: H += 2 X X^T (channel-major) or 2 X^T X (token-major) on the
+        // fp32 matrix-core GEMM, upper tiles only.
+        const float *Xf = static_cast<const float *>(X);
+        GemmDesc g;
+        g.M = d;
+        g.N = d;
+        g.K = n_tok;
+        g.A = Xf;
+        g.lda = ldx;
+        g.a_trans = token_major ? 1 : 0;
+        g.B = Xf;
+        g.ldb = ldx;
+        g.b_trans = token_major ? 0 : 1;
+        g.C = H;
+        g.ldc = d;
+        g.alpha = 2.0f;
+        g.beta = 1.0f;
+        g.upper_only = 1;
+        if ((e = launch_gemm_f32(g, s)) != hipSuccess) return e;
     }
-    GemmDesc g;
-    g.M = d;
-    g.N = d;
-    g.K = n_tok;
-    g.A = static_cast<const float *>(X);
-    g.lda = ldx;
-    g.a_trans = 0;
-    g.B = static_cast<const float *>(X);
-    g.ldb = ldx;
-    g.b_trans = 1;
-    g.C = H;
-    g.ldc = d;
-    g.alpha = 2.0f;
-    g.beta = 1.0f;
-    g.upper_only = 1;
-    hipError_t e = launch_gemm_f32(g, s);
-    if (e != hipSuccess) return e;
-    if (hdiag) {
-        hipLaunchKernelGGL(diag_f64_kernel<float>, dim3((unsigned)d), dim3(kThreads), 0, s,
-                           static_cast<const float *>(X), ldx, n_tok, hdiag);
+    if (!hdiag) return hipSuccess;
+    const bool bf = dt == GPTQ_DT_BF16;
+    if (!token_major) {
+        if (bf)
+            hipLaunchKernelGGL(diag_rows_kernel<uint16_t>, dim3((unsigned)d), dim3(kThreads), 0, s,
+                               static_cast<const uint16_t *>(X), ldx, n_tok, hdiag);
+        else
+            hipLaunchKernelGGL(diag_rows_kernel<float>, dim3((unsigned)d), dim3(kThreads), 0, s,
+                               static_cast<const float *>(X), ldx, n_tok, hdiag);
+        return hipGetLastError();
+    }
+    const int epl = bf ? 4 : 1;
+    const DiagPlan q = plan_diag_cols(d, n_tok, epl);
+    double *dpart = q.splits > 1 ? reinterpret_cast<double *>(static_cast<char *>(ws) + syrk_bytes) : nullptr;
+    const dim3 grid((unsigned)ceil_div(d, 64 * epl), (unsigned)q.splits);
+    if (bf)
+        hipLaunchKernelGGL((diag_cols_kernel<uint16_t, 4>), grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t *>(X), ldx, d, n_tok, q.tchunk, hdiag, dpart);
+    else
+        hipLaunchKernelGGL((diag_cols_kernel<float, 1>), grid, dim3(kThreads), 0, s, static_cast<const float *>(X),
+                           ldx, d, n_tok, q.tchunk, hdiag, dpart);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (dpart) {
+        hipLaunchKernelGGL(diag_reduce_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, dpart,
+                           q.splits, d, hdiag);
         e = hipGetLastError();
     }
     return e;

@@ -88,7 +88,8 @@ def test_argument_errors_are_synchronous():
     assert b"group_size" in lib.gptq_last_error()
     assert _call_quantize(gq.config(block_size=48, group_size=32)) == gq.ERR_UNSUPPORTED  # neither 1 nor 32 k
     assert _call_quantize(gq.config(block_size=96, group_size=64)) == gq.ERR_UNSUPPORTED  # 64 straddles 96-batches
-    assert _call_quantize(gq.config(block_size=96, group_size=128)) == gq.ERR_UNSUPPORTED  # 128 not a multiple of 96
+    # 128 is not a multiple of 96 (with one group per row, 128 = d_in, any block size would do)
+    assert _call_quantize(gq.config(block_size=96, group_size=128), d_in=384) == gq.ERR_UNSUPPORTED
     assert _call_quantize(gq.config(block_size=128, group_size=16)) == gq.ERR_UNSUPPORTED
     assert _call_quantize(gq.config(), ptr=0) == gq.ERR_INVALID_ARG
     assert _call_quantize(gq.config(), ptr=0x10004) == gq.ERR_INVALID_ARG  # misaligned
