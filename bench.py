@@ -175,8 +175,8 @@ def bench_w4a16(args) -> int:
 
 def bench_tokens(args) -> int:
     """H from token-major activations ([n_tok][d_in] bf16, one row per token, as a layer's inputs
-    arrive) on the workload's shape: per 65536-token block a transpose into a channel-major panel,
-    then the matrix-core SYRK.  Timed per call with X resident; H accumulates across calls."""
+    arrive) on the workload's shape: the matrix-core SYRK reading token-major tiles.  Timed per
+    call with X resident; H accumulates across calls."""
     import torch
 
     import datagen
@@ -213,6 +213,55 @@ def bench_tokens(args) -> int:
            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "note": "SYRK flops over the whole call (split-K reduce included)"},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_calib(args) -> int:
+    """The calibration pass of one layer on the workload's shape: a synthetic layer before it
+    (W_prev [d_in][d_in] bf16, N(0, 1/d_in)) runs forward on token-major inputs X_prev
+    ([n_tok][d_in] bf16, the workload's activations) chunk by chunk, each chunk of outputs
+    accumulated into H on the device (gptq_calibrate_hessian)."""
+    import torch
+
+    import datagen
+    import post_weight_quantization_21_amd as gq
+
+    gq.load_library()
+    dev = torch.device("cuda:0")
+    lay = datagen.make_layer(args.workload)
+    d_in, n = lay["d_in"], lay["n_tok"]
+    if lay["X"].dtype != np.uint16:
+        print(f"bench.py --calib: the {args.workload} workload has fp32 activations; use a bf16 workload", file=sys.stderr)
+        return 2
+    Xp = torch.from_numpy(lay["X"].view(np.int16)).to(dev).view(torch.bfloat16).t().contiguous()  # [n][d_in]
+    del lay
+    gen = torch.Generator(device=dev).manual_seed(0)
+    Wp = (torch.randn(d_in, d_in, generator=gen, device=dev) * d_in ** -0.5).to(torch.bfloat16)
+    H = torch.zeros(d_in, d_in, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(gq.workspace_bytes(gq.OP_CALIBRATE, 0, d_in, n), 1), dtype=torch.uint8, device=dev)
+    run = lambda: gq.calibrate_hessian(H, Xp, Wp, ws=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    fwd = 2.0 * n * d_in * d_in
+    syrk = float(d_in) * (d_in + 1) * n
+    tf = (fwd + syrk) / (ms * 1e-3) / 1e12
+    out = {"metric": "calibrate_hessian_ms", "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "bf16->f32",
+           "data": "synthetic", "config": {"workload": args.workload + "_calibrate", "d_prev": d_in, "d_in": d_in,
+                                           "n_tok": n, "chunk_tokens": gq.calibrate_chunk_tokens(d_in)},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "note": "forward GEMM and SYRK flops over the whole pass"},
            "cpu_baseline": None}
     print(json.dumps(out), flush=True)
     return 0
@@ -281,6 +330,8 @@ def main() -> int:
                     help="instead: time the AWQ scale search (20 alphas) on the workload's layer")
     ap.add_argument("--tokens", action="store_true",
                     help="instead: time H from the workload's activations laid out token-major")
+    ap.add_argument("--calib", action="store_true",
+                    help="instead: time a synthetic layer's forward feeding H chunk by chunk")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this benchmark runs GPTQ on one GPU only "
@@ -293,6 +344,8 @@ def main() -> int:
         return bench_awq(args)
     if args.tokens:
         return bench_tokens(args)
+    if args.calib:
+        return bench_calib(args)
 
     import torch
 

@@ -77,7 +77,8 @@ typedef enum {
     GPTQ_OP_W4A16 = 4, /* n_tok = M, the rows of X */
     GPTQ_OP_HESSIAN_TOKENS = 5,
     GPTQ_OP_SMOOTH = 6, /* gptq_smooth_scales */
-    GPTQ_OP_AWQ = 7     /* gptq_awq_search (cfg: bits, symmetric, group_size) */
+    GPTQ_OP_AWQ = 7,    /* gptq_awq_search (cfg: bits, symmetric, group_size) */
+    GPTQ_OP_CALIBRATE = 8 /* gptq_calibrate_hessian (d_in, n_tok) */
 } gptq_op;
 
 /*
@@ -157,6 +158,45 @@ GPTQ_API gptq_status gptq_hessian_accumulate(float *H, double *hdiag, const void
 GPTQ_API gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *X, gptq_dtype x_dtype,
                                                     int64_t d_in, int64_t n_tok, int64_t ldx, void *ws,
                                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The forward of a linear layer that produces the next layer's calibration
+ * inputs (page "量化经典：LLM.int8 / GPTQ / AWQ", §二 step 1: the calibration
+ * set is run through the model layer by layer and each layer's inputs are
+ * recorded; page "LLM 量化方法原理与实现详解", §3.1: the PTQ flow runs the
+ * calibration data through the model).  On the bf16 matrix cores:
+ *
+ *   Y[t][o] = bf16( sum_i X[t][i] W[o][i] )   (fp32 sums, rounded to nearest even)
+ *
+ *   X  [n_tok][ldx] bf16, token-major; W [d_out][ldw] bf16 (the layer's weight,
+ *      one row per output channel); both 16-byte aligned with ldx, ldw
+ *      multiples of 8 and >= d_prev.
+ *   Y  [n_tok][ldy] bf16 out, ldy >= d_out (2-byte aligned).
+ * No workspace.  n_tok == 0 or d_out == 0 is a no-op.
+ */
+GPTQ_API gptq_status gptq_linear_forward(void *Y, int64_t ldy, const void *X, int64_t ldx, const void *W, int64_t ldw,
+                                         int64_t n_tok, int64_t d_prev, int64_t d_out, hipStream_t stream);
+
+/*
+ * Step 1 fed by that forward, chunk by chunk: for each chunk of
+ * gptq_calibrate_chunk_tokens(d_in) tokens, Y = gptq_linear_forward(X chunk, W)
+ * into the workspace, then gptq_hessian_accumulate_tokens(H, hdiag, Y), so the
+ * layer inputs never exist in full (page "量化经典", §二 step 1; page "LLM
+ * 量化方法原理与实现详解", §4.1).
+ *
+ *   H, hdiag  as in gptq_hessian_accumulate (d_in channels), accumulated.
+ *   X, W      as in gptq_linear_forward with d_out = d_in (W is [d_in][ldw]).
+ *   ws        scratch of gptq_workspace_bytes(GPTQ_OP_CALIBRATE, 0, d_in, n_tok, NULL):
+ *             one chunk of Y plus the SYRK's scratch.
+ * The result equals those two calls made chunk by chunk.
+ */
+GPTQ_API gptq_status gptq_calibrate_hessian(float *H, double *hdiag, const void *X, int64_t ldx, const void *W,
+                                            int64_t ldw, int64_t n_tok, int64_t d_prev, int64_t d_in, void *ws,
+                                            size_t ws_bytes, hipStream_t stream);
+
+/* Tokens per chunk of gptq_calibrate_hessian for d_in channels (about 128 MiB
+ * of bf16 layer inputs, a multiple of 1024 in [1024, 65536]). */
+GPTQ_API int64_t gptq_calibrate_chunk_tokens(int64_t d_in);
 
 /*
  * Steps 2-3 -- column order, damping and the inverse-Hessian factor.

@@ -32,6 +32,12 @@ Steps, in the pages' order:
    pre-passes (page "LLM 量化方法原理与实现详解", §4.2 AWQ and §4.3 SmoothQuant)
    and the equivalent problem (W diag(s), diag(s)^-1 H diag(s)^-1) GPTQ then solves.
 
+9. ``linear_forward``: the forward of the layer before, Y = bf16(X W^T), whose
+   outputs are the calibration inputs step 1 sums over (page "量化经典", §二
+   "方法核心" step 1: the calibration set runs through the model layer by layer;
+   page "LLM 量化方法原理与实现详解", §3.1, the PTQ flow); ``bf16_round`` is
+   the format's round-to-nearest-even.
+
 Every function is pinned by ``tests/test_oracle_*.py`` (closed forms, special
 cases, invariants, brute force and the pages' worked example).
 """
@@ -77,6 +83,31 @@ def widen(X: np.ndarray) -> np.ndarray:
     if X.dtype == np.uint16:
         return (X.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return X.astype(np.float64)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp64 values rounded once to the format's 8
+    significant bits, ties to even; subnormals on the 2^-133 grid; past the
+    largest finite value, inf; NaN -> the quiet NaN 0x7FC0."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)  # a = m 2^e, m in [0.5, 1): the leading bit is 2^(e-1)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))  # spacing of 8-bit significands, the subnormal grid below 2^-126
+    r = np.rint(a / q) * q  # round half to even
+    r = np.where(r >= 2.0 ** 128, np.inf, r)
+    bits = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.signbit(x), bits | np.uint16(0x8000), bits)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# the layer before: calibration forward
+# ----------------------------------------------------------------------------
+def linear_forward(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Y[t][o] = bf16(sum_i X[t][i] W[o][i]): X [n][d_prev] and W [d_out][d_prev]
+    as bf16 bit patterns; the products are exact in fp64, summed in fp64, and
+    the sum rounded once to bf16.  Returns Y's bit patterns [n][d_out]."""
+    return bf16_round(widen(X) @ widen(W).T)
 
 
 # ----------------------------------------------------------------------------

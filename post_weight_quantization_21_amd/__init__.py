@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libgptq.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_LOSS, OP_W4A16, OP_HESSIAN_TOKENS, OP_SMOOTH, OP_AWQ = 0, 1, 2, 3, 4, 5, 6, 7
+OP_CALIBRATE = 8
 
 EXPORTED = (
     "gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_rtn_quantize",
@@ -27,6 +28,7 @@ EXPORTED = (
     "gptq_pack_codes", "gptq_w4a16_gemm", "gptq_hessian_accumulate_tokens",
     "gptq_channel_stats", "gptq_smooth_scales", "gptq_awq_search", "gptq_scale_layer",
     "gptq_quantize_layer_noalloc", "gptq_timing_enable", "gptq_timing_read",
+    "gptq_linear_forward", "gptq_calibrate_hessian", "gptq_calibrate_chunk_tokens",
 )
 TIMED_LAZY, TIMED_BATCH = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GPTQ_NOALLOC_SCRATCH_BYTES
@@ -83,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_scale_layer": [vp, i64, i64, vp, vp, vp, vp],
         "gptq_hessian_accumulate_tokens": [vp, vp, vp, i32, i64, i64, i64, vp, sz, vp],
         "gptq_w4a16_gemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i64, vp, i64, vp, sz, vp],
+        "gptq_linear_forward": [vp, i64, vp, i64, vp, i64, i64, i64, i64, vp],
+        "gptq_calibrate_hessian": [vp, vp, vp, i64, vp, i64, i64, i64, i64, vp, sz, vp],
+        "gptq_calibrate_chunk_tokens": [i64],
         "gptq_timing_enable": [i32],
         "gptq_timing_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         "gptq_status_string": [ctypes.c_int],
@@ -91,7 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, args in sig.items():
         f = getattr(lib, name)
         f.argtypes = args
-        f.restype = ctypes.c_char_p if name in ("gptq_status_string", "gptq_last_error") else ctypes.c_int
+        f.restype = (ctypes.c_char_p if name in ("gptq_status_string", "gptq_last_error")
+                     else ctypes.c_int64 if name == "gptq_calibrate_chunk_tokens" else ctypes.c_int)
     _lib = lib
     return lib
 
@@ -179,6 +185,44 @@ def hessian_accumulate_tokens(H, X, hdiag=None, ws=None, stream=None) -> None:
         ws = _workspace(workspace_bytes(OP_HESSIAN_TOKENS, 0, d, n), X.device)
     _check(load_library().gptq_hessian_accumulate_tokens(_ptr(H), _ptr(hdiag), _ptr(X), dt, d, n, X.stride(0),
                                                          _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _bf16_rows(t, name):
+    import torch
+    if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 or t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a 2-D bfloat16 device tensor with unit stride along its rows")
+
+
+def linear_forward(Y, X, W, stream=None) -> None:
+    """Y [n_tok][d_out] (bf16) = bf16(X W^T): X bf16 [n_tok][d_prev] token-major, W bf16 [d_out][d_prev]."""
+    for t, n in ((Y, "Y"), (X, "X"), (W, "W")):
+        _bf16_rows(t, n)
+    n, dp = X.shape
+    do = W.shape[0]
+    if W.shape[1] != dp or tuple(Y.shape) != (n, do):
+        raise ValueError("shapes: X [n][d_prev], W [d_out][d_prev], Y [n][d_out]")
+    _check(load_library().gptq_linear_forward(_ptr(Y), Y.stride(0), _ptr(X), X.stride(0), _ptr(W), W.stride(0), n, dp,
+                                              do, _stream(stream)))
+
+
+def calibrate_chunk_tokens(d_in: int) -> int:
+    return int(load_library().gptq_calibrate_chunk_tokens(d_in))
+
+
+def calibrate_hessian(H, X, W, hdiag=None, ws=None, stream=None) -> None:
+    """H (fp32 [d_in,d_in], upper) += 2 Y^T Y with Y = bf16(X W^T) made chunk by chunk on the device:
+    X bf16 [n_tok][d_prev] (the previous layer's inputs), W bf16 [d_in][d_prev]."""
+    _need_cuda(H, hdiag)
+    _bf16_rows(X, "X")
+    _bf16_rows(W, "W")
+    n, dp = X.shape
+    di = W.shape[0]
+    if W.shape[1] != dp or tuple(H.shape) != (di, di):
+        raise ValueError("shapes: X [n][d_prev], W [d_in][d_prev], H [d_in][d_in]")
+    if ws is None:
+        ws = _workspace(workspace_bytes(OP_CALIBRATE, 0, di, n), X.device)
+    _check(load_library().gptq_calibrate_hessian(_ptr(H), _ptr(hdiag), _ptr(X), X.stride(0), _ptr(W), W.stride(0), n,
+                                                 dp, di, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def prepare_hinv(H, cfg: Config, U, perm=None, info=None, hdiag=None, ws=None, stream=None):

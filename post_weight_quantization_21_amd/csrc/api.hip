@@ -136,6 +136,9 @@ gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_
     case GPTQ_OP_HESSIAN_TOKENS:
         *out = gptq::hessian_ws_bytes(d_in, n_tok, GPTQ_DT_BF16);
         return GPTQ_OK;
+    case GPTQ_OP_CALIBRATE:
+        *out = gptq::calibrate_ws_bytes(d_in, n_tok);
+        return GPTQ_OK;
     case GPTQ_OP_SMOOTH:
         *out = gptq::smooth_ws_bytes(d_out, d_in);
         return GPTQ_OK;
@@ -190,6 +193,40 @@ gptq_status gptq_hessian_accumulate_tokens(float *H, double *hdiag, const void *
         return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
     return hip_status(gptq::run_hessian(H, hdiag, X, x_dtype, d_in, n_tok, ldx, true, ws, stream), fn);
 }
+
+gptq_status gptq_linear_forward(void *Y, int64_t ldy, const void *X, int64_t ldx, const void *W, int64_t ldw,
+                                int64_t n_tok, int64_t d_prev, int64_t d_out, hipStream_t stream) {
+    const char *fn = "gptq_linear_forward";
+    if (n_tok < 0 || d_out < 0 || d_prev <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    if (n_tok == 0 || d_out == 0) return GPTQ_OK;
+    if (!Y || !X || !W) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (ldx < d_prev || ldw < d_prev || ldy < d_out) return fail(GPTQ_ERR_INVALID_ARG, "%s: leading dimension too small", fn);
+    if (!aligned(X) || !aligned(W) || ldx % 8 != 0 || ldw % 8 != 0 || !aligned(Y, 2))
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: X and W must be 16-byte aligned with ldx, ldw multiples of 8", fn);
+    return hip_status(gptq::run_linear_forward(static_cast<uint16_t *>(Y), ldy, static_cast<const uint16_t *>(X), ldx,
+                                               static_cast<const uint16_t *>(W), ldw, n_tok, d_prev, d_out, stream),
+                      fn);
+}
+
+gptq_status gptq_calibrate_hessian(float *H, double *hdiag, const void *X, int64_t ldx, const void *W, int64_t ldw,
+                                   int64_t n_tok, int64_t d_prev, int64_t d_in, void *ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    const char *fn = "gptq_calibrate_hessian";
+    if (n_tok < 0 || d_in <= 0 || d_prev <= 0) return fail(GPTQ_ERR_INVALID_ARG, "%s: bad sizes", fn);
+    if (n_tok == 0) return GPTQ_OK;
+    if (!H || !X || !W) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (ldx < d_prev || ldw < d_prev) return fail(GPTQ_ERR_INVALID_ARG, "%s: leading dimension too small", fn);
+    if (!aligned(H) || (hdiag && !aligned(hdiag, 8)) || !aligned(X) || !aligned(W) || ldx % 8 != 0 || ldw % 8 != 0)
+        return fail(GPTQ_ERR_INVALID_ARG, "%s: X and W must be 16-byte aligned with ldx, ldw multiples of 8", fn);
+    const size_t need = gptq::calibrate_ws_bytes(d_in, n_tok);
+    if (!ws || ws_bytes < need || !aligned(ws))
+        return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    return hip_status(gptq::run_calibrate(H, hdiag, static_cast<const uint16_t *>(X), ldx,
+                                          static_cast<const uint16_t *>(W), ldw, n_tok, d_prev, d_in, ws, stream),
+                      fn);
+}
+
+int64_t gptq_calibrate_chunk_tokens(int64_t d_in) { return d_in > 0 ? gptq::calibrate_chunk_tokens(d_in) : 0; }
 
 gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in, const gptq_config *cfg, float *U,
                               int32_t *perm, int32_t *info_dev, void *ws, size_t ws_bytes, hipStream_t stream) {

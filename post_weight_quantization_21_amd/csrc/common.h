@@ -64,6 +64,14 @@ size_t hessian_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt);
 // token_major: X is [n_tok][ldx] (channels contiguous), else [d_in][ldx].
 hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, int64_t d_in, int64_t n_tok,
                        int64_t ldx, bool token_major, void *ws, hipStream_t s);
+// Y[t][o] = bf16(sum_i X[t][i] W[o][i]) on the bf16 matrix cores (hessian.hip).
+hipError_t run_linear_forward(uint16_t *Y, int64_t ldy, const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              int64_t n_tok, int64_t d_prev, int64_t d_out, hipStream_t s);
+// Forward of a layer in token chunks, each chunk's outputs accumulated into H.
+int64_t calibrate_chunk_tokens(int64_t d_in);
+size_t calibrate_ws_bytes(int64_t d_in, int64_t n_tok);
+hipError_t run_calibrate(float *H, double *hdiag, const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                         int64_t n_tok, int64_t d_prev, int64_t d_in, void *ws, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Prepare (prepare.hip)

@@ -211,26 +211,65 @@ struct Frags {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// grid.x = 8 * ceil(tiles / 8) * splits.  Each wave owns a 128 x 128 quarter
-// of the 256 x 256 tile as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators.
-// out_partial == nullptr: H += 2 acc (upper triangle); else the raw partial
-// tile goes to out_partial[split * ntiles + row-major tile index].
-template <bool TOK>
-__global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx, int64_t d,
-                                                             int64_t n_tok, int64_t kchunk, int nt, int64_t ntiles,
-                                                             int splits, float *__restrict__ H,
-                                                             float *__restrict__ out_partial) {
-    // XCD x owns band-order positions [g0, g1) and runs them split after split.
+// Operands of the matrix-core kernel below.
+//   SYRK (MODE 0 channel-major, 1 token-major): A = B = X with d channels and
+//     n_tok tokens; the upper tiles in band order, split over tokens.
+//   GEMM (MODE 2): C[m][n] = bf16(sum_k A[m][k] B[n][k]), A [M][lda] and
+//     B [N][ldb] both contiguous along k, C [M][ldc]; every tile, each XCD
+//     taking a contiguous range of the row-major tile order.
+struct MmaArgs {
+    const uint16_t *A, *B;
+    int64_t lda, ldb;
+    int64_t ma, mb;  // rows of A and B
+    int64_t K;       // the summed axis (tokens for the SYRK)
+    // SYRK plan and outputs
+    int64_t kchunk, ntiles;
+    int nt, splits;
+    float *H, *part;
+    // GEMM output
+    uint16_t *C;
+    int64_t ldc;
+};
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// grid.x = 8 * ceil(tiles / 8) * splits (GEMM: 8 * ceil(tiles / 8)).  Each wave
+// owns a 128 x 128 quarter of the 256 x 256 tile as 4 x 4
+// v_mfma_f32_32x32x16_bf16 accumulators.  SYRK: part == nullptr: H += 2 acc
+// (upper triangle); else the raw partial tile goes to
+// part[split * ntiles + row-major tile index].
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void mma_bf16_kernel(MmaArgs g) {
+    constexpr bool TOK = MODE == 1, GEMM = MODE == 2;
+    const uint16_t *__restrict__ X = g.A;
+    const int64_t ldx = g.lda, d = g.ma;
     const int64_t xcd = blockIdx.x % kXCDs, slot = blockIdx.x / kXCDs;
-    const int64_t g0 = xcd * ntiles / kXCDs, g1 = (xcd + 1) * ntiles / kXCDs, gsz = g1 - g0;
-    if (gsz <= 0 || slot >= gsz * splits) return;
-    const int64_t split = slot / gsz;
     int ti, tj;
-    tile_of_band(g0 + slot % gsz, nt, ti, tj);
-    const bool diag = ti == tj;
+    int64_t split = 0;
+    if constexpr (GEMM) {
+        const int gx = (int)ceil_div(g.mb, TS);
+        const int64_t tiles = (int64_t)gx * ceil_div(g.ma, TS);
+        const int64_t t0 = xcd * tiles / kXCDs, t1 = (xcd + 1) * tiles / kXCDs;
+        if (slot >= t1 - t0) return;
+        ti = (int)((t0 + slot) / gx);
+        tj = (int)((t0 + slot) % gx);
+    } else {
+        // XCD x owns band-order positions [g0, g1) and runs them split after split.
+        const int64_t g0 = xcd * g.ntiles / kXCDs, g1 = (xcd + 1) * g.ntiles / kXCDs, gsz = g1 - g0;
+        if (gsz <= 0 || slot >= gsz * g.splits) return;
+        split = slot / gsz;
+        tile_of_band(g0 + slot % gsz, g.nt, ti, tj);
+    }
+    const bool diag = !GEMM && ti == tj;
     const int64_t r0 = (int64_t)ti * TS, c0 = (int64_t)tj * TS;
-    const int64_t kbeg = split * kchunk;
-    const int64_t kend = (kbeg + kchunk) < n_tok ? (kbeg + kchunk) : n_tok;
+    const int64_t kbeg = GEMM ? 0 : split * g.kchunk;
+    const int64_t kend = GEMM ? g.K : ((kbeg + g.kchunk) < g.K ? (kbeg + g.kchunk) : g.K);
     const int nfull = kend > kbeg ? (int)((kend - kbeg) / KT) : 0;
     const bool has_tail = kend > kbeg + (int64_t)nfull * KT;
 
@@ -294,9 +333,9 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
             auto issue_piece = [&](int st, int slot_, int p) {
                 const int64_t k0 = kbeg + (int64_t)st * KT;
                 if (p < 4)
-                    panel_piece(sm.a[slot_], X, ldx, d, r0, k0, wave, lane, p);
+                    panel_piece(sm.a[slot_], g.A, g.lda, g.ma, r0, k0, wave, lane, p);
                 else
-                    panel_piece(sm.b[slot_], X, ldx, d, c0, k0, wave, lane, p - 4);
+                    panel_piece(sm.b[slot_], g.B, g.ldb, g.mb, c0, k0, wave, lane, p - 4);
             };
 #pragma unroll
             for (int st = 0; st < NS - 1; ++st)
@@ -404,8 +443,8 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
         const int64_t k0 = kbeg + (int64_t)nfull * KT;
         __syncthreads();  // every wave is done with the ring
         if constexpr (!TOK) {
-            panel_tail(sm.a[0], X, ldx, d, r0, k0, kend, tid);
-            panel_tail(sm.b[0], X, ldx, d, c0, k0, kend, tid);
+            panel_tail(sm.a[0], g.A, g.lda, g.ma, r0, k0, kend, tid);
+            panel_tail(sm.b[0], g.B, g.ldb, g.mb, c0, k0, kend, tid);
         } else {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -431,8 +470,22 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
         }
     }
 
-    if (out_partial) {
-        float *dst = out_partial + (split * ntiles + tile_linear(ti, tj, nt)) * (TS * TS);
+    if constexpr (GEMM) {
+        // bf16 C, one 32 x 32 sub-tile at a time (32 lanes write 64 contiguous bytes)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = r0 + wm * 128 + i * 32 + mfma32_row(r, lane);
+                    const int64_t n = c0 + wn * 128 + j * 32 + mfma32_col(lane);
+                    if (m < g.ma && n < g.mb) g.C[m * g.ldc + n] = bf16_rne(acc[i][j][r]);
+                }
+        return;
+    }
+    if (g.part) {
+        float *dst = g.part + (split * g.ntiles + tile_linear(ti, tj, g.nt)) * (TS * TS);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -447,6 +500,7 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(const uint16_t *__r
     }
     if (idle) return;
     // H += 2 acc, one 32 x 32 sub-tile at a time: its reads before its writes.
+    float *H = g.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -666,6 +720,57 @@ size_t diag_part_bytes(int64_t d, int64_t n_tok, gptq_dtype dt) {
 
 }  // namespace
 
+hipError_t run_linear_forward(uint16_t *Y, int64_t ldy, const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              int64_t n_tok, int64_t d_prev, int64_t d_out, hipStream_t s) {
+    if (n_tok <= 0 || d_out <= 0) return hipSuccess;
+    MmaArgs a{};
+    a.A = X;
+    a.lda = ldx;
+    a.ma = n_tok;
+    a.B = W;
+    a.ldb = ldw;
+    a.mb = d_out;
+    a.K = d_prev;
+    a.C = Y;
+    a.ldc = ldy;
+    const int64_t tiles = ceil_div(n_tok, TS) * ceil_div(d_out, TS);
+    hipLaunchKernelGGL(mma_bf16_kernel<2>, dim3((unsigned)(kXCDs * ceil_div(tiles, kXCDs))), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// Tokens per chunk of the calibration pass: the chunk of layer inputs is about
+// 128 MiB (it stays in the last-level cache between its write and the SYRK's
+// reads), a multiple of 1024 tokens in [1024, 65536].
+int64_t calibrate_chunk_tokens(int64_t d_in) {
+    const int64_t ldy = (d_in + 3) / 4 * 4;
+    int64_t c = ((int64_t)128 << 20) / (2 * ldy) / 1024 * 1024;
+    return c < 1024 ? 1024 : (c > 65536 ? 65536 : c);
+}
+
+size_t calibrate_ws_bytes(int64_t d_in, int64_t n_tok) {
+    if (n_tok <= 0) return 0;
+    const int64_t chunk = std::min<int64_t>(calibrate_chunk_tokens(d_in), n_tok);
+    const int64_t ldy = (d_in + 3) / 4 * 4;
+    size_t h = hessian_ws_bytes(d_in, chunk, GPTQ_DT_BF16);
+    if (n_tok % chunk) h = std::max(h, hessian_ws_bytes(d_in, n_tok % chunk, GPTQ_DT_BF16));
+    return align_up((size_t)chunk * (size_t)ldy * 2, 256) + h;
+}
+
+hipError_t run_calibrate(float *H, double *hdiag, const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                         int64_t n_tok, int64_t d_prev, int64_t d_in, void *ws, hipStream_t s) {
+    const int64_t chunk = std::min<int64_t>(calibrate_chunk_tokens(d_in), n_tok);
+    const int64_t ldy = (d_in + 3) / 4 * 4;
+    uint16_t *Y = static_cast<uint16_t *>(ws);
+    void *hws = static_cast<char *>(ws) + align_up((size_t)chunk * (size_t)ldy * 2, 256);
+    for (int64_t t0 = 0; t0 < n_tok; t0 += chunk) {
+        const int64_t c = std::min<int64_t>(chunk, n_tok - t0);
+        hipError_t e = run_linear_forward(Y, ldy, X + t0 * ldx, ldx, W, ldw, c, d_prev, d_in, s);
+        if (e != hipSuccess) return e;
+        if ((e = run_hessian(H, hdiag, Y, GPTQ_DT_BF16, d_in, c, ldy, true, hws, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // The same for both layouts: the SYRK's partial tiles, then the token-major
 // diagonal pass's partial sums.
 size_t hessian_ws_bytes(int64_t d_in, int64_t n_tok, gptq_dtype dt) {
@@ -684,13 +789,21 @@ hipError_t run_hessian(float *H, double *hdiag, const void *X, gptq_dtype dt, in
         syrk_bytes = syrk_part_bytes(p);
         float *part = p.splits > 1 ? static_cast<float *>(ws) : nullptr;
         const dim3 grid((unsigned)(kXCDs * ceil_div(p.ntiles, kXCDs) * p.splits));
-        const uint16_t *Xb = static_cast<const uint16_t *>(X);
+        MmaArgs a{};
+        a.A = a.B = static_cast<const uint16_t *>(X);
+        a.lda = a.ldb = ldx;
+        a.ma = a.mb = d;
+        a.K = n_tok;
+        a.kchunk = p.kchunk;
+        a.ntiles = p.ntiles;
+        a.nt = p.nt;
+        a.splits = p.splits;
+        a.H = H;
+        a.part = part;
         if (token_major)
-            hipLaunchKernelGGL(syrk_bf16_kernel<true>, grid, dim3(kThreads), 0, s, Xb, ldx, d, n_tok, p.kchunk, p.nt,
-                               p.ntiles, p.splits, H, part);
+            hipLaunchKernelGGL(mma_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a);
         else
-            hipLaunchKernelGGL(syrk_bf16_kernel<false>, grid, dim3(kThreads), 0, s, Xb, ldx, d, n_tok, p.kchunk, p.nt,
-                               p.ntiles, p.splits, H, part);
+            hipLaunchKernelGGL(mma_bf16_kernel<0>, grid, dim3(kThreads), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (part) {
             hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)(p.ntiles * (TS * TS / (kThreads * 4)))), dim3(kThreads),

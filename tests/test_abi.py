@@ -115,3 +115,15 @@ def test_argument_errors_are_synchronous():
     assert lib.gptq_hessian_accumulate(p, None, p, gq.DT_BF16, 64, 0, 64, None, 0, None) == gq.OK  # no-op
     assert lib.gptq_layer_loss(p, p, p, p, None, p, 64, 128, 48, p, p, 1 << 30, None) == gq.ERR_INVALID_ARG
     assert lib.gptq_rtn_quantize(None, 4, 128, ctypes.byref(cfg), p, p, p, None) == gq.ERR_INVALID_ARG
+    # calibration forward: 16-byte rows, leading dimensions, workspace
+    assert lib.gptq_linear_forward(p, 64, p, 60, p, 64, 8, 60, 64, None) == gq.ERR_INVALID_ARG  # ldx % 8
+    assert lib.gptq_linear_forward(p, 64, ctypes.c_void_p(0x10008), 64, p, 64, 8, 64, 64, None) == gq.ERR_INVALID_ARG
+    assert lib.gptq_linear_forward(p, 32, p, 64, p, 64, 8, 64, 64, None) == gq.ERR_INVALID_ARG  # ldy < d_out
+    assert lib.gptq_linear_forward(None, 64, None, 64, None, 64, 0, 64, 64, None) == gq.OK  # no tokens
+    need = gq.workspace_bytes(gq.OP_CALIBRATE, 0, 256, 5000)
+    assert need >= 5000 * 256 * 2
+    assert lib.gptq_calibrate_hessian(p, None, p, 64, p, 64, 5000, 64, 256, p, need - 1, None) == gq.ERR_WORKSPACE
+    assert lib.gptq_calibrate_hessian(p, None, p, 60, p, 64, 5000, 60, 256, p, need, None) == gq.ERR_INVALID_ARG
+    assert lib.gptq_calibrate_chunk_tokens(4096) == 16384
+    assert lib.gptq_calibrate_chunk_tokens(8192) == 8192
+    assert lib.gptq_calibrate_chunk_tokens(1 << 20) == 1024 and lib.gptq_calibrate_chunk_tokens(16) == 65536
