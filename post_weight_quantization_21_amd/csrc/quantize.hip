@@ -378,6 +378,9 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     return l;
 }
 
+// Rows from which the superblock's inner updates are left-looking.
+constexpr int64_t kLeftLookRows = 16384;
+
 // W[:, c1:c1+n] += (-E) U[k0:k0+k, c1:c1+n] with -E^T stored as Et [k][ldet].
 hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, int64_t ldet, const float *U, int64_t k0,
                        int64_t k, int64_t c1, int64_t n, hipStream_t s) {
@@ -475,10 +478,16 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     const int vec = (d_in % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) && ((reinterpret_cast<uintptr_t>(cdst) & 15) == 0);
     const int64_t sc = lay.sc;
     const bool deferred = sc < d_in;  // superblocks leave an update for the columns beyond them
+    // Inside a superblock, tall layers bring each batch up to date just before
+    // it (one product over the superblock's earlier batches, K = their
+    // columns); short ones, whose single batch column of tiles would leave most
+    // of the chip idle, update the rest of the superblock after each batch.
+    const bool left = deferred && d_out >= kLeftLookRows;
     for (int64_t s0 = 0; s0 < d_in; s0 += sc) {
         const int64_t s1 = std::min<int64_t>(s0 + sc, d_in);
         for (int64_t c0 = s0; c0 < s1; c0 += B) {
             const int nc = (int)std::min<int64_t>(B, s1 - c0);
+            if (left && (e = lazy_update(W, d_out, d_in, Et, ldet, U, s0, c0 - s0, c0, nc, s)) != hipSuccess) return e;
             if (!fixed && gt == 0 && c0 % g == 0) {
                 const int64_t waves = d_out;
                 hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W,
@@ -522,7 +531,7 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
             if (e != hipSuccess) return e;
             // the rest of the superblock
             const int64_t c1 = c0 + nc;
-            if ((e = lazy_update(W, d_out, d_in, Eb, ldet, U, c0, nc, c1, s1 - c1, s)) != hipSuccess) return e;
+            if (!left && (e = lazy_update(W, d_out, d_in, Eb, ldet, U, c0, nc, c1, s1 - c1, s)) != hipSuccess) return e;
         }
         // every column beyond the superblock, with the superblock's whole E
         if (deferred && (e = lazy_update(W, d_out, d_in, Et, ldet, U, s0, s1 - s0, s1, d_in - s1, s)) != hipSuccess)
