@@ -719,18 +719,64 @@ hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int6
     return hipSuccess;
 }
 
+// The upper-right block X = U[0:h, h:h+w] of a node [0, 2h) (left half
+// L = [0, h), right half R = [h, h+w)) solves T_LL X = -T_LR U_RR = -Tw.  Its
+// left half's inverse U_LL is complete only when the factorization ends, so
+// instead of X = -U_LL Tw at the end, X is found by back substitution in row
+// blocks of kRegion from the bottom, one block per region the factorization
+// passes: X_J = -U_JJ Tw_J for the block J = [x, x + kRegion) (its diagonal
+// inverse is the region's), then Tw_I += T_IJ X_J for the rows I = [0, x)
+// above it, so the end is left with the first block only.
+hipError_t solve_left_block(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, int64_t h,
+                            int64_t w, hipStream_t st) {
+    const int64_t r = std::min<int64_t>(kRegion, h - x);
+    GemmDesc a;  // U[x:x+r, h:h+w] = -U[x:x+r, x:x+r] Tw[x:x+r, h:h+w]
+    a.M = r;
+    a.N = w;
+    a.K = r;
+    a.A = U + x * d + x;
+    a.lda = d;
+    a.a_upper = 1;
+    a.B = Tw + x * lda + h;
+    a.ldb = lda;
+    a.C = U + x * d + h;
+    a.ldc = d;
+    a.alpha = -1.0f;
+    a.beta = 0.0f;
+    hipError_t e = launch_gemm_f32(a, st);
+    if (e != hipSuccess || x == 0) return e;
+    GemmDesc b;  // Tw[0:x, h:h+w] += T[0:x, x:x+r] U[x:x+r, h:h+w]
+    b.M = x;
+    b.N = w;
+    b.K = r;
+    b.A = Tf + x;
+    b.lda = lda;
+    b.B = U + x * d + h;
+    b.ldb = d;
+    b.C = Tw + h;
+    b.ldc = lda;
+    b.alpha = 1.0f;
+    b.beta = 1.0f;
+    return launch_gemm_f32(b, st);
+}
+
+// Nodes [0, 2h) whose upper-right block is solved region by region (the
+// others, with h = kRegion, are one product at the end).
+inline bool solved_by_rows(int64_t h) { return h >= 2 * kRegion; }
+
 // The inverse's work that becomes ready once the factorization has passed
 // column x (a multiple of kRegion; x = 0 at the end): the region at x, then,
 // for the nodes of 2, 4, ... regions, the left product of the node starting
 // at x while x is aligned to it, and the right product of the node whose
-// middle is x (its right half, starting at x, is complete by then).
+// middle is x (its right half, starting at x, is complete by then); then the
+// row block at x of every node [0, 2h) with h > x.
 hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st) {
     hipError_t e = assemble_region(Tf, U, Tw, d, lda, x, st);
     if (e != hipSuccess) return e;
     for (int64_t n = 2 * kRegion; n / 2 < d; n *= 2) {
         const int64_t half = n / 2;
         if (x % n == 0) {
-            if (x + half < d)
+            if (x + half < d && !(x == 0 && solved_by_rows(half)))
                 if ((e = merge_left(U, Tw, d, lda, x, half, std::min<int64_t>(half, d - x - half), 1, 0, st)) != hipSuccess)
                     return e;
         } else if (x % n == half) {
@@ -742,6 +788,9 @@ hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
             break;
         }
     }
+    for (int64_t h = 2 * kRegion; h < d; h *= 2)
+        if (solved_by_rows(h) && x < h)
+            if ((e = solve_left_block(Tf, U, Tw, d, lda, x, h, std::min<int64_t>(h, d - h), st)) != hipSuccess) return e;
     return hipSuccess;
 }
 
