@@ -444,8 +444,8 @@ def main() -> int:
     lazy_tf = lazy_flops / (lazy_ms * 1e-3) / 1e12 if lazy_ms > 0 else 0.0
     roof_syrk = {"bound": "mfma", "achieved": round(syrk_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(syrk_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload, "hessian"),
-                 "kernel": "hessian_accumulate (syrk_bf16_kernel + split-K reduce" +
-                           (" + fp64 diagonal)" if lay["act_order"] else ")"),
+                 "kernel": "hessian_accumulate (mma_bf16_kernel<0>: the SYRK, + syrk_reduce_kernel" +
+                           (" + diag_rows_kernel)" if lay["act_order"] else ")"),
                  "flops_per_launch": syrk_flops, "ms_per_launch": round(t_h, 3)}
     roof_lazy = {"bound": "mfma", "achieved": round(lazy_tf, 1), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(lazy_tf / PEAK_F32_TFLOPS, 4), "traffic": measured_traffic(args.workload, "lazy"),
