@@ -393,18 +393,23 @@ GPTQ_API gptq_status gptq_w4a16_gemm(const void *X, gptq_dtype x_dtype, int64_t 
  * Kernel timing for benchmarks (off by default).  While enabled, the column
  * pass records a pair of HIP events around each of its kernel launches of the
  * kinds below, on the stream the kernel runs on:
- *   GPTQ_TIMED_LAZY   the trailing-update products of the lazy batches (fp32
- *                     matrix cores);
- *   GPTQ_TIMED_BATCH  the batch kernels of the column pass.
- * gptq_timing_read(op, ms, count) waits for the recorded events of that kind,
- * returns their summed elapsed milliseconds and how many launches they cover
- * (host pointers), and forgets them.  Launches that run beside each other on
- * different streams are timed each on its own.  Process-wide; recording adds
- * two event records per launch.
+ *   GPTQ_TIMED_LAZY        the trailing-update products of the lazy batches
+ *                          that run on the fp32 matrix cores;
+ *   GPTQ_TIMED_BATCH       the batch kernels of the column pass;
+ *   GPTQ_TIMED_LAZY_SPLIT  the trailing-update products that run on the bf16
+ *                          matrix cores through the exact three-term split of
+ *                          their fp32 operands (six bf16 products per fp32 one).
+ * gptq_timing_read(op, ms, count, flops) waits for the recorded events of that
+ * kind, returns their summed elapsed milliseconds, how many launches they
+ * cover and, if `flops` is not NULL, the floating-point operations those
+ * launches perform as fp32 arithmetic (2 M N K per product; 0 for the batch
+ * kernels), all through host pointers, and forgets them.  Launches that run
+ * beside each other on different streams are timed each on its own.
+ * Process-wide; recording adds two event records per launch.
  */
-typedef enum { GPTQ_TIMED_LAZY = 0, GPTQ_TIMED_BATCH = 1 } gptq_timed_op;
+typedef enum { GPTQ_TIMED_LAZY = 0, GPTQ_TIMED_BATCH = 1, GPTQ_TIMED_LAZY_SPLIT = 2 } gptq_timed_op;
 GPTQ_API gptq_status gptq_timing_enable(int32_t on);
-GPTQ_API gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count);
+GPTQ_API gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count, double *flops);
 
 /* Scratch bytes needed by `op` for these sizes (cfg may be NULL for
  * GPTQ_OP_HESSIAN and GPTQ_OP_LOSS).  `out` is a host pointer. */

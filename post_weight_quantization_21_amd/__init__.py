@@ -30,7 +30,7 @@ EXPORTED = (
     "gptq_quantize_layer_noalloc", "gptq_timing_enable", "gptq_timing_read",
     "gptq_linear_forward", "gptq_calibrate_hessian", "gptq_calibrate_chunk_tokens",
 )
-TIMED_LAZY, TIMED_BATCH = 0, 1
+TIMED_LAZY, TIMED_BATCH, TIMED_LAZY_SPLIT = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GPTQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -89,7 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_calibrate_hessian": [vp, vp, vp, i64, vp, i64, i64, i64, i64, vp, sz, vp],
         "gptq_calibrate_chunk_tokens": [i64],
         "gptq_timing_enable": [i32],
-        "gptq_timing_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
+        "gptq_timing_read": [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)],
         "gptq_status_string": [ctypes.c_int],
         "gptq_last_error": [],
     }
@@ -129,11 +129,11 @@ def timing_enable(on: bool = True) -> None:
     _check(load_library().gptq_timing_enable(int(bool(on))))
 
 
-def timing_read(op: int):
-    """(summed milliseconds, launches) of the recorded kernels of one kind, then forget them."""
-    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
-    _check(load_library().gptq_timing_read(int(op), ctypes.byref(ms), ctypes.byref(n)))
-    return ms.value, n.value
+def timing_read(op: int, with_flops: bool = False):
+    """(summed milliseconds, launches[, fp32 flops]) of the recorded kernels of one kind, then forget them."""
+    ms, n, fl = ctypes.c_double(0.0), ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(load_library().gptq_timing_read(int(op), ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl)))
+    return (ms.value, n.value, fl.value) if with_flops else (ms.value, n.value)
 
 
 def workspace_bytes(op: int, d_out: int, d_in: int, n_tok: int = 0, cfg: Config | None = None) -> int:

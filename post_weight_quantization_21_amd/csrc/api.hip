@@ -106,11 +106,14 @@ gptq_status gptq_timing_enable(int32_t on) {
     return GPTQ_OK;
 }
 
-gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count) {
+gptq_status gptq_timing_read(int32_t op, double *ms, int64_t *count, double *flops) {
     const char *fn = "gptq_timing_read";
     if (op < 0 || op >= gptq::kTimedOps) return fail(GPTQ_ERR_INVALID_ARG, "%s: unknown op %d", fn, op);
     if (!ms || !count) return fail(GPTQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    return hip_status(gptq::timing_read(static_cast<gptq::TimedOp>(op), ms, count), fn);
+    double w = 0.0;
+    const hipError_t e = gptq::timing_read(static_cast<gptq::TimedOp>(op), ms, count, &w);
+    if (flops) *flops = w;
+    return hip_status(e, fn);
 }
 
 gptq_status gptq_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t n_tok, const gptq_config *cfg, size_t *out) {

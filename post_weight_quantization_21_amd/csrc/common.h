@@ -55,6 +55,12 @@ struct GemmDesc {
 constexpr int kGemmTile = 128;
 int64_t gemm_num_tiles(const GemmDesc &g);
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s);
+// The same product on the bf16 matrix cores through an exact three-term split
+// of each fp32 operand (gemm_split.hip): no triangles, no batch, K a multiple
+// of 32, 16-byte aligned operands, lda and ldb multiples of 4, and M (N) a
+// multiple of 4 when A (B) is stored K-major.
+bool gemm_split_supported(const GemmDesc &g);
+hipError_t launch_gemm_split(const GemmDesc &g, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Hessian (hessian.hip)
@@ -142,12 +148,13 @@ hipError_t side_stream(SidePurpose purpose, SideStream *&out);
 hipError_t signal_wait(hipEvent_t ev, hipStream_t from, hipStream_t to);
 
 // Optional event timing of kernel groups (gptq_timing_enable / gptq_timing_read).
-enum TimedOp { kTimedLazy = 0, kTimedBatch = 1, kTimedOps = 2 };
+enum TimedOp { kTimedLazy = 0, kTimedBatch = 1, kTimedLazySplit = 2, kTimedOps = 3 };
 void timing_set(bool on);
-hipError_t timing_read(TimedOp op, double *ms, int64_t *count);
+// Summed milliseconds, launches and work (the `work` of each scope, e.g. flops).
+hipError_t timing_read(TimedOp op, double *ms, int64_t *count, double *work);
 class TimedScope {
   public:
-    TimedScope(TimedOp op, hipStream_t s);
+    TimedScope(TimedOp op, hipStream_t s, double work = 0.0);
     ~TimedScope();
     TimedScope(const TimedScope &) = delete;
     TimedScope &operator=(const TimedScope &) = delete;
@@ -155,6 +162,7 @@ class TimedScope {
   private:
     TimedOp op_;
     hipStream_t s_;
+    double work_;
     hipEvent_t start_ = nullptr, stop_ = nullptr;
 };
 

@@ -378,6 +378,9 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, const gptq_config &c) {
     return l;
 }
 
+// K from which a trailing update runs through the split-bf16 GEMM.
+constexpr int64_t kSplitMinK = 512;
+
 // Rows from which the superblock's inner updates are left-looking.
 constexpr int64_t kLeftLookRows = 16384;
 
@@ -385,7 +388,6 @@ constexpr int64_t kLeftLookRows = 16384;
 hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, int64_t ldet, const float *U, int64_t k0,
                        int64_t k, int64_t c1, int64_t n, hipStream_t s) {
     if (n <= 0 || k <= 0) return hipSuccess;
-    TimedScope ts(kTimedLazy, s);
     GemmDesc g;
     g.M = d_out;
     g.N = n;
@@ -399,7 +401,13 @@ hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, i
     g.ldc = d_in;
     g.alpha = 1.0f;
     g.beta = 1.0f;
-    return launch_gemm_f32(g, s);
+    // Long, wide updates (the superblocks') on the bf16 matrix cores through
+    // the exact three-term split, whose 256 x 256 tiles need N >= 512 and
+    // enough of them to fill the chip; the in-superblock ones on fp32 ones.
+    const int64_t split_tiles = ceil_div(d_out, 256) * ceil_div(n, 256);
+    const bool split = k >= kSplitMinK && n >= 512 && split_tiles >= 64 && gemm_split_supported(g);
+    TimedScope ts(split ? kTimedLazySplit : kTimedLazy, s, 2.0 * (double)d_out * (double)n * (double)k);
+    return split ? launch_gemm_split(g, s) : launch_gemm_f32(g, s);
 }
 
 }  // namespace

@@ -44,7 +44,11 @@ struct TimingState {
     std::mutex mu;
     bool on = false;
     std::vector<hipEvent_t> pool;
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[kTimedOps];
+    struct Rec {
+        hipEvent_t start, stop;
+        double work;
+    };
+    std::vector<Rec> pending[kTimedOps];
 };
 TimingState &timing() {
     static TimingState t;
@@ -67,7 +71,7 @@ void timing_set(bool on) {
     t.on = on;
 }
 
-TimedScope::TimedScope(TimedOp op, hipStream_t s) : op_(op), s_(s) {
+TimedScope::TimedScope(TimedOp op, hipStream_t s, double work) : op_(op), s_(s), work_(work) {
     TimingState &t = timing();
     std::lock_guard<std::mutex> lock(t.mu);
     if (!t.on) return;
@@ -84,28 +88,30 @@ TimedScope::~TimedScope() {
     TimingState &t = timing();
     std::lock_guard<std::mutex> lock(t.mu);
     if (hipEventRecord(stop_, s_) == hipSuccess) {
-        t.pending[op_].emplace_back(start_, stop_);
+        t.pending[op_].push_back({start_, stop_, work_});
     } else {
         t.pool.push_back(start_);
         t.pool.push_back(stop_);
     }
 }
 
-hipError_t timing_read(TimedOp op, double *ms, int64_t *count) {
+hipError_t timing_read(TimedOp op, double *ms, int64_t *count, double *work) {
     TimingState &t = timing();
     std::lock_guard<std::mutex> lock(t.mu);
-    double sum = 0.0;
+    double sum = 0.0, w = 0.0;
     hipError_t err = hipSuccess;
-    for (auto &pr : t.pending[op]) {
+    for (auto &r : t.pending[op]) {
         float el = 0.0f;
-        hipError_t e = hipEventSynchronize(pr.second);
-        if (e == hipSuccess) e = hipEventElapsedTime(&el, pr.first, pr.second);
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&el, r.start, r.stop);
         if (e != hipSuccess && err == hipSuccess) err = e;
         sum += el;
-        t.pool.push_back(pr.first);
-        t.pool.push_back(pr.second);
+        w += r.work;
+        t.pool.push_back(r.start);
+        t.pool.push_back(r.stop);
     }
     *ms = sum;
+    *work = w;
     *count = (int64_t)t.pending[op].size();
     t.pending[op].clear();
     return err;
