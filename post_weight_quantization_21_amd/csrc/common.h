@@ -43,6 +43,7 @@ struct GemmDesc {
     int a_upper = 0;     // A upper triangular: A[m][k] == 0 for k < m (K range trimmed)
     int b_upper = 0;     // B upper triangular: B[k][n] == 0 for k > n (K range trimmed)
     int batch = 1;       // blockIdx.z; operands advance by the strides below
+    int max_wgs = 0;     // > 0: at most this many workgroups, each looping over tiles (leaves CUs to other streams)
     int64_t strideA = 0, strideB = 0, strideC = 0;
     // EPI_DOT: instead of storing, partial[tile] = sum over the tile of
     // (op(A) op(B))[m][n] * Dm[m*ldd+n] in fp64 (one double per workgroup).

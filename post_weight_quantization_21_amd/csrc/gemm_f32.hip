@@ -10,6 +10,8 @@
 // 32, double buffered through registers, one barrier per slab.  Operands are
 // stored K-major in LDS so both matrix-core operands are read as consecutive
 // 4-byte words; each k-step's operands are read one step ahead of its MFMAs.
+#include <algorithm>
+
 #include "common.h"
 
 namespace gptq {
@@ -102,21 +104,12 @@ struct SlabLoader {
     }
 };
 
+// One T x T tile of C (tile row tm, column tn, batch bz); `pidx` indexes the
+// partial sum of EPI_DOT.
 template <int EPI, int VA, int VB, int T>
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
+__device__ __forceinline__ void gemm_f32_tile(const GemmDesc &g, int tm, int tn, int bz, int64_t pidx) {
     constexpr int QB = T / 64;  // 32x32 MFMA blocks per wave along each dimension
     constexpr int HW = T / 2;   // wave tile edge
-    // With B upper triangular the tiles of the last columns have the longest K:
-    // they are dispatched first, column by column over every row of tiles, so
-    // the launch does not end on long tiles (with A upper, the first rows are
-    // the longest, and they already come first).
-    int tm = blockIdx.y, tn = blockIdx.x;
-    if (g.b_upper) {
-        const int id = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;  // dispatch order
-        tn = (int)gridDim.x - 1 - id / (int)gridDim.y;
-        tm = id % (int)gridDim.y;
-    }
-    const int bz = blockIdx.z;
     if (g.upper_only && tm > tn) return;  // strictly below the diagonal: nothing to store
     const int64_t m0 = (int64_t)tm * T, n0 = (int64_t)tn * T;
 
@@ -243,8 +236,45 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
         if (tid == 0) {
             double t = 0.0;
             for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
-            g.partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+            g.partial[pidx] = t;
         }
+    }
+}
+
+// Tile order of a launch: row-major over the tiles; with B upper triangular the
+// tiles of the last columns have the longest K, so they are dispatched first,
+// column by column over every row of tiles, and the launch does not end on long
+// tiles (with A upper, the first rows are the longest, and they already come first).
+__device__ __forceinline__ void tile_of(const GemmDesc &g, int64_t id, int gx, int gy, int &tm, int &tn, int &bz) {
+    const int64_t per = (int64_t)gx * gy;
+    bz = (int)(id / per);
+    const int r = (int)(id - (int64_t)bz * per);
+    if (g.b_upper) {
+        tn = gx - 1 - r / gy;
+        tm = r % gy;
+    } else {
+        tm = r / gx;
+        tn = r % gx;
+    }
+}
+
+// One tile per workgroup (grid gx x gy x batch), or with max_wgs a persistent
+// grid of max_wgs workgroups that takes the tiles in the same order.
+template <int EPI, int VA, int VB, int T>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmDesc g) {
+    const int gx = (int)ceil_div(g.N, T), gy = (int)ceil_div(g.M, T);
+    int tm, tn, bz;
+    if (g.max_wgs <= 0) {
+        const int64_t id = (int64_t)blockIdx.z * gx * gy + (int64_t)blockIdx.y * gx + blockIdx.x;
+        tile_of(g, id, gx, gy, tm, tn, bz);
+        gemm_f32_tile<EPI, VA, VB, T>(g, tm, tn, bz, (int64_t)blockIdx.y * gridDim.x + blockIdx.x);
+        return;
+    }
+    const int64_t total = (int64_t)gx * gy * g.batch;
+    for (int64_t id = blockIdx.x; id < total; id += gridDim.x) {
+        if (id != blockIdx.x) __syncthreads();  // the previous tile's LDS reads are done
+        tile_of(g, id, gx, gy, tm, tn, bz);
+        gemm_f32_tile<EPI, VA, VB, T>(g, tm, tn, bz, id);
     }
 }
 
@@ -327,15 +357,8 @@ __device__ __forceinline__ void lds_bar() {
 }
 
 template <int EPI, int AKM, int BKM>
-__global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
+__device__ __forceinline__ void gemm_f32_lds_tile(const GemmDesc &g, int tm, int tn, int bz, int64_t pidx) {
     constexpr int QB = 2, HW = 64;
-    int tm = blockIdx.y, tn = blockIdx.x;
-    if (g.b_upper) {
-        const int id = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;
-        tn = (int)gridDim.x - 1 - id / (int)gridDim.y;
-        tm = id % (int)gridDim.y;
-    }
-    const int bz = blockIdx.z;
     if (g.upper_only && tm > tn) return;
     const int64_t m0 = (int64_t)tm * LT, n0 = (int64_t)tn * LT;
     const float *A = g.A + bz * g.strideA;
@@ -451,14 +474,40 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
         if (tid == 0) {
             double t = 0.0;
             for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
-            g.partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+            g.partial[pidx] = t;
         }
     }
 }
 
+template <int EPI, int AKM, int BKM>
+__global__ __launch_bounds__(kThreads) void gemm_f32_lds_kernel(GemmDesc g) {
+    const int gx = (int)ceil_div(g.N, LT), gy = (int)ceil_div(g.M, LT);
+    int tm, tn, bz;
+    if (g.max_wgs <= 0) {
+        const int64_t id = (int64_t)blockIdx.z * gx * gy + (int64_t)blockIdx.y * gx + blockIdx.x;
+        tile_of(g, id, gx, gy, tm, tn, bz);
+        gemm_f32_lds_tile<EPI, AKM, BKM>(g, tm, tn, bz, (int64_t)blockIdx.y * gridDim.x + blockIdx.x);
+        return;
+    }
+    const int64_t total = (int64_t)gx * gy * g.batch;
+    for (int64_t id = blockIdx.x; id < total; id += gridDim.x) {
+        if (id != blockIdx.x) __syncthreads();  // the previous tile's LDS reads are done
+        tile_of(g, id, gx, gy, tm, tn, bz);
+        gemm_f32_lds_tile<EPI, AKM, BKM>(g, tm, tn, bz, id);
+    }
+}
+
+// One workgroup per tile, or a persistent grid of max_wgs workgroups.
+template <int T>
+dim3 launch_grid(const GemmDesc &g) {
+    const int64_t gx = ceil_div(g.N, T), gy = ceil_div(g.M, T);
+    if (g.max_wgs > 0) return dim3((unsigned)std::min<int64_t>(gx * gy * g.batch, g.max_wgs));
+    return dim3((unsigned)gx, (unsigned)gy, (unsigned)g.batch);
+}
+
 template <int EPI>
 void launch_lds(const GemmDesc &g, hipStream_t s) {
-    dim3 grid((unsigned)ceil_div(g.N, LT), (unsigned)ceil_div(g.M, LT), (unsigned)g.batch);
+    const dim3 grid = launch_grid<LT>(g);
     const int akm = g.a_trans ? 1 : 0, bkm = g.b_trans ? 0 : 1;
     if (akm && bkm)
         hipLaunchKernelGGL((gemm_f32_lds_kernel<EPI, 1, 1>), grid, dim3(kThreads), 0, s, g);
@@ -474,7 +523,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 template <int EPI, int T>
 void launch_tile(const GemmDesc &g, int va, int vb, hipStream_t s) {
-    dim3 grid((unsigned)ceil_div(g.N, T), (unsigned)ceil_div(g.M, T), (unsigned)g.batch);
+    const dim3 grid = launch_grid<T>(g);
     if (va && vb)
         hipLaunchKernelGGL((gemm_f32_kernel<EPI, 1, 1, T>), grid, dim3(kThreads), 0, s, g);
     else if (va)
@@ -492,8 +541,10 @@ constexpr int kCUs = 256;
 // The loss reduction indexes its partial sums by 128-wide tiles: EPI_DOT always uses them.
 int64_t gemm_num_tiles(const GemmDesc &g) { return ceil_div(g.M, kGemmTile) * ceil_div(g.N, kGemmTile); }
 
-hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s) {
-    if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+hipError_t launch_gemm_f32(const GemmDesc &gd, hipStream_t s) {
+    if (gd.M <= 0 || gd.N <= 0 || gd.batch <= 0) return hipSuccess;
+    GemmDesc g = gd;
+    if (g.epilogue == EPI_DOT) g.max_wgs = 0;  // its partial sums are indexed by workgroup
     const bool bz = g.batch > 1;
     // 16-byte chunks wholly inside or outside: aligned base and stride, and
     // the contiguous extent (the tile-wide dim, or K) a multiple of 4.

@@ -650,9 +650,10 @@ __global__ __launch_bounds__(kFThreads) void p_kernel(const float *__restrict__ 
 // so the first can run as soon as the factorization has passed j0.  Batched
 // over `npairs` nodes of one level (`stride` apart along the diagonal).
 hipError_t merge_right(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t i0, int64_t ni, int64_t nj,
-                       int64_t npairs, int64_t stride, hipStream_t st) {
+                       int64_t npairs, int64_t stride, hipStream_t st, int wgs) {
     const int64_t j0 = i0 + ni;
     GemmDesc g;
+    g.max_wgs = wgs;
     g.batch = (int)npairs;
     g.M = ni;
     g.N = nj;
@@ -670,9 +671,10 @@ hipError_t merge_right(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
 }
 
 hipError_t merge_left(float *U, const float *Tw, int64_t d, int64_t lda, int64_t i0, int64_t ni, int64_t nj,
-                      int64_t npairs, int64_t stride, hipStream_t st) {
+                      int64_t npairs, int64_t stride, hipStream_t st, int wgs) {
     const int64_t j0 = i0 + ni;
     GemmDesc h;
+    h.max_wgs = wgs;
     h.batch = (int)npairs;
     h.M = ni;
     h.N = nj;
@@ -696,9 +698,15 @@ hipError_t merge_left(float *U, const float *Tw, int64_t d, int64_t lda, int64_t
 // second stream, beside the rest of the factorization.
 constexpr int64_t kRegion = 512;
 
+// Workgroups of each product launched on a side stream while the
+// factorization's chain runs on the caller's stream (0: one per tile): fewer
+// than the chip holds, so the chain's launches find free compute units.
+constexpr int kSideWgs = 0;
+
 // U over the region [x, min(x + kRegion, d)): the diagonal inverses, then the
 // merges level by level (full nodes batched, the last node possibly partial).
-hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st) {
+hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st,
+                           int wgs) {
     const int64_t end = std::min<int64_t>(x + kRegion, d);
     hipLaunchKernelGGL(invert_blocks_kernel, dim3((unsigned)ceil_div(end - x, NB)), dim3(kWave), 0, st, Tf, U, d, lda, x);
     hipError_t e = hipGetLastError();
@@ -706,14 +714,14 @@ hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int6
     for (int64_t sz = NB; sz < end - x; sz *= 2) {
         const int64_t full = (end - x) / (2 * sz);
         if (full > 0) {
-            if ((e = merge_right(Tf, U, Tw, d, lda, x, sz, sz, full, 2 * sz, st)) != hipSuccess) return e;
-            if ((e = merge_left(U, Tw, d, lda, x, sz, sz, full, 2 * sz, st)) != hipSuccess) return e;
+            if ((e = merge_right(Tf, U, Tw, d, lda, x, sz, sz, full, 2 * sz, st, wgs)) != hipSuccess) return e;
+            if ((e = merge_left(U, Tw, d, lda, x, sz, sz, full, 2 * sz, st, wgs)) != hipSuccess) return e;
         }
         const int64_t i0 = x + 2 * full * sz;
         const int64_t ni = std::min<int64_t>(sz, end - i0), nj = end - i0 - ni;
         if (nj > 0) {
-            if ((e = merge_right(Tf, U, Tw, d, lda, i0, ni, nj, 1, 0, st)) != hipSuccess) return e;
-            if ((e = merge_left(U, Tw, d, lda, i0, ni, nj, 1, 0, st)) != hipSuccess) return e;
+            if ((e = merge_right(Tf, U, Tw, d, lda, i0, ni, nj, 1, 0, st, wgs)) != hipSuccess) return e;
+            if ((e = merge_left(U, Tw, d, lda, i0, ni, nj, 1, 0, st, wgs)) != hipSuccess) return e;
         }
     }
     return hipSuccess;
@@ -728,9 +736,10 @@ hipError_t assemble_region(const float *Tf, float *U, float *Tw, int64_t d, int6
 // inverse is the region's), then Tw_I += T_IJ X_J for the rows I = [0, x)
 // above it, so the end is left with the first block only.
 hipError_t solve_left_block(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, int64_t h,
-                            int64_t w, hipStream_t st) {
+                            int64_t w, hipStream_t st, int wgs) {
     const int64_t r = std::min<int64_t>(kRegion, h - x);
     GemmDesc a;  // U[x:x+r, h:h+w] = -U[x:x+r, x:x+r] Tw[x:x+r, h:h+w]
+    a.max_wgs = wgs;
     a.M = r;
     a.N = w;
     a.K = r;
@@ -746,6 +755,7 @@ hipError_t solve_left_block(const float *Tf, float *U, float *Tw, int64_t d, int
     hipError_t e = launch_gemm_f32(a, st);
     if (e != hipSuccess || x == 0) return e;
     GemmDesc b;  // Tw[0:x, h:h+w] += T[0:x, x:x+r] U[x:x+r, h:h+w]
+    b.max_wgs = wgs;
     b.M = x;
     b.N = w;
     b.K = r;
@@ -770,17 +780,18 @@ inline bool solved_by_rows(int64_t h) { return h >= 2 * kRegion; }
 // at x while x is aligned to it, and the right product of the node whose
 // middle is x (its right half, starting at x, is complete by then); then the
 // row block at x of every node [0, 2h) with h > x.
-hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st) {
-    hipError_t e = assemble_region(Tf, U, Tw, d, lda, x, st);
+hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t lda, int64_t x, hipStream_t st,
+                       int wgs) {
+    hipError_t e = assemble_region(Tf, U, Tw, d, lda, x, st, wgs);
     if (e != hipSuccess) return e;
     for (int64_t n = 2 * kRegion; n / 2 < d; n *= 2) {
         const int64_t half = n / 2;
         if (x % n == 0) {
             if (x + half < d && !(x == 0 && solved_by_rows(half)))
-                if ((e = merge_left(U, Tw, d, lda, x, half, std::min<int64_t>(half, d - x - half), 1, 0, st)) != hipSuccess)
+                if ((e = merge_left(U, Tw, d, lda, x, half, std::min<int64_t>(half, d - x - half), 1, 0, st, wgs)) != hipSuccess)
                     return e;
         } else if (x % n == half) {
-            if ((e = merge_right(Tf, U, Tw, d, lda, x - half, half, std::min<int64_t>(half, d - x), 1, 0, st)) !=
+            if ((e = merge_right(Tf, U, Tw, d, lda, x - half, half, std::min<int64_t>(half, d - x), 1, 0, st, wgs)) !=
                 hipSuccess)
                 return e;
             break;
@@ -790,7 +801,8 @@ hipError_t assemble_at(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
     }
     for (int64_t h = 2 * kRegion; h < d; h *= 2)
         if (solved_by_rows(h) && x < h)
-            if ((e = solve_left_block(Tf, U, Tw, d, lda, x, h, std::min<int64_t>(h, d - h), st)) != hipSuccess) return e;
+            if ((e = solve_left_block(Tf, U, Tw, d, lda, x, h, std::min<int64_t>(h, d - h), st, wgs)) != hipSuccess)
+                return e;
     return hipSuccess;
 }
 
@@ -895,7 +907,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
             // only in rows >= k0; p_kernel stages P^T in Tw's first NB rows.)
             if (k0 > 0 && k0 % kRegion == 0) {
                 if ((e = fork_to(*ss, s)) != hipSuccess) return e;
-                if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st)) != hipSuccess) return e;
+                if ((e = assemble_at(Tf, U, Tw, d, lda, k0, ss->st, kSideWgs)) != hipSuccess) return e;
             }
         }
         if (p0 > 0) {
@@ -937,6 +949,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                 r.alpha = -1.0f;
                 r.beta = 1.0f;
                 r.upper_only = 1;
+                r.max_wgs = kSideWgs;
                 if ((e = launch_gemm_f32(r, ss->st2)) != hipSuccess) return e;
                 if ((e = hipEventRecord(ev_rest, ss->st2)) != hipSuccess) return e;
             }
@@ -945,7 +958,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
     // The rest of U = T^-1 once T is complete, then the caller's stream waits
     // for all of it.
     if ((e = fork_to(*ss, s)) != hipSuccess) return e;
-    if ((e = assemble_at(Tf, U, Tw, d, lda, 0, ss->st)) != hipSuccess) return e;
+    if ((e = assemble_at(Tf, U, Tw, d, lda, 0, ss->st, 0)) != hipSuccess) return e;
     if ((e = signal_wait(ss->ev[1], ss->st, s)) != hipSuccess) return e;
     return hipStreamWaitEvent(s, ev_rest, 0);
 }

@@ -127,3 +127,17 @@ def test_argument_errors_are_synchronous():
     assert lib.gptq_calibrate_chunk_tokens(4096) == 16384
     assert lib.gptq_calibrate_chunk_tokens(8192) == 8192
     assert lib.gptq_calibrate_chunk_tokens(1 << 20) == 1024 and lib.gptq_calibrate_chunk_tokens(16) == 65536
+
+
+def test_timing_read_arguments():
+    """Unknown kinds and NULL outputs are rejected; with nothing recorded a kind reads as zero (no GPU work)."""
+    lib = gq.load_library()
+    ms, n, fl = ctypes.c_double(1.0), ctypes.c_int64(5), ctypes.c_double(2.0)
+    for op in (-1, 3):
+        assert lib.gptq_timing_read(op, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl)) == gq.ERR_INVALID_ARG
+    assert lib.gptq_timing_read(gq.TIMED_LAZY, None, ctypes.byref(n), None) == gq.ERR_INVALID_ARG
+    assert lib.gptq_timing_read(gq.TIMED_LAZY, ctypes.byref(ms), None, None) == gq.ERR_INVALID_ARG
+    for op in (gq.TIMED_LAZY, gq.TIMED_BATCH, gq.TIMED_LAZY_SPLIT):
+        assert lib.gptq_timing_read(op, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl)) == gq.OK
+        assert (ms.value, n.value, fl.value) == (0.0, 0, 0.0)
+    assert lib.gptq_timing_read(gq.TIMED_BATCH, ctypes.byref(ms), ctypes.byref(n), None) == gq.OK  # flops optional
