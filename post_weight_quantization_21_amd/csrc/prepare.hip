@@ -7,10 +7,10 @@
 // of U.  Route (2/3 d^3 flops, fp32):
 //   1. H_d = P H P^T + lambda I           (gather + one-workgroup damping)
 //   2. UL-Cholesky H_d = T T^T, T upper   (blocked on two levels, from the
-//      bottom-right corner: panels of 256 columns, each factored in steps of
+//      bottom-right corner: panels of 512 columns, each factored in steps of
 //      64, one launch per step -- the step's column of T by back substitution,
 //      the rank-64 update of the panel's remaining columns on matrix cores, the
-//      next diagonal block factored by one workgroup -- then one rank-256
+//      next diagonal block factored by one workgroup -- then one rank-512
 //      update of the whole leading block by the fp32 matrix-core GEMM)
 //   3. U = T^-1                           (the diagonal blocks are inverted
 //      all at once after the factorization; the off-diagonal blocks are merged
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kFThreads) void step_kernel(float *__restrict__ A, 
                                                          int nt, int tj_lo, int32_t *__restrict__ info) {
     // Tiles in reverse order: workgroup 0 takes the last diagonal tile, whose
     // factorization of the next block is the step's longest chain.  Only the
-    // tile columns tj_lo .. nt-1 (the rest of the current 256-column panel) are
+    // tile columns tj_lo .. nt-1 (the rest of the current panel) are
     // updated; the columns left of the panel get the panel's whole product later.
     int ti, tj;
     tile_upper_cols(step_tiles(tj_lo, nt) - 1 - blockIdx.x, tj_lo, nt, ti, tj);
@@ -815,7 +815,9 @@ int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
 
 // Outer level of the factorization: the leading block gets each panel's
 // product at once.
-constexpr int64_t kPanel = 256;  // columns per panel of the outer level
+// Columns per panel of the outer level: wider panels mean fewer, longer
+// products of the leading block and longer steps (512 measured best of 128-1024).
+constexpr int64_t kPanel = 512;
 
 }  // namespace
 
