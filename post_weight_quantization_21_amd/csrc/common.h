@@ -57,9 +57,9 @@ constexpr int kGemmTile = 128;
 int64_t gemm_num_tiles(const GemmDesc &g);
 hipError_t launch_gemm_f32(const GemmDesc &g, hipStream_t s);
 // The same product on the bf16 matrix cores through an exact three-term split
-// of each fp32 operand (gemm_split.hip): no triangles, no batch, K a multiple
-// of 32, 16-byte aligned operands, lda and ldb multiples of 4, and M (N) a
-// multiple of 4 when A (B) is stored K-major.
+// of each fp32 operand (gemm_split.hip): upper_only only for a square C, no
+// batch, K a multiple of 32, 16-byte aligned operands, lda and ldb multiples
+// of 4, and M (N) a multiple of 4 when A (B) is stored K-major.
 bool gemm_split_supported(const GemmDesc &g);
 hipError_t launch_gemm_split(const GemmDesc &g, hipStream_t s);
 

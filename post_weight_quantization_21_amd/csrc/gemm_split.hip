@@ -165,14 +165,29 @@ struct IC {
 template <int AKM, int BKM>
 __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
     const int gx = (int)ceil_div(g.N, ST);
-    const int64_t tiles = (int64_t)gx * ceil_div(g.M, ST);
+    // upper_only (M = N): only the tiles on and above the diagonal, row-major
+    const int64_t tiles = g.upper_only ? (int64_t)gx * (gx + 1) / 2 : (int64_t)gx * ceil_div(g.M, ST);
     // L2 domain x runs tiles [t0, t1) in row-major order: its resident
     // workgroups share rows of A.
     const int64_t xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     const int64_t t0 = xcd * tiles / kXcds, t1 = (xcd + 1) * tiles / kXcds;
     if (slot >= t1 - t0) return;
-    const int64_t m0 = (t0 + slot) / gx * ST, n0 = (t0 + slot) % gx * ST;
-    const int nst = (int)(g.K / SK);
+    int64_t tm = (t0 + slot) / gx, tn = (t0 + slot) % gx;
+    if (g.upper_only) {
+        int64_t t = t0 + slot, i = 0;
+        while (t >= gx - i) t -= gx - i++;  // row i holds gx - i tiles
+        tm = i;
+        tn = i + t;
+    }
+    const int64_t m0 = tm * ST, n0 = tn * ST;
+    // Triangular operands are zero outside their triangle: A upper (A[m][k] = 0
+    // for k < m) starts K at the tile's first row, B upper (B[k][n] = 0 for
+    // k > n) ends it after the tile's last column.  Both ends are multiples of
+    // 256 or K, so the stage count stays even.
+    int64_t kbeg = 0, kend = g.K;
+    if (g.a_upper) kbeg = m0 < g.K ? m0 : g.K;
+    if (g.b_upper) kend = n0 + ST < g.K ? n0 + ST : g.K;
+    const int nst = kend > kbeg ? (int)((kend - kbeg) / SK) : 0;
 
     __shared__ SplitSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
     // the last stage again, into a slot nobody reads, so the loads in flight
     // at each wait are fixed.
     auto issue = [&](int st, int part) {
-        const int64_t k0 = (int64_t)(st < nst ? st : nst - 1) * SK;
+        const int64_t k0 = kbeg + (int64_t)(st < nst ? st : nst - 1) * SK;
         if (part < 4)
             stage_load<AKM>(sm.a[st % SNS], g.A, g.lda, k0, m0, g.M, wave, lane, part);
         else
@@ -277,7 +292,8 @@ __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
 
     // C = alpha acc + beta C, one accumulator block at a time; interior tiles
     // without bounds checks.
-    const bool full = m0 + ST <= g.M && n0 + ST <= g.N;
+    // with upper_only, a diagonal tile stores only m <= n
+    const bool full = m0 + ST <= g.M && n0 + ST <= g.N && !(g.upper_only && m0 == n0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -300,7 +316,7 @@ __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int dr = 8 * (r >> 2) + (r & 3);
-                    if (mb + dr < g.M) {
+                    if (mb + dr < g.M && (!g.upper_only || mb + dr <= n)) {
                         float v = g.alpha * acc[i][j][r];
                         if (g.beta != 0.0f) v += g.beta * cp[dr * g.ldc];
                         cp[dr * g.ldc] = v;
@@ -317,7 +333,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool gemm_split_supported(const GemmDesc &g) {
     // 16-byte chunks wholly inside or outside: aligned bases and leading
     // dimensions, the contiguous extents (M or N when K-major, else K) multiples of 4.
-    return !g.upper_only && !g.a_upper && !g.b_upper && g.batch == 1 && g.epilogue == EPI_STORE && g.K > 0 &&
+    return (!g.upper_only || g.M == g.N) && g.batch == 1 && g.epilogue == EPI_STORE && g.K > 0 &&
            g.K % (2 * SK) == 0 && aligned16(g.A) && aligned16(g.B) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
            (!g.a_trans || g.M % 4 == 0) && (g.b_trans || g.N % 4 == 0);
 }
@@ -325,7 +341,8 @@ bool gemm_split_supported(const GemmDesc &g) {
 hipError_t launch_gemm_split(const GemmDesc &g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (!gemm_split_supported(g)) return hipErrorInvalidValue;
-    const int64_t tiles = ceil_div(g.M, ST) * ceil_div(g.N, ST);
+    const int64_t gx = ceil_div(g.N, ST);
+    const int64_t tiles = g.upper_only ? gx * (gx + 1) / 2 : ceil_div(g.M, ST) * gx;
     const dim3 grid((unsigned)(kXcds * ceil_div(tiles, kXcds)));
     const int akm = g.a_trans ? 1 : 0, bkm = g.b_trans ? 0 : 1;
     if (akm && bkm)

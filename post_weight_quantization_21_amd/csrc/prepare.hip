@@ -642,6 +642,17 @@ __global__ __launch_bounds__(kFThreads) void p_kernel(const float *__restrict__ 
     }
 }
 
+// Wide products with K of 512 and more (the leading block's products of a
+// panel, the inverse's merges and row-block solves): on the bf16 matrix cores
+// through the exact three-term split when they have enough 256 x 256 tiles to
+// fill the chip, else on the fp32 ones.
+hipError_t launch_wide_product(const GemmDesc &g, hipStream_t s) {
+    const int64_t gx = ceil_div(g.N, 256);
+    const int64_t tiles = g.upper_only ? gx * (gx + 1) / 2 : ceil_div(g.M, 256) * gx;
+    if (g.K >= 512 && tiles >= 64 && gemm_split_supported(g)) return launch_gemm_split(g, s);
+    return launch_gemm_f32(g, s);
+}
+
 // Pairwise merges of inverted blocks: inv([[A, B], [0, C]]) = [[A^-1, -A^-1 B C^-1], [0, C^-1]],
 // i.e. U12 = -U11 T12 U22 for the node [i0, i0 + ni + nj) with children
 // [i0, j0 = i0 + ni) and [j0, j0 + nj).  Two products:
@@ -667,7 +678,7 @@ hipError_t merge_right(const float *Tf, float *U, float *Tw, int64_t d, int64_t 
     g.ldc = lda;
     g.strideA = g.strideC = stride * (lda + 1);
     g.strideB = stride * (d + 1);
-    return launch_gemm_f32(g, st);
+    return launch_wide_product(g, st);
 }
 
 hipError_t merge_left(float *U, const float *Tw, int64_t d, int64_t lda, int64_t i0, int64_t ni, int64_t nj,
@@ -690,13 +701,14 @@ hipError_t merge_left(float *U, const float *Tw, int64_t d, int64_t lda, int64_t
     h.beta = 0.0f;
     h.strideA = h.strideC = stride * (d + 1);
     h.strideB = stride * (lda + 1);
-    return launch_gemm_f32(h, st);
+    return launch_wide_product(h, st);
 }
 
 // Columns per region of the inverse's assembly: once the factorization has
 // passed a region, its diagonal inverses and the merges inside it run on a
 // second stream, beside the rest of the factorization.
 constexpr int64_t kRegion = 512;
+
 
 // Workgroups of each product launched on a side stream while the
 // factorization's chain runs on the caller's stream (0: one per tile): fewer
@@ -752,7 +764,7 @@ hipError_t solve_left_block(const float *Tf, float *U, float *Tw, int64_t d, int
     a.ldc = d;
     a.alpha = -1.0f;
     a.beta = 0.0f;
-    hipError_t e = launch_gemm_f32(a, st);
+    hipError_t e = launch_wide_product(a, st);
     if (e != hipSuccess || x == 0) return e;
     GemmDesc b;  // Tw[0:x, h:h+w] += T[0:x, x:x+r] U[x:x+r, h:h+w]
     b.max_wgs = wgs;
@@ -767,7 +779,7 @@ hipError_t solve_left_block(const float *Tf, float *U, float *Tw, int64_t d, int
     b.ldc = lda;
     b.alpha = 1.0f;
     b.beta = 1.0f;
-    return launch_gemm_f32(b, st);
+    return launch_wide_product(b, st);
 }
 
 // Nodes [0, 2h) whose upper-right block is solved region by region (the
@@ -934,7 +946,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
             g.ldc = lda;
             g.alpha = -1.0f;
             g.beta = 1.0f;  // the strictly lower part of A is never read
-            if ((e = launch_gemm_f32(g, s)) != hipSuccess) return e;
+            if ((e = launch_wide_product(g, s)) != hipSuccess) return e;
             if (n0 > 0) {
                 if ((e = hipStreamWaitEvent(ss->st2, ev_panel, 0)) != hipSuccess) return e;
                 GemmDesc r;
@@ -952,7 +964,7 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
                 r.beta = 1.0f;
                 r.upper_only = 1;
                 r.max_wgs = kSideWgs;
-                if ((e = launch_gemm_f32(r, ss->st2)) != hipSuccess) return e;
+                if ((e = launch_wide_product(r, ss->st2)) != hipSuccess) return e;
                 if ((e = hipEventRecord(ev_rest, ss->st2)) != hipSuccess) return e;
             }
         }

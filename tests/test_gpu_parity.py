@@ -78,7 +78,7 @@ def _spd_h(oracle_mod, d, seed, recipe="down_proj_7b"):
 
 
 @pytest.mark.parametrize("d,act_order", [(64, False), (77, True), (130, False), (200, False), (200, True),
-                                         (1000, True), (2048, False), (2200, True)])
+                                         (1000, True), (2048, False), (2200, True), (4096, True)])
 def test_prepare_parity(oracle_mod, d, act_order):
     """U from the GPU vs the oracle's factor of the same fp32 Hessian.
 
@@ -102,6 +102,36 @@ def test_prepare_parity(oracle_mod, d, act_order):
     assert np.array_equal(host(perm), p_ref)
     Hp = H32.astype(np.float64)[np.ix_(p_ref, p_ref)]
     Hd = oracle_mod.damp(Hp, 0.01)
+    Uref = oracle_mod.inv_chol_upper(Hd)
+    Ug = host(U).astype(np.float64)
+    assert not Ug[np.tril_indices(d, -1)].any()
+    rel = np.linalg.norm(Ug - Uref) / np.linalg.norm(Uref)
+    res = np.abs(Ug.T @ Ug @ Hd - np.eye(d)).max()
+    log(f"  rel={rel:.3e} residual={res:.3e}")
+    assert rel < 1e-3 and res < 1e-3
+
+
+def test_prepare_parity_wide_panel_products(oracle_mod):
+    """d = 8704: the leading block's panel products are wide enough (64 tiles of 256 x 256 and more)
+    for the split-bf16 product on both streams, the caller's (the next panel's columns) and the side
+    stream (the upper triangle left of them).  Same bars as test_prepare_parity; fewer tokens than
+    there (the damping keeps H_d well conditioned)."""
+    torch = torch_mod()
+    d = 8704
+    log(f"prepare d={d} (split panel products)")
+    r = datagen.recipe("down_proj_7b", d_out=4, d_in=d, n_tok=d + 1024)
+    H64 = oracle_mod.hessian(datagen.make_activations(r, 3))
+    H32 = H64.astype(np.float32)
+    hdiag = np.diag(H64).copy()
+    cfg = gq.config(4, False, 0, 128, 0.01, True)
+    U = torch.empty(d, d, dtype=torch.float32, device="cuda")
+    perm = torch.empty(d, dtype=torch.int32, device="cuda")
+    info = gq.prepare_hinv(cuda(np.triu(H32)), cfg, U, perm, hdiag=cuda(hdiag))
+    torch.cuda.synchronize()
+    assert int(host(info)[0]) == 0
+    p_ref = oracle_mod.act_order_perm(hdiag)
+    assert np.array_equal(host(perm), p_ref)
+    Hd = oracle_mod.damp(H32.astype(np.float64)[np.ix_(p_ref, p_ref)], 0.01)
     Uref = oracle_mod.inv_chol_upper(Hd)
     Ug = host(U).astype(np.float64)
     assert not Ug[np.tril_indices(d, -1)].any()
