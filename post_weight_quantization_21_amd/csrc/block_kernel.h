@@ -2,9 +2,9 @@
 // section: each quantized column's error goes onto the not-yet-quantized
 // columns through the matching row of the inverse Hessian factor).
 //
-// Four lanes per output row.  The row's BT weights of the batch stay in
-// registers (BT/4 per lane) for the whole batch; the BT x BT block of U sits
-// in LDS.  For each column j:
+// L lanes per output row (4, or 16 for layers with few rows).  The row's BT
+// weights of the batch stay in registers (BT/L per lane) for the whole batch;
+// the BT x BT block of U sits in LDS.  For each column j:
 // take the column's grid (SRC, see GridSource: fitted from the current
 // weights at a group start, or read from the grids fitted before), quantize, form
 // e = (w_j - w_hat_j) / U[j][j], update w_k -= e U[j][k] for the batch's later
@@ -21,31 +21,33 @@
 
 namespace gptq {
 
-constexpr int kRowLanes = 4;  // lanes per output row
-
-// Each output row is owned by a quad of lanes; lane q of the quad keeps
-// columns q, q+4, q+8, ... of the batch in registers.  Column j's owner
-// broadcasts the weight to its quad (DPP), all four lanes quantize it (same
-// result), and each lane pushes the error onto its own later columns.
-// NT threads per workgroup (NT / 4 rows).
-template <int BT, int GT, int NT, int SRC>
+// Each output row is owned by L consecutive lanes; lane q of the group keeps
+// columns q, q+L, q+2L, ... of the batch in registers.  Column j's owner
+// broadcasts the weight to its group (DPP), all L lanes quantize it (same
+// result), and each lane pushes the error onto its own later columns.  With
+// L = 16 each lane carries a quarter of the FMAs of L = 4 on the column chain,
+// which sets the time when the layer has too few rows to fill the chip.
+// NT threads per workgroup (NT / L rows).
+template <int BT, int GT, int NT, int SRC, int L>
 __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     static_assert(SRC != kColumnGrids || GT == 0, "per-column grids take no group tile");
-    constexpr int CPL = BT / kRowLanes;
-    constexpr int kRows = NT / kRowLanes;
+    static_assert(L == 4 || L == 16, "four or sixteen lanes per row");
+    static_assert(BT % (4 * L) == 0 && (GT == 0 || GT % L == 0), "whole 16-byte words of U per lane; groups of whole steps");
+    constexpr int CPL = BT / L;
+    constexpr int kRows = NT / L;
     // The B x B block of U, strictly upper part (zero on and below the
-    // diagonal), laid out per quad lane: ut[j][p][q][i] = U[j][q + 4 (4p + i)],
+    // diagonal), laid out per group lane: ut[j][p][q][i] = U[j][q + L (4p + i)],
     // so lane q reads its columns of row j as contiguous 16-byte words and the
-    // four lanes of a quad hit four different bank groups.
+    // lanes of a group hit different bank groups.
     constexpr int NP = CPL / 4;
-    __shared__ __attribute__((aligned(16))) float ut[BT][NP][kRowLanes][4];
+    __shared__ __attribute__((aligned(16))) float ut[BT][NP][L][4];
     __shared__ float inv_d[BT];
     __shared__ int32_t pcol[BT];
     __shared__ int32_t gcol[SRC == kColumnGrids ? BT : 1];  // group of each column (per-column grids)
     const int tid = threadIdx.x;
     const int nc = a.ncols;
-    const int q = tid & (kRowLanes - 1);
-    const int64_t r = (int64_t)blockIdx.x * kRows + (tid >> 2);
+    const int q = tid & (L - 1);
+    const int64_t r = (int64_t)blockIdx.x * kRows + tid / L;
     const bool active = r < a.d_out;
     float *wrow = a.W + r * a.ldw + a.c0;
     // Global loads of the prologue are all issued before the first wait: the
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         const float *wsrc = a.W + (active ? r : a.d_out - 1) * a.ldw + a.c0;
 #pragma unroll
         for (int t = 0; t < CPL; ++t) {
-            const int k = q + kRowLanes * t;
+            const int k = q + L * t;
             uint32_t m = (active && k < nc) ? ~0u : 0u;
             asm volatile("" : "+v"(m));
             w[t] = __uint_as_float(__float_as_uint(wsrc[k < nc ? k : nc - 1]) & m);
@@ -145,12 +147,12 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                 const int e4 = tid + (p0 + u) * NT;
                 const int i = (e4 * 4) / BT, k = (e4 * 4) % BT;
                 const float4 v = uv[u];
-                // columns k .. k+3 belong to quad lanes 0..3, at t = k / 4
-                const int t = k / kRowLanes;
-                ut[i][t / 4][0][t % 4] = (k + 0 > i) ? v.x : 0.0f;
-                ut[i][t / 4][1][t % 4] = (k + 1 > i) ? v.y : 0.0f;
-                ut[i][t / 4][2][t % 4] = (k + 2 > i) ? v.z : 0.0f;
-                ut[i][t / 4][3][t % 4] = (k + 3 > i) ? v.w : 0.0f;
+                // columns k .. k+3 belong to group lanes k % L .. k % L + 3, at t = k / L
+                const int t = k / L, l0 = k % L;
+                ut[i][t / 4][l0 + 0][t % 4] = (k + 0 > i) ? v.x : 0.0f;
+                ut[i][t / 4][l0 + 1][t % 4] = (k + 1 > i) ? v.y : 0.0f;
+                ut[i][t / 4][l0 + 2][t % 4] = (k + 2 > i) ? v.z : 0.0f;
+                ut[i][t / 4][l0 + 3][t % 4] = (k + 3 > i) ? v.w : 0.0f;
             }
         }
     }
@@ -198,14 +200,14 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     float idn[2];
     auto load_row = [&](int j, float4(&dst)[NP], float &id) {
 #pragma unroll
-        for (int p = (j / kRowLanes) / 4; p < NP; ++p) dst[p] = *reinterpret_cast<const float4 *>(&ut[j][p][q][0]);
+        for (int p = (j / L) / 4; p < NP; ++p) dst[p] = *reinterpret_cast<const float4 *>(&ut[j][p][q][0]);
         id = inv_d[j];
     };
     load_row(0, urow[0], idn[0]);
 
 #pragma unroll
     for (int j = 0; j < BT; ++j) {
-        const int oq = j & (kRowLanes - 1), ot = j / kRowLanes;
+        const int oq = j & (L - 1), ot = j / L;
         const int cur = j & 1;
         if (j + 1 < BT) load_row(j + 1, urow[cur ^ 1], idn[cur ^ 1]);
         if constexpr (SRC == kColumnGrids)
@@ -220,23 +222,23 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             if (j % GT == 0) {
                 float amax = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
-                for (int t = j / kRowLanes; t < (j + GT) / kRowLanes; ++t) {
+                for (int t = j / L; t < (j + GT) / L; ++t) {
                     amax = fmaxf(amax, fabsf(w[t]));
                     lo = fminf(lo, w[t]);
                     hi = fmaxf(hi, w[t]);
                 }
-                amax = fmaxf(amax, quad_xor1(amax));
-                lo = fminf(lo, quad_xor1(lo));
-                hi = fmaxf(hi, quad_xor1(hi));
-                amax = fmaxf(amax, quad_xor2(amax));
-                lo = fminf(lo, quad_xor2(lo));
-                hi = fmaxf(hi, quad_xor2(hi));
+#pragma unroll
+                for (int st = 0; st < lanes_steps<L>(); ++st) {
+                    amax = fmaxf(amax, lanes_step<L>(amax, st));
+                    lo = fminf(lo, lanes_step<L>(lo, st));
+                    hi = fmaxf(hi, lanes_step<L>(hi, st));
+                }
                 gr = grid_make(amax, lo, hi, a.bits, a.sym);
-                fit_sz[tid >> 2][j / GT][0] = gr.s;
-                fit_sz[tid >> 2][j / GT][1] = gr.zero;
+                fit_sz[tid / L][j / GT][0] = gr.s;
+                fit_sz[tid / L][j / GT][1] = gr.zero;
             }
         }
-        const float wj = quad_bcast(w[ot], oq);
+        const float wj = lanes_bcast<L>(w[ot], oq);
         const float ql = grid_level(wj, gr);
         const float code = ql + gr.zadd;
         // e = (w_j - (code - zero) s) / U_jj, with code - zero = ql - zd exact;
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
             for (int g = 0; g < NG; ++g)
                 if (g * GT < nc) {
                     const int64_t gi = (a.c0 + g * GT) / a.g;
-                    a.scales[r * a.ng + gi] = fit_sz[tid >> 2][g][0];
-                    a.zeros[r * a.ng + gi] = fit_sz[tid >> 2][g][1];
+                    a.scales[r * a.ng + gi] = fit_sz[tid / L][g][0];
+                    a.zeros[r * a.ng + gi] = fit_sz[tid / L][g][1];
                 }
         }
     }
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     uint8_t *crow = a.codes + r * a.ldc;
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
-        const int k = q + kRowLanes * t;
+        const int k = q + L * t;
         if (k < nc) {
             wrow[k] = w[t];
             crow[pcol[k]] = (uint8_t)(cw[t / 4] >> (8 * (t & 3)));
@@ -278,47 +280,52 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     }
 }
 
-template <int BT, int GT, int NT>
+template <int BT, int GT, int NT, int L>
 hipError_t launch_block_gt(const BlockArgs &a, int src, unsigned grid, hipStream_t s) {
     if (src == kStoredGrids)
-        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kStoredGrids>), dim3(grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kStoredGrids, L>), dim3(grid), dim3(NT), 0, s, a);
     else
-        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kFitGrids>), dim3(grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, GT, NT, kFitGrids, L>), dim3(grid), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
-template <int BT, int NT>
+template <int BT, int NT, int L>
 hipError_t launch_block_nt(const BlockArgs &a, int gt, int src, hipStream_t s) {
-    const unsigned grid = (unsigned)ceil_div(a.d_out, NT / kRowLanes);
+    const unsigned grid = (unsigned)ceil_div(a.d_out, NT / L);
     if (src == kColumnGrids) {
         if (!a.gperm || !a.gtab || gt != 0) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kColumnGrids>), dim3(grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kColumnGrids, L>), dim3(grid), dim3(NT), 0, s, a);
         return hipGetLastError();
     }
     switch (gt) {
     case 0:  // the grid is read at the batch start either way
-        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kFitGrids>), dim3(grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((gptq_block_kernel<BT, 0, NT, kFitGrids, L>), dim3(grid), dim3(NT), 0, s, a);
         return hipGetLastError();
     case 32:
-        return launch_block_gt<BT, 32, NT>(a, src, grid, s);
+        return launch_block_gt<BT, 32, NT, L>(a, src, grid, s);
     case 64:
-        if constexpr (BT >= 64) return launch_block_gt<BT, 64, NT>(a, src, grid, s);
+        if constexpr (BT >= 64) return launch_block_gt<BT, 64, NT, L>(a, src, grid, s);
         return hipErrorInvalidValue;
     case 128:
-        if constexpr (BT >= 128) return launch_block_gt<BT, 128, NT>(a, src, grid, s);
+        if constexpr (BT >= 128) return launch_block_gt<BT, 128, NT, L>(a, src, grid, s);
         return hipErrorInvalidValue;
     default:
         return hipErrorInvalidValue;
     }
 }
 
-// Four-wave workgroups (64 rows).  One-wave workgroups (16 rows), which
-// spread a small layer over more CUs, measured slower: each row's column chain,
-// not the CU count, sets the time.
+// Four-wave workgroups.  Four lanes per row (64 rows per workgroup) when the
+// layer has rows enough for about two waves per SIMD, else sixteen (16 rows per
+// workgroup, batches of 64 and 128 columns).  One-wave workgroups at four lanes
+// per row, which spread a small layer over more CUs, measured slower: each
+// row's column chain, not the CU count, sets the time.
+constexpr int64_t kWideRowsMax = 8192;  // rows up to which a row takes 16 lanes
 template <int BT>
 hipError_t launch_block_bt(const BlockArgs &a, int gt, int src, hipStream_t s) {
     if (!a.Et || !a.W || !a.U || !a.codes) return hipErrorInvalidValue;
-    return launch_block_nt<BT, kBlockThreads>(a, gt, src, s);
+    if constexpr (BT >= 64)
+        if (a.d_out <= kWideRowsMax) return launch_block_nt<BT, kBlockThreads, 16>(a, gt, src, s);
+    return launch_block_nt<BT, kBlockThreads, 4>(a, gt, src, s);
 }
 
 }  // namespace gptq
