@@ -384,6 +384,11 @@ constexpr int64_t kSplitMinK = 512;
 // Rows from which the superblock's inner updates are left-looking.
 constexpr int64_t kLeftLookRows = 16384;
 
+// Left-looking: once the superblock's batches not yet applied to the rest of
+// it reach this many columns, one product applies them to all of it (K = 512
+// on the split GEMM) instead of growing every later batch's product.
+constexpr int64_t kCatchUpCols = 512;
+
 // W[:, c1:c1+n] += (-E) U[k0:k0+k, c1:c1+n] with -E^T stored as Et [k][ldet].
 hipError_t lazy_update(float *W, int64_t d_out, int64_t d_in, const float *Et, int64_t ldet, const float *U, int64_t k0,
                        int64_t k, int64_t c1, int64_t n, hipStream_t s) {
@@ -491,12 +496,29 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     // columns); short ones, whose single batch column of tiles would leave most
     // of the chip idle, update the rest of the superblock after each batch.
     const bool left = deferred && d_out >= kLeftLookRows;
+    const bool refit = !fixed && gt == 0;  // a grid fitted at each group start from the group's current weights
     for (int64_t s0 = 0; s0 < d_in; s0 += sc) {
         const int64_t s1 = std::min<int64_t>(s0 + sc, d_in);
+        // Left-looking: every column in [c0, s1) already has the errors of the
+        // columns before lb; each batch takes those of [lb, c0) just before it.
+        int64_t lb = s0;
         for (int64_t c0 = s0; c0 < s1; c0 += B) {
             const int nc = (int)std::min<int64_t>(B, s1 - c0);
-            if (left && (e = lazy_update(W, d_out, d_in, Et, ldet, U, s0, c0 - s0, c0, nc, s)) != hipSuccess) return e;
-            if (!fixed && gt == 0 && c0 % g == 0) {
+            if (left) {
+                // Catch up the rest of the superblock: where a grid is about to be
+                // fitted from a whole group (every column of the group must hold every
+                // earlier column's error), and where [lb, c0) has grown to
+                // kCatchUpCols columns.
+                if (c0 > lb && ((refit && c0 % g == 0) || c0 - lb >= kCatchUpCols)) {
+                    if ((e = lazy_update(W, d_out, d_in, Et + (lb - s0) * ldet, ldet, U, lb, c0 - lb, c0, s1 - c0, s)) !=
+                        hipSuccess)
+                        return e;
+                    lb = c0;
+                }
+                if ((e = lazy_update(W, d_out, d_in, Et + (lb - s0) * ldet, ldet, U, lb, c0 - lb, c0, nc, s)) != hipSuccess)
+                    return e;
+            }
+            if (refit && c0 % g == 0) {
                 const int64_t waves = d_out;
                 hipLaunchKernelGGL(rtn_kernel, dim3((unsigned)ceil_div(waves * kWave, kThreads)), dim3(kThreads), 0, s, W,
                                    d_in, d_out, g, ng, c0 / g, (int64_t)1, c.bits, c.symmetric, 1, (uint8_t *)nullptr,

@@ -1,6 +1,7 @@
 """Layers whose superblock updates take the split-bf16 product (K >= 512, N >= 512, at least 64
 tiles of 256 x 256), with ragged row and column tiles: right-looking and left-looking inner
-updates, K = 1024 and K = 512 superblocks, with and without a column order.
+updates (with their catch-up products: every 512 columns, and before a grid is fitted from a
+group that spans batches), K = 1024 and K = 512 superblocks, with and without a column order.
 
 Rows are independent given U and the order, so the oracle's pass on sampled rows (the last rows,
 which sit in the partial row tile, included) is an exact per-row expectation: >= 99.9 % identical
@@ -36,6 +37,9 @@ CASES = [
     (16388, 1536, 0, False, 4, True, 128),
     # 113 x 8 = 904 tiles in the first superblock update, a ragged last row tile of 4 rows
     (28676, 3072, 0, False, 4, True, 128),
+    # tall layer, dynamic groups of 256 over batches of 128: before each group's grid is
+    # fitted the rest of the superblock is brought up to date (left-looking catch-up)
+    (16388, 2048, 0, False, 4, False, 256),
 ]
 
 
