@@ -64,21 +64,46 @@ __global__ __launch_bounds__(kThreads) void scatter_rank_kernel(const int32_t *_
     if (i < d) perm[rank[i]] = (int32_t)i;
 }
 
-// A[a][b] = H[pa][pb] for a <= b (upper triangle of P H P^T), from H's upper
-// triangle.  Rows a are grid-stride (grid y is capped).
-__global__ __launch_bounds__(kThreads) void gather_sym_kernel(const float *__restrict__ H, const int32_t *__restrict__ perm,
-                                                              int64_t d, int64_t lda, float *__restrict__ A) {
-    for (int64_t a = blockIdx.y; a < d; a += gridDim.y)
-        for (int64_t b = a + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < d; b += (int64_t)gridDim.x * kThreads) {
-            int64_t pa = perm ? min(max((int64_t)perm[a], (int64_t)0), d - 1) : a;
-            int64_t pb = perm ? min(max((int64_t)perm[b], (int64_t)0), d - 1) : b;
-            if (pa > pb) {
-                int64_t t = pa;
-                pa = pb;
-                pb = t;
-            }
-            A[a * lda + b] = H[pa * d + pb];
-        }
+// A[a][b] = S[pa][pb] for a <= b (upper triangle of P S P^T), S with row
+// stride lds: one workgroup per row a (grid-stride), its threads along b, so
+// the writes are coalesced and the reads fall in one row of S (a row of H's
+// upper triangle when there is no permutation: pa = a <= b = pb).
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const float *__restrict__ S, int64_t lds,
+                                                               const int32_t *__restrict__ perm, int64_t d, int64_t lda,
+                                                               float *__restrict__ A) {
+    for (int64_t a = blockIdx.x; a < d; a += gridDim.x) {
+        const int64_t pa = perm ? min(max((int64_t)perm[a], (int64_t)0), d - 1) : a;
+        const float *__restrict__ src = S + pa * lds;
+        float *__restrict__ dst = A + a * lda;
+        for (int64_t b = a + threadIdx.x; b < d; b += kThreads)
+            dst[b] = src[perm ? min(max((int64_t)perm[b], (int64_t)0), d - 1) : b];
+    }
+}
+
+// S = H + H^T - diag(H) from H's upper triangle (both triangles of S written),
+// by 64 x 64 tiles (ti <= tj) through LDS so that the mirrored tile is also
+// written along rows.  Grid (nt, nt); the blocks below the diagonal exit.
+constexpr int kSymTile = 64;
+__global__ __launch_bounds__(kThreads) void symmetrize_kernel(const float *__restrict__ H, int64_t d, int64_t lds,
+                                                              float *__restrict__ S) {
+    const int ti = blockIdx.y, tj = blockIdx.x;
+    if (ti > tj) return;
+    __shared__ float t[kSymTile][kSymTile + 1];
+    const int64_t r0 = (int64_t)ti * kSymTile, c0 = (int64_t)tj * kSymTile;
+    const int cx = threadIdx.x % kSymTile, ry = threadIdx.x / kSymTile;  // 4 rows per pass
+    for (int r = ry; r < kSymTile; r += kThreads / kSymTile) {
+        const int64_t i = r0 + r, j = c0 + cx;
+        t[r][cx] = (i < d && j < d && i <= j) ? H[i * d + j] : 0.0f;
+    }
+    __syncthreads();
+    for (int r = ry; r < kSymTile; r += kThreads / kSymTile) {
+        // S[r0 + r][c0 + cx] (the tile itself; on a diagonal tile its lower part mirrored)
+        const int64_t i = r0 + r, j = c0 + cx;
+        if (i < d && j < d) S[i * lds + j] = (ti < tj || r <= cx) ? t[r][cx] : t[cx][r];
+        // S[c0 + r][r0 + cx] = H[r0 + cx][c0 + r] (the mirror of an off-diagonal tile)
+        const int64_t i2 = c0 + r, j2 = r0 + cx;
+        if (ti < tj && i2 < d && j2 < d) S[i2 * lds + j2] = t[cx][r];
+    }
 }
 
 // lambda = damp_rel * mean(diag A) (fp64, fixed tree); A[i][i] += lambda.  One workgroup.
@@ -860,9 +885,18 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
         hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(d, kThreads)), dim3(kThreads), 0, s, perm, d);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned gx = (unsigned)((d + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(gather_sym_kernel, dim3(gx, (unsigned)std::min<int64_t>(d, 65535)), dim3(kThreads), 0, s, H,
-                       act_order ? perm : nullptr, d, lda, A);
+    // The working matrix: H's upper triangle as it is, or under a column order
+    // the upper triangle of P H P^T, gathered by rows from H's symmetric
+    // completion (staged in Tw, which is free until the factorization).
+    const unsigned grow = (unsigned)std::min<int64_t>(d, 4096);
+    if (act_order) {
+        const unsigned nt = (unsigned)ceil_div(d, kSymTile);
+        hipLaunchKernelGGL(symmetrize_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lda, Tw);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(gather_rows_kernel, dim3(grow), dim3(kThreads), 0, s, Tw, lda, perm, d, lda, A);
+    } else {
+        hipLaunchKernelGGL(gather_rows_kernel, dim3(grow), dim3(kThreads), 0, s, H, d, nullptr, d, lda, A);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, A, d, lda, damp_rel);
     if ((e = hipGetLastError()) != hipSuccess) return e;
