@@ -244,6 +244,7 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d_in,
     if (d_in > (int64_t)1 << 20) return fail(GPTQ_ERR_UNSUPPORTED, "%s: d_in too large", fn);
     const size_t need = gptq::prepare_ws_bytes(d_in);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned workspace", fn);
     return hip_status(gptq::run_prepare(H, hdiag, d_in, cfg->damp_rel, cfg->act_order ? 1 : 0, U, perm, info_dev, ws, stream), fn);
 }
 
@@ -255,6 +256,7 @@ gptq_status gptq_quantize_layer(float *W, int64_t d_out, int64_t d_in, const flo
     if (st != GPTQ_OK) return st;
     const size_t need = gptq::quantize_ws_bytes(d_out, d_in, *cfg);
     if (!ws || ws_bytes < need) return fail(GPTQ_ERR_WORKSPACE, "%s: need %zu workspace bytes, got %zu", fn, need, ws ? ws_bytes : (size_t)0);
+    if (need > 0 && !aligned(ws)) return fail(GPTQ_ERR_INVALID_ARG, "%s: misaligned workspace", fn);
     return hip_status(gptq::run_quantize(W, d_out, d_in, U, perm, *cfg, codes, scales, zeros, g_idx, ws, stream), fn);
 }
 

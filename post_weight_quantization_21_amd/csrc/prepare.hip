@@ -80,6 +80,27 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const float *__re
     }
 }
 
+// The same under a column order for rows of at most kStagedRowMax entries:
+// row pa of S is staged in LDS with 16-byte loads (S's rows are 16-byte
+// aligned: lds a multiple of 4, S aligned), and the permuted picks read LDS.
+constexpr int64_t kStagedRowMax = 16384;
+__global__ __launch_bounds__(kThreads) void gather_perm_rows_kernel(const float *__restrict__ S, int64_t lds,
+                                                                    const int32_t *__restrict__ perm, int64_t d,
+                                                                    int64_t lda, float *__restrict__ A) {
+    extern __shared__ float4 row4[];
+    const float *row = reinterpret_cast<const float *>(row4);
+    const int64_t n4 = (d + 3) / 4;  // within the row's padding (lds >= 4 n4)
+    for (int64_t a = blockIdx.x; a < d; a += gridDim.x) {
+        const int64_t pa = min(max((int64_t)perm[a], (int64_t)0), d - 1);
+        const float4 *__restrict__ src = reinterpret_cast<const float4 *>(S + pa * lds);
+        __syncthreads();  // the previous row's picks are done
+        for (int64_t i = threadIdx.x; i < n4; i += kThreads) row4[i] = src[i];
+        __syncthreads();
+        float *__restrict__ dst = A + a * lda;
+        for (int64_t b = a + threadIdx.x; b < d; b += kThreads) dst[b] = row[min(max((int64_t)perm[b], (int64_t)0), d - 1)];
+    }
+}
+
 // S = H + H^T - diag(H) from H's upper triangle (both triangles of S written),
 // by 64 x 64 tiles (ti <= tj) through LDS so that the mirrored tile is also
 // written along rows.  Grid (nt, nt); the blocks below the diagonal exit.
@@ -893,7 +914,11 @@ hipError_t run_prepare(const float *H, const double *hdiag, int64_t d, float dam
         const unsigned nt = (unsigned)ceil_div(d, kSymTile);
         hipLaunchKernelGGL(symmetrize_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lda, Tw);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(gather_rows_kernel, dim3(grow), dim3(kThreads), 0, s, Tw, lda, perm, d, lda, A);
+        if (d <= kStagedRowMax)
+            hipLaunchKernelGGL(gather_perm_rows_kernel, dim3(grow), dim3(kThreads), (size_t)ceil_div(d, 4) * 16, s, Tw, lda,
+                               perm, d, lda, A);
+        else
+            hipLaunchKernelGGL(gather_rows_kernel, dim3(grow), dim3(kThreads), 0, s, Tw, lda, perm, d, lda, A);
     } else {
         hipLaunchKernelGGL(gather_rows_kernel, dim3(grow), dim3(kThreads), 0, s, H, d, nullptr, d, lda, A);
     }

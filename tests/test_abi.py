@@ -109,6 +109,12 @@ def test_argument_errors_are_synchronous():
     assert lib.gptq_prepare_hinv(p, None, 64, ctypes.byref(cfg), p, p, p, p, 16, None) == gq.ERR_WORKSPACE
     bad = gq.config(damp_rel=-1.0)
     assert lib.gptq_prepare_hinv(p, None, 64, ctypes.byref(bad), p, p, p, p, 1 << 30, None) == gq.ERR_INVALID_ARG
+    # the workspace is read with 16-byte loads: a misaligned one is rejected
+    q = ctypes.c_void_p(0x20008)
+    assert lib.gptq_prepare_hinv(p, None, 64, ctypes.byref(cfg), p, p, p, q, 1 << 30, None) == gq.ERR_INVALID_ARG
+    assert b"workspace" in lib.gptq_last_error()
+    assert lib.gptq_quantize_layer(p, 64, 128, p, None, ctypes.byref(cfg), p, p, p, None, q, 1 << 30, None) == \
+        gq.ERR_INVALID_ARG
     # ldx * sizeof(bf16) must be a multiple of 16 bytes
     assert lib.gptq_hessian_accumulate(p, None, p, gq.DT_BF16, 64, 100, 100, p, 1 << 30, None) == gq.ERR_INVALID_ARG
     assert lib.gptq_hessian_accumulate(p, None, p, 5, 64, 64, 64, p, 1 << 30, None) == gq.ERR_INVALID_ARG
