@@ -1,6 +1,7 @@
 """gptq_quantize_layer_noalloc (the column pass on the library's fixed scratch array) against
-gptq_quantize_layer with a workspace: the same kernels, so the same bits.  Two calls in a row on the
-same array, the second on a smaller layer, and a layer too large for the array."""
+gptq_quantize_layer with a workspace: the same kernels, so the same bits.  Calls in a row on the
+same array, each on a smaller layer than the one before (the first with superblock updates on the
+split product), and a layer too large for the array."""
 import numpy as np
 import pytest
 
@@ -44,7 +45,7 @@ def _run(fn, W, U, cfg, perm):
 
 
 # (d_out, d_in, bits, sym, group, act_order): the first call, then a smaller one on the same array
-CALLS = [(1024, 2304, 4, False, 128, True), (200, 640, 3, True, 32, False)]
+CALLS = [(4096, 3584, 4, False, 128, False), (1024, 2304, 4, False, 128, True), (200, 640, 3, True, 32, False)]
 
 
 def test_noalloc_matches_workspace_entry_point():
