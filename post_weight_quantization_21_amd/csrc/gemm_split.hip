@@ -290,10 +290,46 @@ __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
         wait_vm<0>();
     }
 
-    // C = alpha acc + beta C, one accumulator block at a time; interior tiles
-    // without bounds checks.
+    // C = alpha acc + beta C; interior tiles without bounds checks.
     // with upper_only, a diagonal tile stores only m <= n
     const bool full = m0 + ST <= g.M && n0 + ST <= g.N && !(g.upper_only && m0 == n0);
+    // Accumulator block (i, j) of this lane: element r at row dr(r), column 0.
+    auto cptr = [&](int i, int j) {
+        const int64_t mb = m0 + wm * 128 + i * 32 + 4 * half, n = n0 + wn * 128 + j * 32 + lrow;
+        return g.C + mb * g.ldc + n;
+    };
+    auto dr = [](int r) { return 8 * (r >> 2) + (r & 3); };
+    if (full && g.beta != 0.0f) {
+        // The operand registers are free now: C is read two accumulator
+        // blocks at a time (32 loads per lane), the next pair's loads issued
+        // before this pair's stores.
+        float cold[2][2][16];
+        auto load_pair = [&](int p, float(&c)[2][16]) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float *cp = cptr(p >> 1, 2 * (p & 1) + jj);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) c[jj][r] = cp[dr(r) * g.ldc];
+            }
+        };
+        load_pair(0, cold[0]);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            if (p + 1 < 8) load_pair(p + 1, cold[(p + 1) & 1]);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int i = p >> 1, j = 2 * (p & 1) + jj;
+                float *cp = cptr(i, j);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = g.alpha * acc[i][j][r];
+                    v += g.beta * cold[p & 1][jj][r];
+                    cp[dr(r) * g.ldc] = v;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -301,17 +337,8 @@ __global__ __launch_bounds__(kThr) void gemm_split_kernel(GemmDesc g) {
             const int64_t mb = m0 + wm * 128 + i * 32 + 4 * half, n = n0 + wn * 128 + j * 32 + lrow;
             float *cp = g.C + mb * g.ldc + n;
             if (full) {
-                float cold[16];
-                if (g.beta != 0.0f) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) cold[r] = cp[(8 * (r >> 2) + (r & 3)) * g.ldc];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = g.alpha * acc[i][j][r];
-                    if (g.beta != 0.0f) v += g.beta * cold[r];
-                    cp[(8 * (r >> 2) + (r & 3)) * g.ldc] = v;
-                }
+                for (int r = 0; r < 16; ++r) cp[(8 * (r >> 2) + (r & 3)) * g.ldc] = g.alpha * acc[i][j][r];
             } else if (n < g.N) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
