@@ -135,6 +135,36 @@ __device__ __forceinline__ void panel_piece(uint4 (*dst)[4], const uint16_t *X, 
                                      (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 16][0]), 16, 0, 0);
 }
 
+// Channel-major pair stages: 64 tokens, so each row's piece is one whole
+// 128-byte line.  Loads of 64-byte pieces (half a line per row per 32-token
+// stage) streamed X into LDS at about 7.7 TB/s; whole lines at about 12 TB/s
+// (same tiles, splits and work order, loads only).  Image: two slots of
+// 256 rows x 128 B per panel; logical chunk c (tokens 8c .. 8c+7) of row r at
+// position c ^ swz8(r).  Rows alternate between the two halves of the 64
+// banks (128-byte pitch), so the 16 rows one b128 read pass touches at a
+// common chunk spread over all 16 bank groups when swz8(r) = (r / 2) % 8.
+constexpr int KP = 2 * KT;  // tokens per pair stage
+struct PairSmem {
+    uint4 a[2][TS][8];
+    uint4 b[2][TS][8];
+};
+
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// One 1 KB piece of a pair stage: 8 rows x 128 B; wave w fills rows
+// 64 w .. 64 w + 63 in eight pieces i = 0..7.  Rows past d are clamped to row
+// d-1 (valid memory; those outputs are discarded).
+__device__ __forceinline__ void pair_piece(uint4 (*dst)[8], const uint16_t *X, int64_t ldx, int64_t d, int64_t row0,
+                                           int64_t k0, int wave, int lane, int i) {
+    const int row = wave * 64 + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz8(row);
+    int64_t gr = row0 + row;
+    gr = gr < d ? gr : d - 1;
+    const uint16_t *src = X + gr * ldx + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)(&dst[wave * 64 + i * 8][0]), 16, 0, 0);
+}
+
 // Channel-major: the same LDS image of a partial stage (tokens k0 .. kend-1,
 // the rest zero) from masked register loads.
 __device__ __forceinline__ void panel_tail(uint4 (*dst)[4], const uint16_t *X, int64_t ldx, int64_t d, int64_t row0,
@@ -270,10 +300,9 @@ __global__ __launch_bounds__(kThreads) void mma_bf16_kernel(MmaArgs g) {
     const int64_t r0 = (int64_t)ti * TS, c0 = (int64_t)tj * TS;
     const int64_t kbeg = GEMM ? 0 : split * g.kchunk;
     const int64_t kend = GEMM ? g.K : ((kbeg + g.kchunk) < g.K ? (kbeg + g.kchunk) : g.K);
-    const int nfull = kend > kbeg ? (int)((kend - kbeg) / KT) : 0;
-    const bool has_tail = kend > kbeg + (int64_t)nfull * KT;
 
     __shared__ SyrkSmem sm;
+    static_assert(sizeof(PairSmem) == sizeof(SyrkSmem), "the pair stages use the ring's memory");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -305,6 +334,84 @@ __global__ __launch_bounds__(kThreads) void mma_bf16_kernel(MmaArgs g) {
         acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q >> 2], f.b[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
     };
 
+    // Channel-major: whole 64-token pair stages first, through two slots, the
+    // next pair's loads one pair ahead; each pair is four 16-token steps of
+    // the same MFMAs in the same token order as the 32-token stages below, so
+    // H does not depend on how the tokens are staged.  Then at most one 32-token
+    // stage and the tail.
+    int64_t kb2 = kbeg;
+    if constexpr (!TOK) {
+        const int npair = kend > kbeg ? (int)((kend - kbeg) / KP) : 0;
+        if (npair > 0) {
+            PairSmem &ps = *reinterpret_cast<PairSmem *>(&sm);
+            const int sw8 = swz8(lrow);
+            auto read_pfrag = [&](int slot_, int hs, int p, Frags &f) {
+                const int pos = (2 * hs + half) ^ sw8;
+                if (p < 4)
+                    f.a[p] = __builtin_bit_cast(bf16x8, ps.a[slot_][wm * 128 + p * 32 + lrow][pos]);
+                else
+                    f.b[p - 4] = __builtin_bit_cast(bf16x8, ps.b[slot_][wn * 128 + (p - 4) * 32 + lrow][pos]);
+            };
+            // Piece p (0..7: panel A, 8..15: panel B) of pair pr; past the end the
+            // last pair again, into a slot nobody reads.
+            auto issue_pair = [&](int pr, int slot_, int p) {
+                const int64_t k0 = kbeg + (int64_t)min(pr, npair - 1) * KP;
+                if (p < 8)
+                    pair_piece(ps.a[slot_], g.A, g.lda, g.ma, r0, k0, wave, lane, p);
+                else
+                    pair_piece(ps.b[slot_], g.B, g.ldb, g.mb, c0, k0, wave, lane, p - 8);
+            };
+#pragma unroll
+            for (int p = 0; p < 16; ++p) issue_pair(0, 0, p);
+#pragma unroll
+            for (int p = 0; p < 16; ++p) issue_pair(1, 1, p);
+            wait_vm_lgkm0<16>();  // pair 0 landed
+            bar();
+            Frags f0, f1;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) read_pfrag(0, 0, p, f0);
+            for (int k = 0; k < npair; ++k) {
+                const int cur = k & 1;
+                // steps 0-2: the MFMAs of one step while the next step's operands are read
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f0, q);
+                    if (q >= 1 && q <= 8) read_pfrag(cur, 1, q - 1, f1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f1, q);
+                    if (q >= 1 && q <= 8) read_pfrag(cur, 2, q - 1, f0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f0, q);
+                    if (q >= 1 && q <= 8) read_pfrag(cur, 3, q - 1, f1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // Step 3 holds its operands: this slot is free once every wave
+                // has read them, and pair k + 1 (this wave's only loads in
+                // flight) must have landed for every wave.
+                wait_vm_lgkm0<0>();
+                bar();
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    mfma(f1, q);
+                    issue_pair(k + 2, cur, q);
+                    if (q >= 7 && q <= 14) read_pfrag(cur ^ 1, 0, q - 7, f0);  // unused after the last pair
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            wait_vm_lgkm0<0>();
+            kb2 = kbeg + (int64_t)npair * KP;
+            __syncthreads();  // the 32-token ring below reuses the slots
+        }
+    }
+    const int nfull = kend > kb2 ? (int)((kend - kb2) / KT) : 0;
+    const bool has_tail = kend > kb2 + (int64_t)nfull * KT;
+
     // Token-major staging: wave w loads and stores units u = 0, 1 of a stage:
     // panel A (waves 0, 1) or B (waves 2, 3), 8-token chunk tg = 2 (w % 2) + u,
     // this lane's 4 channels.  Each token's row is addressed from a wave-uniform
@@ -331,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void mma_bf16_kernel(MmaArgs g) {
             // fixed: at each wait, the stage being waited for is followed by one
             // more.
             auto issue_piece = [&](int st, int slot_, int p) {
-                const int64_t k0 = kbeg + (int64_t)st * KT;
+                const int64_t k0 = kb2 + (int64_t)st * KT;
                 if (p < 4)
                     panel_piece(sm.a[slot_], g.A, g.lda, g.ma, r0, k0, wave, lane, p);
                 else
@@ -440,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void mma_bf16_kernel(MmaArgs g) {
         }
     }
     if (has_tail) {
-        const int64_t k0 = kbeg + (int64_t)nfull * KT;
+        const int64_t k0 = kb2 + (int64_t)nfull * KT;
         __syncthreads();  // every wave is done with the ring
         if constexpr (!TOK) {
             panel_tail(sm.a[0], g.A, g.lda, g.ma, r0, k0, kend, tid);
@@ -686,7 +793,7 @@ SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
             best_s = s;
         }
     }
-    p.kchunk = ceil_div(ceil_div(n_tok, best_s), KT) * KT;
+    p.kchunk = ceil_div(ceil_div(n_tok, best_s), KP) * KP;  // whole pair stages: 128-byte aligned rows
     p.splits = (int)ceil_div(n_tok, p.kchunk);
     if (p.splits < 1) p.splits = 1;
     return p;
