@@ -11,24 +11,24 @@
 // to fill the chip, tokens are split across workgroups and the partial tiles
 // are summed in a fixed order by a second kernel, so H is bit-reproducible.
 //
-// Two input layouts share one kernel and one LDS image (per stage, 256 rows =
-// channels of 32 tokens, as four 16-byte chunks of 8 tokens):
-//   channel-major X[d][ldx] (tokens contiguous): each row's 64 bytes of a
-//     stage go straight from global memory into LDS (global_load_lds_dwordx4);
+// Two input layouts share one kernel and one order of matrix-core products
+// (16-token steps in token order), so both give the same H bit for bit:
+//   channel-major X[d][ldx] (tokens contiguous): stages of 64 tokens, so each
+//     row's piece is one whole 128-byte line, go straight from global memory
+//     into LDS (global_load_lds_dwordx4) through two slots, the next stage's
+//     loads one stage ahead; a split's last tokens (fewer than 64) go through
+//     the 32-token stages below;
 //   token-major X[n][ldx] (channels contiguous, as a layer's inputs arrive):
 //     each lane loads 8 tokens x 4 channels (8-byte loads, 512 contiguous
 //     bytes per token and wave), transposes them in registers with byte
-//     permutes and writes four 16-byte chunks, one per channel.  No transposed
-//     copy of X is ever made.
-// The LDS image, and so the MFMA operands, are the same in both cases, so both
-// layouts give the same H bit for bit.
+//     permutes and writes four 16-byte chunks, one per channel, into an image
+//     of 256 rows = channels of 32 tokens; a ring of four such stages, three
+//     stages of loads in flight in registers.  No transposed copy of X is ever
+//     made.
 //
-// Pipeline: a ring of four LDS stages, filled ahead of the matrix cores
-// (channel-major: by direct loads, three stages ahead; token-major: through
-// registers, three stages of loads in flight); the MFMA operands of the next
-// 16-token step are read from LDS while the current step's MFMAs run; loads,
-// LDS reads and writes are issued between the MFMAs.  Work order: workgroup b runs
-// on XCD b % 8.  The upper tiles, in bands of four tile rows taken column by
+// Pipeline: the MFMA operands of the next 16-token step are read from LDS
+// while the current step's MFMAs run; loads, LDS reads and writes are issued
+// between the MFMAs.  Work order: workgroup b runs on XCD b % 8.  The upper tiles, in bands of four tile rows taken column by
 // column, are cut into eight contiguous groups, one per XCD, and every XCD
 // walks its group split after split: the tiles an XCD holds at once share a
 // few row panels in its L2, and all XCDs read the same token range at the same
