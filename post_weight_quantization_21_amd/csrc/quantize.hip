@@ -290,6 +290,57 @@ __global__ __launch_bounds__(kThreads) void unpermute_codes_kernel(const uint8_t
     }
 }
 
+// The same for rows of at most kCodeRegMax codes: thread t owns the 4-byte
+// words t + 256 i of every row, their columns' source positions are read once
+// per workgroup and kept in registers (two 16-bit positions per word), and all
+// of a row's loads are issued before the first wait.
+constexpr int kCodeIters = 16;
+constexpr int64_t kCodeRegMax = 4 * (int64_t)kThreads * kCodeIters;  // 16384 codes per row
+__global__ __launch_bounds__(kThreads) void unpermute_codes_reg_kernel(const uint8_t *__restrict__ cp,
+                                                                       const int32_t *__restrict__ inv, int64_t d_out,
+                                                                       int64_t d_in, uint8_t *__restrict__ codes) {
+    extern __shared__ uint32_t rowc[];
+    const uint8_t *rb = reinterpret_cast<const uint8_t *>(rowc);
+    const int tid = threadIdx.x;
+    const int64_t nw = d_in / 4;
+    uint32_t ip[kCodeIters][2];
+#pragma unroll
+    for (int i = 0; i < kCodeIters; ++i) {
+        const int64_t k = tid + (int64_t)kThreads * i;
+        if (k < nw) {
+            const int64_t c = 4 * k;
+            ip[i][0] = (uint32_t)clamp_col(inv[c + 0], d_in) | ((uint32_t)clamp_col(inv[c + 1], d_in) << 16);
+            ip[i][1] = (uint32_t)clamp_col(inv[c + 2], d_in) | ((uint32_t)clamp_col(inv[c + 3], d_in) << 16);
+        } else {
+            ip[i][0] = ip[i][1] = 0u;
+        }
+    }
+    for (int64_t r = blockIdx.x; r < d_out; r += gridDim.x) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(cp + r * d_in);
+        uint32_t v[kCodeIters];
+#pragma unroll
+        for (int i = 0; i < kCodeIters; ++i) {
+            const int64_t k = tid + (int64_t)kThreads * i;
+            if (k < nw) v[i] = src[k];
+        }
+#pragma unroll
+        for (int i = 0; i < kCodeIters; ++i) {
+            const int64_t k = tid + (int64_t)kThreads * i;
+            if (k < nw) rowc[k] = v[i];
+        }
+        __syncthreads();
+        uint32_t *dst = reinterpret_cast<uint32_t *>(codes + r * d_in);
+#pragma unroll
+        for (int i = 0; i < kCodeIters; ++i) {
+            const int64_t k = tid + (int64_t)kThreads * i;
+            if (k < nw)
+                dst[k] = (uint32_t)rb[ip[i][0] & 0xffffu] | ((uint32_t)rb[ip[i][0] >> 16] << 8) |
+                         ((uint32_t)rb[ip[i][1] & 0xffffu] << 16) | ((uint32_t)rb[ip[i][1] >> 16] << 24);
+        }
+        __syncthreads();  // rowc is reused by the next row
+    }
+}
+
 // Whether the act-order permutation of W runs in place (else: copy, then gather).
 bool row_perm_inplace(const float *W, int64_t d_in) {
     return d_in <= kRowPermMax && d_in % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
@@ -569,7 +620,11 @@ hipError_t run_quantize(float *W, int64_t d_out, int64_t d_in, const float *U, c
     }
     if (cperm) {
         const unsigned grid = (unsigned)std::min<int64_t>(d_out, 2048);
-        hipLaunchKernelGGL(unpermute_codes_kernel, dim3(grid), dim3(kThreads), (size_t)d_in, s, cdst, inv, d_out, d_in, codes);
+        if (d_in <= kCodeRegMax)
+            hipLaunchKernelGGL(unpermute_codes_reg_kernel, dim3(grid), dim3(kThreads), (size_t)d_in, s, cdst, inv, d_out, d_in,
+                               codes);
+        else
+            hipLaunchKernelGGL(unpermute_codes_kernel, dim3(grid), dim3(kThreads), (size_t)d_in, s, cdst, inv, d_out, d_in, codes);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
