@@ -86,6 +86,9 @@ def _layer(rng, d_out, d_in, group):
     (4, 50, 352, 32, False),        # few tokens, d_in not a multiple of 128: scales staged in LDS
     (40, 70, 352, 32, False),       # d_in not a multiple of 64: the generic kernel, two token blocks
     (200, 64, 96, 32, True),        # ... four token blocks, column gather
+    (1100, 14522, 256, 128, True),  # over a thousand 128 x 128 tiles, ragged on both sides; column gather
+    (1100, 14522, 192, 64, False),  # ... 64-column groups, an odd chunk count
+    (1100, 14522, 192, 32, False),  # ... 32-column groups
 ])
 def test_w4a16_parity(oracle_mod, M, d_out, d_in, group, with_perm):
     torch = torch_mod()
